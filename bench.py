@@ -1,0 +1,366 @@
+#!/usr/bin/env python3
+"""Benchmark of the blockwise-FP8 linear layer on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input.
+Default workload ("layer"): one decoder layer's four linears (QKV 2048->4096,
+O 2048->2048, gate/up 2048->12288, down 6144->2048) at 8192 tokens, each
+doing row-group + column-group quantization of X, block quantization of W
+(with the transposed copy for Dgrad), Fprop, row-group + column-group
+quantization of dY, Dgrad and Wgrad -- 2.474 TFLOP of FP8 GEMM per step.
+
+Other workloads: "linear" (the 8192 x 2048 -> 12288 gate/up linear, quantize
++ Fprop only) and "stack28" (28 decoder layers, forward chained through the
+layer outputs, then backward, timed against the same GEMMs in bf16).
+
+Prints ONE JSON line.  Inputs are seeded synthetic tensors generated on the
+device before timing.  Per-launch durations come from HIP events recorded on
+the launch stream around every kernel of the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "blockwise-FP8 linear TFLOP/s (fprop+dgrad+wgrad, 8192 tok) + % FP8 peak"
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+TOKENS = 8192
+LINEARS = (("qkv", 4096, 2048), ("o", 2048, 2048), ("gate_up", 12288, 2048), ("down", 2048, 6144))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=("layer", "linear", "stack28"), default="layer")
+    ap.add_argument("--algo", choices=("default", "promote", "scaled"), default="default")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    return ap.parse_args()
+
+
+class Timer:
+    """Events around each launch, on the stream the library launches on."""
+
+    def __init__(self, torch, enabled):
+        self.torch = torch
+        self.enabled = enabled
+        self.recs = []
+
+    def run(self, kind, flops, nbytes, fn):
+        if not self.enabled:
+            return fn()
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn()
+        e.record()
+        self.recs.append((kind, flops, nbytes, s, e))
+        return out
+
+    def summary(self):
+        agg = {}
+        for kind, flops, nbytes, s, e in self.recs:
+            ms = s.elapsed_time(e)
+            a = agg.setdefault(kind, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+            a["launches"] += 1
+            a["ms"] += ms
+            a["flops"] += flops
+            a["bytes"] += nbytes
+        return agg
+
+
+def build_layer(torch, fb, synth, seed, linears=LINEARS, x_in=None):
+    """Allocate inputs and every output / scratch buffer for one layer."""
+    L = []
+    for li, (name, n, k) in enumerate(linears):
+        d = {"name": name, "N": n, "K": k}
+        d["x"] = synth.device_normal_bf16((TOKENS, k), 1.0, seed * 1000 + 3 * li)
+        d["w"] = synth.device_normal_bf16((n, k), 0.02, seed * 1000 + 3 * li + 1)
+        d["dy"] = synth.device_normal_bf16((TOKENS, n), 1e-3, seed * 1000 + 3 * li + 2)
+        u8, f32 = torch.uint8, torch.float32
+        d["qx"] = torch.empty((TOKENS, k), dtype=u8, device="cuda")
+        d["sx"] = torch.empty((TOKENS, k // 128), dtype=f32, device="cuda")
+        d["qxT"] = torch.empty((k, TOKENS), dtype=u8, device="cuda")
+        d["sxT"] = torch.empty((k, TOKENS // 128), dtype=f32, device="cuda")
+        d["qw"] = torch.empty((n, k), dtype=u8, device="cuda")
+        d["qwT"] = torch.empty((k, n), dtype=u8, device="cuda")
+        d["sw"] = torch.empty((n // 128, k // 128), dtype=f32, device="cuda")
+        d["qdy"] = torch.empty((TOKENS, n), dtype=u8, device="cuda")
+        d["sdy"] = torch.empty((TOKENS, n // 128), dtype=f32, device="cuda")
+        d["qdyT"] = torch.empty((n, TOKENS), dtype=u8, device="cuda")
+        d["sdyT"] = torch.empty((n, TOKENS // 128), dtype=f32, device="cuda")
+        d["y"] = torch.empty((TOKENS, n), dtype=torch.bfloat16, device="cuda")
+        d["dx"] = torch.empty((TOKENS, k), dtype=torch.bfloat16, device="cuda")
+        d["dw"] = torch.empty((n, k), dtype=torch.bfloat16, device="cuda")
+        ws = fb.fp8_block_gemm_workspace_size(fb.FP8BLK_OP_WGRAD, TOKENS, n, k)
+        d["ws"] = torch.empty(max(ws, 16), dtype=u8, device="cuda")
+        L.append(d)
+    return L
+
+
+def qbytes(rows, cols):
+    return rows * cols * 3 + rows * (cols // 128) * 4
+
+
+def fwd_linear(fb, T, d, algo, x=None):
+    n, k = d["N"], d["K"]
+    x = d["x"] if x is None else x
+    T.run("quant_rowgroup", 0, qbytes(TOKENS, k), lambda: fb.fp8_quantize_rowgroup(x, q=d["qx"], s=d["sx"]))
+    T.run("quant_colgroup", 0, qbytes(TOKENS, k), lambda: fb.fp8_quantize_colgroup(x, qT=d["qxT"], sT=d["sxT"]))
+    T.run("quant_block", 0, n * k * 4 + (n // 128) * (k // 128) * 4,
+          lambda: fb.fp8_quantize_block(d["w"], q=d["qw"], qT=d["qwT"], s=d["sw"]))
+    T.run("gemm_fprop", 2.0 * TOKENS * n * k, 0,
+          lambda: fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, d["qx"], d["sx"], d["qw"], d["sw"], TOKENS, n, k,
+                                    algo=algo, out=d["y"]))
+    return d["y"]
+
+
+def bwd_linear(fb, T, d, algo):
+    n, k = d["N"], d["K"]
+    T.run("quant_rowgroup", 0, qbytes(TOKENS, n), lambda: fb.fp8_quantize_rowgroup(d["dy"], q=d["qdy"], s=d["sdy"]))
+    T.run("quant_colgroup", 0, qbytes(TOKENS, n),
+          lambda: fb.fp8_quantize_colgroup(d["dy"], qT=d["qdyT"], sT=d["sdyT"]))
+    T.run("gemm_dgrad", 2.0 * TOKENS * n * k, 0,
+          lambda: fb.fp8_block_gemm(fb.FP8BLK_OP_DGRAD, d["qdy"], d["sdy"], d["qwT"], d["sw"], TOKENS, n, k,
+                                    algo=algo, out=d["dx"]))
+    T.run("gemm_wgrad", 2.0 * TOKENS * n * k, 0,
+          lambda: fb.fp8_block_gemm(fb.FP8BLK_OP_WGRAD, d["qdyT"], d["sdyT"], d["qxT"], d["sxT"], TOKENS, n, k,
+                                    algo=algo, out=d["dw"], workspace=d["ws"]))
+
+
+def layer_step(fb, T, L, algo):
+    for d in L:
+        fwd_linear(fb, T, d, algo)
+    for d in reversed(L):
+        bwd_linear(fb, T, d, algo)
+
+
+def linear_step(fb, T, d, algo):
+    n, k = d["N"], d["K"]
+    T.run("quant_rowgroup", 0, qbytes(TOKENS, k), lambda: fb.fp8_quantize_rowgroup(d["x"], q=d["qx"], s=d["sx"]))
+    T.run("quant_block", 0, n * k * 3 + (n // 128) * (k // 128) * 4,
+          lambda: fb.fp8_quantize_block(d["w"], transpose=False, q=d["qw"], s=d["sw"]))
+    T.run("gemm_fprop", 2.0 * TOKENS * n * k, 0,
+          lambda: fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, d["qx"], d["sx"], d["qw"], d["sw"], TOKENS, n, k,
+                                    algo=algo, out=d["y"]))
+
+
+def stack_step(fb, T, layers, algo):
+    """28 layers: forward chained (O input = QKV output columns 0..2047, gate/up
+    input = O output, down input = gate/up output columns 0..6143, next layer
+    input = down output), then backward with each linear's own dY and the
+    column-group copy of its input kept from the forward pass."""
+    x = layers[0][0]["x"]
+    for L in layers:
+        qkv, o, gu, dn = L
+        y = fwd_linear(fb, T, qkv, algo, x)
+        y = fwd_linear(fb, T, o, algo, y[:, :2048])
+        y = fwd_linear(fb, T, gu, algo, y)
+        x = fwd_linear(fb, T, dn, algo, y[:, :6144])
+    for L in reversed(layers):
+        for d in reversed(L):
+            bwd_linear(fb, T, d, algo)
+
+
+def gemm_flops(linears):
+    return sum(3 * 2.0 * TOKENS * n * k for _, n, k in linears)
+
+
+def bf16_baseline(torch, linears, reps, steps=5):
+    """The same GEMM shapes as the FP8 step, in bf16 via torch.matmul."""
+    mats = []
+    for _, n, k in linears:
+        x = torch.randn(TOKENS, k, device="cuda", dtype=torch.bfloat16)
+        w = torch.randn(n, k, device="cuda", dtype=torch.bfloat16)
+        dy = torch.randn(TOKENS, n, device="cuda", dtype=torch.bfloat16)
+        mats.append((x, w.t().contiguous(), dy, w, dy.t().contiguous()))
+
+    def one():
+        for _ in range(reps):
+            for x, wt, dy, w, dyt in mats:
+                torch.matmul(x, wt)
+                torch.matmul(dy, w)
+                torch.matmul(dyt, x)
+
+    one()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    return dt, gemm_flops(linears) * reps / dt / 1e12
+
+
+def cpu_baseline(budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the layer
+    workload, scaled to a whole-step rate: per linear, the oracle quantizes
+    all five operands at full size (timed), then computes a few output rows
+    of each GEMM (timed, scaled by total rows / sampled rows).  Stops after
+    the linear that crosses the time budget."""
+    import numpy as np
+    import oracle
+    from blockwise_fp8_linear_amd import synth
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    rows_per = max(8, threads)
+    rng = np.random.default_rng(7)
+    flops = t_est = t_spent = 0.0
+    done = []
+    for li, (name, n, k) in enumerate(LINEARS):
+        x = synth.normal_bf16((TOKENS, k), 1.0, 0, 3, 3 * li)
+        w = synth.normal_bf16((n, k), 0.02, 0, 3, 3 * li + 1)
+        dy = synth.normal_bf16((TOKENS, n), 1e-3, 0, 3, 3 * li + 2)
+        t0 = time.perf_counter()
+        qx, sx = oracle.quantize_rowgroup(x)
+        qxT, sxT = oracle.quantize_colgroup(x)
+        qw, _, sw = oracle.quantize_block(w, transpose=False)
+        qdy, sdy = oracle.quantize_rowgroup(dy)
+        qdyT, sdyT = oracle.quantize_colgroup(dy)
+        t_q = time.perf_counter() - t0
+        rows_m = rng.choice(TOKENS, rows_per, replace=False)
+        rows_n = rng.choice(n, rows_per, replace=False)
+        t0 = time.perf_counter()
+        oracle.gemm_fprop(qx, sx, qw, sw, rows=rows_m)
+        t_f = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.gemm_dgrad(qdy, sdy, qw, sw, rows=rows_m)
+        t_d = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.gemm_wgrad(qdyT, sdyT, qxT, sxT, rows=rows_n)
+        t_w = time.perf_counter() - t0
+        t_spent += t_q + t_f + t_d + t_w
+        t_est += t_q + (t_f + t_d) * TOKENS / rows_per + t_w * n / rows_per
+        flops += 3 * 2.0 * TOKENS * n * k
+        done.append(name)
+        if t_spent > budget_s:
+            break
+    return {
+        "value": round(flops / t_est / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"linears {done}: full-size oracle quantization of X, W and dY (row, column and block "
+                   f"groups) plus {rows_per} output rows of each of fprop/dgrad/wgrad, GEMM time scaled to all "
+                   f"rows; {t_spent:.1f} s of CPU work, est. {t_est:.0f} s per full step, "
+                   f"{platform.processor() or platform.machine()}, {os.cpu_count()} logical CPUs"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+              "the data-parallel sharding is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import blockwise_fp8_linear_amd as fb
+    from blockwise_fp8_linear_amd import synth
+
+    fb.load_library()
+    torch.cuda.set_device(0)
+    algo = {"default": fb.FP8BLK_ALGO_DEFAULT, "promote": fb.FP8BLK_ALGO_PROMOTE,
+            "scaled": fb.FP8BLK_ALGO_SCALED_MFMA}[args.algo]
+
+    if args.workload == "layer":
+        L = build_layer(torch, fb, synth, 0)
+        step = lambda T: layer_step(fb, T, L, algo)
+        step_flops = gemm_flops(LINEARS)
+        reps, linears = 1, LINEARS
+        desc = "one decoder layer's linears (QKV, O, gate/up, down), fprop+dgrad+wgrad, 8192 tokens"
+    elif args.workload == "linear":
+        L = build_layer(torch, fb, synth, 0, linears=(("gate_up", 12288, 2048),))
+        step = lambda T: linear_step(fb, T, L[0], algo)
+        step_flops = 2.0 * TOKENS * 12288 * 2048
+        reps, linears = None, None
+        desc = "gate/up linear 8192x2048 -> 12288: quantize + fprop"
+    else:
+        layers = [build_layer(torch, fb, synth, s) for s in range(28)]
+        step = lambda T: stack_step(fb, T, layers, algo)
+        step_flops = 28 * gemm_flops(LINEARS)
+        reps, linears = 28, LINEARS
+        desc = "28 decoder layers' linears, forward chained then backward, 8192 tokens"
+
+    null = Timer(torch, False)
+    for _ in range(args.warmup):
+        step(null)
+    torch.cuda.synchronize()
+
+    T = Timer(torch, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(T)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall / args.steps * 1e3
+    value = step_flops / (ms * 1e-3) / 1e12
+
+    agg = T.summary()
+    breakdown = {}
+    for kind, a in agg.items():
+        avg_ms = a["ms"] / a["launches"]
+        e = {"launches_per_step": a["launches"] // args.steps, "avg_ms": round(avg_ms, 5),
+             "ms_per_step": round(a["ms"] / args.steps, 4)}
+        if a["flops"]:
+            e["TFLOP/s"] = round(a["flops"] / (a["ms"] * 1e-3) / 1e12, 1)
+        if a["bytes"]:
+            e["GB/s"] = round(a["bytes"] / (a["ms"] * 1e-3) / 1e9, 1)
+        breakdown[kind] = e
+    gemm_kinds = [k for k in agg if k.startswith("gemm")]
+    gemm_ms = sum(agg[k]["ms"] for k in gemm_kinds)
+    gemm_flops_t = sum(agg[k]["flops"] for k in gemm_kinds)
+    dom = max(agg, key=lambda k: agg[k]["ms"])
+    a = agg[dom]
+    if a["flops"]:
+        ach = a["flops"] / a["launches"] / (a["ms"] / a["launches"] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": None}
+    else:
+        ach = a["bytes"] / a["launches"] / (a["ms"] / a["launches"] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": desc, "tokens": TOKENS, "algo": args.algo,
+                   "gemm_tflop_per_step": round(step_flops / 1e12, 4)},
+        "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
+        "gemm_only_TFLOP/s": round(gemm_flops_t / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
+        "roofline": roof,
+        "breakdown": breakdown,
+    }
+    if linears is not None and not args.no_bf16_baseline:
+        dt, tf = bf16_baseline(torch, linears, reps if args.workload != "stack28" else 28)
+        out["bf16_baseline"] = {"ms_per_step": round(dt * 1e3, 3), "TFLOP/s": round(tf, 1),
+                                "fp8_over_bf16": round(dt * 1e3 / ms, 3),
+                                "what": "the same GEMMs in bf16 via torch.matmul (hipBLASLt), no quantization"}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+// C ABI of libfp8blk: argument validation and dispatch.  The contract of each
+// entry point is documented in include/fp8blk.h.
+#include "../../include/fp8blk.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "fp8blk_launch.h"
+
+namespace {
+
+constexpr int64_t kGroup = 128;
+constexpr int kMaxDevices = 64;
+// Once-initialised per-device answer to "is this a gfx950?": 0 unknown, 1 yes, 2 no.
+std::atomic<int> g_device_ok[kMaxDevices];
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool mult128(int64_t v) { return v > 0 && v % kGroup == 0; }
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8BLK_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FP8BLK_ERR_DEVICE;
+  int known = g_device_ok[dev].load(std::memory_order_acquire);
+  if (known == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8BLK_ERR_HIP;
+    known = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_ok[dev].store(known, std::memory_order_release);
+  }
+  return known == 1 ? FP8BLK_OK : FP8BLK_ERR_DEVICE;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? FP8BLK_OK : FP8BLK_ERR_HIP; }
+
+// Largest element count the 32-bit index arithmetic inside the kernels covers.
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8_status_string(int status) {
+  switch (status) {
+    case FP8BLK_OK: return "ok";
+    case FP8BLK_ERR_NULL: return "fp8blk: a required pointer is NULL";
+    case FP8BLK_ERR_DIM: return "fp8blk: a dimension is <= 0 or not a multiple of 128";
+    case FP8BLK_ERR_ALIGN: return "fp8blk: a pointer or leading dimension is not 16-byte aligned";
+    case FP8BLK_ERR_ARG: return "fp8blk: bad enum value, leading dimension smaller than the row, or size too large";
+    case FP8BLK_ERR_WORKSPACE: return "fp8blk: workspace smaller than fp8_block_gemm_workspace_size()";
+    case FP8BLK_ERR_HIP: return "fp8blk: HIP runtime error at launch";
+    case FP8BLK_ERR_DEVICE: return "fp8blk: the current device is not gfx950";
+    default: return "fp8blk: unknown status";
+  }
+}
+
+int fp8_quantize_rowgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                          float* s, int scale_mode, hipStream_t stream) {
+  if (scale_mode != FP8BLK_SCALE_POW2) return FP8BLK_ERR_ARG;
+  if (!x || !q || !s) return FP8BLK_ERR_NULL;
+  if (rows <= 0 || !mult128(cols)) return FP8BLK_ERR_DIM;
+  if (ld_x < cols || ld_q < cols) return FP8BLK_ERR_ARG;
+  if (rows * (cols / kGroup) >= (int64_t(1) << 31) || rows * ld_x > kMaxElems || rows * ld_q > kMaxElems)
+    return FP8BLK_ERR_ARG;
+  if (!aligned16(x) || !aligned16(q) || !aligned4(s) || ld_x % 8 || ld_q % 16) return FP8BLK_ERR_ALIGN;
+  if (int rc = check_device()) return rc;
+  return finish(fp8blk::launch_quant_rowgroup(x, rows, cols, ld_x, q, ld_q, s, stream));
+}
+
+int fp8_quantize_colgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qT, int64_t ld_qT,
+                          float* sT, int scale_mode, hipStream_t stream) {
+  if (scale_mode != FP8BLK_SCALE_POW2) return FP8BLK_ERR_ARG;
+  if (!x || !qT || !sT) return FP8BLK_ERR_NULL;
+  if (!mult128(rows) || !mult128(cols)) return FP8BLK_ERR_DIM;
+  if (ld_x < cols || ld_qT < rows) return FP8BLK_ERR_ARG;
+  if ((rows / 128) * (cols / 64) >= (int64_t(1) << 31) || rows * ld_x > kMaxElems || cols * ld_qT > kMaxElems)
+    return FP8BLK_ERR_ARG;
+  if (!aligned16(x) || !aligned16(qT) || !aligned4(sT) || ld_x % 8 || ld_qT % 16) return FP8BLK_ERR_ALIGN;
+  if (int rc = check_device()) return rc;
+  return finish(fp8blk::launch_quant_colgroup(x, rows, cols, ld_x, qT, ld_qT, sT, stream));
+}
+
+int fp8_quantize_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld_w, uint8_t* q, uint8_t* qT,
+                       float* s, int scale_mode, hipStream_t stream) {
+  if (scale_mode != FP8BLK_SCALE_POW2) return FP8BLK_ERR_ARG;
+  if (!w || !q || !s) return FP8BLK_ERR_NULL;
+  if (!mult128(rows) || !mult128(cols)) return FP8BLK_ERR_DIM;
+  if (ld_w < cols) return FP8BLK_ERR_ARG;
+  if ((rows / 128) * (cols / 128) >= (int64_t(1) << 31) || rows * ld_w > kMaxElems || rows * cols > kMaxElems)
+    return FP8BLK_ERR_ARG;
+  if (!aligned16(w) || !aligned16(q) || (qT && !aligned16(qT)) || !aligned4(s) || ld_w % 8) return FP8BLK_ERR_ALIGN;
+  if (int rc = check_device()) return rc;
+  return finish(fp8blk::launch_quant_block(w, rows, cols, ld_w, q, qT, s, stream));
+}
+
+static int check_gemm_common(int64_t M, int64_t N, int64_t K, const void* a, const float* sa, const void* b,
+                             const float* sb, const void* out, int out_dtype) {
+  if (out_dtype != FP8BLK_OUT_BF16 && out_dtype != FP8BLK_OUT_FP32) return FP8BLK_ERR_ARG;
+  if (!a || !sa || !b || !sb || !out) return FP8BLK_ERR_NULL;
+  if (!mult128(M) || !mult128(N) || !mult128(K)) return FP8BLK_ERR_DIM;
+  if (M * N > kMaxElems || M * K > kMaxElems || N * K > kMaxElems || M / 128 >= (1 << 20) || N / 128 >= (1 << 20) ||
+      K / 128 >= (1 << 20))
+    return FP8BLK_ERR_ARG;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(out) || !aligned4(sa) || !aligned4(sb)) return FP8BLK_ERR_ALIGN;
+  return FP8BLK_OK;
+}
+
+// The algorithm FP8BLK_ALGO_DEFAULT resolves to.
+constexpr fp8blk::GemmAlgo kDefaultAlgo = fp8blk::GemmAlgo::Promote;
+
+int fp8_block_gemm(int op, int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa, const uint8_t* b,
+                   const float* sb, void* out, int out_dtype, int algo, void* workspace, size_t ws_bytes,
+                   hipStream_t stream) {
+  if (op != FP8BLK_OP_FPROP && op != FP8BLK_OP_DGRAD && op != FP8BLK_OP_WGRAD) return FP8BLK_ERR_ARG;
+  if (algo != FP8BLK_ALGO_DEFAULT && algo != FP8BLK_ALGO_PROMOTE && algo != FP8BLK_ALGO_SCALED_MFMA)
+    return FP8BLK_ERR_ARG;
+  if (int rc = check_gemm_common(M, N, K, a, sa, b, sb, out, out_dtype)) return rc;
+  fp8blk::GemmArgs g{};
+  g.a = a; g.sa = sa; g.b = b; g.sb = sb;
+  g.out = out; g.out_f32 = out_dtype == FP8BLK_OUT_FP32;
+  if (op == FP8BLK_OP_FPROP) {
+    // Y[m][n] = sum_k X[m][k] W[n][k]; weight block (n/128, k/128)
+    g.I = M; g.J = N; g.R = K;
+    g.sb_j = K / kGroup; g.sb_r = 1; g.bmode = fp8blk::BScale::Block;
+  } else if (op == FP8BLK_OP_DGRAD) {
+    // dX[m][k] = sum_n dY[m][n] W[n][k]: B = qwT [K][N]; the weight block
+    // holding (n, k) has scale sw[(n/128) * (K/128) + k/128]
+    g.I = M; g.J = K; g.R = N;
+    g.sb_j = 1; g.sb_r = K / kGroup; g.bmode = fp8blk::BScale::Block;
+  } else {
+    // dW[n][k] = sum_m dY[m][n] X[m][k]: A = qdyT [N][M], B = qxT [K][M]
+    g.I = N; g.J = K; g.R = M;
+    g.sb_j = 0; g.sb_r = 0; g.bmode = fp8blk::BScale::Row;
+  }
+  const size_t need = fp8blk::gemm_workspace_bytes(g.I, g.J, g.R, g.bmode);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need)) return FP8BLK_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return FP8BLK_ERR_ALIGN;
+  if (int rc = check_device()) return rc;
+  g.ws = static_cast<float*>(workspace);
+  g.splits = fp8blk::gemm_splits(g.I, g.J, g.R, g.bmode);
+  const fp8blk::GemmAlgo al = algo == FP8BLK_ALGO_PROMOTE      ? fp8blk::GemmAlgo::Promote
+                              : algo == FP8BLK_ALGO_SCALED_MFMA ? fp8blk::GemmAlgo::ScaledMfma
+                                                                : kDefaultAlgo;
+  return finish(fp8blk::launch_gemm(g, al, stream));
+}
+
+int fp8_block_gemm_fprop(int64_t M, int64_t N, int64_t K, const uint8_t* qx, const float* sx, const uint8_t* qw,
+                         const float* sw, void* y, int out_dtype, hipStream_t stream) {
+  return fp8_block_gemm(FP8BLK_OP_FPROP, M, N, K, qx, sx, qw, sw, y, out_dtype, FP8BLK_ALGO_DEFAULT, nullptr, 0,
+                        stream);
+}
+
+int fp8_block_gemm_dgrad(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy, const uint8_t* qwT,
+                         const float* sw, void* dx, int out_dtype, hipStream_t stream) {
+  return fp8_block_gemm(FP8BLK_OP_DGRAD, M, N, K, qdy, sdy, qwT, sw, dx, out_dtype, FP8BLK_ALGO_DEFAULT, nullptr, 0,
+                        stream);
+}
+
+int fp8_block_gemm_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* qdyT, const float* sdyT,
+                         const uint8_t* qxT, const float* sxT, void* dw, int out_dtype, void* workspace,
+                         size_t ws_bytes, hipStream_t stream) {
+  return fp8_block_gemm(FP8BLK_OP_WGRAD, M, N, K, qdyT, sdyT, qxT, sxT, dw, out_dtype, FP8BLK_ALGO_DEFAULT, workspace,
+                        ws_bytes, stream);
+}
+
+size_t fp8_block_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
+  if (!mult128(M) || !mult128(N) || !mult128(K)) return (size_t)-1;
+  switch (op) {
+    case FP8BLK_OP_FPROP: return fp8blk::gemm_workspace_bytes(M, N, K, fp8blk::BScale::Block);
+    case FP8BLK_OP_DGRAD: return fp8blk::gemm_workspace_bytes(M, K, N, fp8blk::BScale::Block);
+    case FP8BLK_OP_WGRAD: return fp8blk::gemm_workspace_bytes(N, K, M, fp8blk::BScale::Row);
+    default: return (size_t)-1;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// Device-side helpers shared by the gfx950 kernels of libfp8blk.
+//
+// Conventions follow include/fp8blk.h: bf16 values arrive as raw 16-bit
+// patterns, E4M3 codes are OCP "fn" bytes, scales are powers of two stored
+// as fp32 (so their exponent field is an E8M0 byte).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8blk {
+
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// DPP controls (GFX9 encoding): rotate right within a 16-lane row, quad
+// permutations, and the mirror within each 8-lane half row.
+constexpr int kDppRowRor1 = 0x121;
+constexpr int kDppRowRor2 = 0x122;
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Largest of the two 16-bit halves, per half, of two packed words.
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  ushort2_t x = __builtin_bit_cast(ushort2_t, a);
+  ushort2_t y = __builtin_bit_cast(ushort2_t, b);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
+}
+
+// |x| of two packed bf16 values is their bit pattern without the sign bit,
+// and for non-NaN values the unsigned order of those patterns is the order
+// of the magnitudes, so an integer max is an exact amax.
+__device__ __forceinline__ uint32_t abs2(uint32_t w) { return w & 0x7FFF7FFFu; }
+
+// Max over the 16 lanes of a DPP row; every lane of the row gets the result.
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = max(v, dpp<kDppRowRor8>(v));
+  v = max(v, dpp<kDppRowRor4>(v));
+  v = max(v, dpp<kDppRowRor2>(v));
+  v = max(v, dpp<kDppRowRor1>(v));
+  return v;
+}
+
+// Per-half max of two packed 16-bit values over each aligned group of 8
+// lanes; every lane of the group gets it.  (A 32-bit max would order by the
+// high half and lose the low one.)
+__device__ __forceinline__ uint32_t lane8_max_pk(uint32_t v) {
+  v = pk_max_u16(v, dpp<kDppQuadSwap1>(v));
+  v = pk_max_u16(v, dpp<kDppQuadSwap2>(v));
+  v = pk_max_u16(v, dpp<kDppHalfMirror>(v));
+  return v;
+}
+
+// Max over all 64 lanes of a wave (result in every lane).
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = row16_max(v);
+  v = max(v, (uint32_t)__shfl_xor((int)v, 16, 64));
+  v = max(v, (uint32_t)__shfl_xor((int)v, 32, 64));
+  return v;
+}
+
+// Scale exponent from the bf16 pattern of a non-negative amax.
+// amax = (1 + m/128) * 2^(E-127) and 448 = 1.75 * 2^8, so the smallest e with
+// amax <= 448 * 2^e is E - 135, plus one when m > 96.  A zero amax gives 0
+// (scale 1); bf16 subnormals and everything below 448 * 2^-126 clamp to -126.
+// For finite bf16 input the result lies in [-126, 120].
+__device__ __forceinline__ int scale_exponent(uint32_t amax_bits) {
+  int E = (int)(amax_bits >> 7);
+  int m = (int)(amax_bits & 0x7F);
+  int e = E - 135 + (m > 96 ? 1 : 0);
+  e = e < -126 ? -126 : e;
+  return amax_bits == 0 ? 0 : e;
+}
+
+// 2^e for e in [-126, 127] and 2^-e for e in [-126, 126], built from bits.
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+// bf16 pattern (low or high half of a word) to fp32, exactly.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Four bf16 (two words) times 2^-e, rounded to E4M3 (RNE) into one word,
+// byte i holding element i.  The multiply by a power of two is exact, so
+// the conversion is the only rounding; the scale rule keeps |x * 2^-e| <= 448,
+// inside the converter's finite range.
+__device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, float inv) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w0) * inv, bf16_hi(w0) * inv, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w1) * inv, bf16_hi(w1) * inv, r, true);
+  return (uint32_t)r;
+}
+
+// Same for four values given as lo/hi halves of four different words
+// (used where a word holds two columns).
+__device__ __forceinline__ uint32_t quant4_sel(float a, float b, float c, float d, float inv) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a * inv, b * inv, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c * inv, d * inv, r, true);
+  return (uint32_t)r;
+}
+
+// 4x4 byte transpose: in[r] holds bytes (r,0..3); out[c] gets bytes (0..3,c).
+__device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[4]) {
+  uint32_t a = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);  // r0c0 r1c0 r0c1 r1c1
+  uint32_t b = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);  // r0c2 r1c2 r0c3 r1c3
+  uint32_t c = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);  // r2c0 r3c0 r2c1 r3c1
+  uint32_t d = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);  // r2c2 r3c2 r2c3 r3c3
+  out[0] = __builtin_amdgcn_perm(c, a, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(c, a, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(d, b, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
+}
+
+// Round fp32 to bf16 (nearest even) for finite values.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// XCD-aware remap of a linear workgroup id.  Consecutive ids are dealt to the
+// 8 XCDs in turn; this makes each XCD own a contiguous range of logical ids
+// (when the count divides evenly) so neighbouring tiles share an L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
+  constexpr uint32_t kXcds = 8;
+  if (nblocks % kXcds != 0) return bid;
+  return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
+}
+
+}  // namespace fp8blk

@@ -1,0 +1,49 @@
+// Internal launch entry points of libfp8blk (host side).  Arguments are
+// validated by the C ABI layer (api.cpp) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8blk {
+
+hipError_t launch_quant_rowgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                                 int64_t ld_q, float* s, hipStream_t stream);
+hipError_t launch_quant_colgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qT,
+                                 int64_t ld_qT, float* sT, hipStream_t stream);
+hipError_t launch_quant_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld_w, uint8_t* q, uint8_t* qT,
+                              float* s, hipStream_t stream);
+
+// How the B operand's scales are indexed.  A's scales are always per row:
+// sa[i * (R/128) + rb].  B_BLOCK: sb[(j/128) * sb_j + rb * sb_r] (a 128x128
+// weight block); B_ROW: sb[j * (R/128) + rb].
+enum class BScale { Block, Row };
+
+struct GemmArgs {
+  int64_t I, J, R;          // out is I x J, reduction length R
+  const uint8_t* a;         // [I][R]
+  const float* sa;          // [I][R/128]
+  const uint8_t* b;         // [J][R]
+  const float* sb;
+  int64_t sb_j, sb_r;       // strides for BScale::Block
+  BScale bmode;
+  void* out;                // [I][J]
+  bool out_f32;
+  float* ws;                // split-K partials (may be null when splits == 1)
+  int splits;
+};
+
+// Number of split-K slices the GEMM launcher uses at this shape and the
+// workspace bytes that needs.
+int gemm_splits(int64_t I, int64_t J, int64_t R, BScale bmode);
+size_t gemm_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode);
+
+// Promote: MFMA from zero per 128-deep block, scale product applied on the
+// VALU into fp32 accumulators.  ScaledMfma: the gfx950 block-scaled MFMA
+// applies the power-of-two scales in the matrix core and accumulates in place.
+enum class GemmAlgo { Promote, ScaledMfma };
+
+hipError_t launch_gemm(const GemmArgs& g, GemmAlgo algo, hipStream_t stream);
+
+}  // namespace fp8blk

@@ -1,0 +1,404 @@
+// Block-scaled FP8 GEMM for gfx950:  out[i][j] = sum over 128-deep reduction
+// blocks b of sa(i,b) * sb(j,b) * sum_{r in b} A[i][r] * B[j][r]
+// with E4M3 operands, fp32 accumulation and bf16 (RNE) or fp32 output.
+//
+// This one "TN" kernel serves the three contractions of the FP8 linear layer
+// ("Puro-2B ... part 3/7", section 3.2, fourth paragraph: Fprop, Dgrad and
+// Wgrad all on the FP8 path): both operands are stored contiguous along the
+// reduction dimension, so
+//   Fprop  Y  = X W^T : A = qx   [M][K], B = qw  [N][K], B scales per block
+//   Dgrad  dX = dY W  : A = qdy  [M][N], B = qwT [K][N], B scales per block
+//   Wgrad  dW = dY^T X: A = qdyT [N][M], B = qxT [K][M], B scales per row
+// (one scale per 128 along the reduction dimension for activations and
+// gradients, per 128x128 block for weights: section 3.2, second paragraph).
+//
+// Structure (per workgroup): a BM x BN output tile, the reduction walked in
+// 128-deep blocks.  Each block's A and B tiles (BM x 128 and BN x 128 bytes)
+// are staged in LDS, double buffered, with the 16-byte chunks of a row
+// XOR-swizzled by (row & 7) so that the MFMA fragment reads are free of bank
+// conflicts.  One v_mfma_*_16x16x128_f8f6f4 consumes exactly one 128-deep
+// block for a 16x16 sub-tile, so the per-block scale product is applied
+// between blocks:
+//   PROMOTE = true : P = MFMA(A_b, B_b) from zero, then acc += P * (sa*sb)
+//                    on the VALU, in fp32;
+//   PROMOTE = false: the gfx950 block-scaled MFMA, which multiplies each
+//                    operand row by its power-of-two scale (an E8M0 byte:
+//                    the fp32 scale's exponent field) inside the matrix core
+//                    and accumulates in place.
+// The MFMA operands are swapped (B tile as the instruction's A operand) so
+// that each lane ends up holding 4 consecutive output columns of one row,
+// which makes the scale a single value per lane (per row) for the weight
+// block case and the epilogue a row-contiguous 8- or 16-byte store.
+// Scales of a chunk of up to kChunk reduction blocks are staged in LDS as
+// E8M0 bytes.
+#include "fp8blk_device.h"
+#include "fp8blk_launch.h"
+
+namespace fp8blk {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+constexpr int kChunk = 32;  // reduction blocks whose scales sit in LDS at once
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, bool PROMOTE_, bool BROW_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int TM = WM / 16, TN = WN / 16;
+  static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+  static constexpr bool PROMOTE = PROMOTE_, BROW = BROW_;
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int SA_BYTES = kChunk * BM;
+  static constexpr int SB_BYTES = BROW ? kChunk * BN : kChunk * (BN / 128 > 0 ? BN / 128 : 1);
+  static constexpr int LDS = 2 * STAGE + SA_BYTES + ((SB_BYTES + 15) / 16) * 16;
+  static constexpr int A_LOADS = A_BYTES / 16 / THREADS;  // 16-byte chunks per thread
+  static constexpr int B_LOADS = B_BYTES / 16 / THREADS;
+  static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0, "tile/threads");
+  static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must sit inside one 128-block");
+  static_assert(TM % 4 == 0 || TM < 4, "scale bytes are read in words");
+};
+
+__device__ __forceinline__ uint32_t e8_of(float s) { return (__float_as_uint(s) >> 23) & 0xFFu; }
+__device__ __forceinline__ float f_of_e8(uint32_t e) { return __uint_as_float(e << 23); }
+
+// Read a 32-byte MFMA fragment: row `row` of a swizzled [rows][128 B] tile,
+// logical 16-byte chunks 2g and 2g+1.
+__device__ __forceinline__ v8i read_frag(const uint8_t* tile, uint32_t row, uint32_t g) {
+  const uint32_t sw = row & 7;
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + row * 128 + (((2 * g) ^ sw) << 4));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + row * 128 + (((2 * g + 1) ^ sw) << 4));
+  v8i f;
+  f[0] = (int)lo[0]; f[1] = (int)lo[1]; f[2] = (int)lo[2]; f[3] = (int)lo[3];
+  f[4] = (int)hi[0]; f[5] = (int)hi[1]; f[6] = (int)hi[2]; f[7] = (int)hi[3];
+  return f;
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t tiles_m, int64_t tiles_n,
+                                                          int64_t kb_per_split) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint8_t* const tiles = lds;
+  uint8_t* const sa_lds = lds + 2 * C::STAGE;
+  uint8_t* const sb_lds = sa_lds + C::SA_BYTES;
+
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63;
+  const uint32_t wave = tid >> 6;
+  const uint32_t wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const uint32_t l16 = lane & 15, g4 = lane >> 4;
+
+  // ---- which tile / split this workgroup owns
+  const int64_t ntiles = tiles_m * tiles_n;
+  const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t split = L / ntiles;
+  const int64_t tile = L - split * ntiles;
+  constexpr int64_t GM = 8;
+  const int64_t group = tile / (GM * tiles_n);
+  const int64_t first_m = group * GM;
+  const int64_t gsize = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+  const int64_t in_group = tile - group * GM * tiles_n;
+  const int64_t tm = first_m + in_group % gsize;
+  const int64_t tn = in_group / gsize;
+  const int64_t i0 = tm * C::BM, j0 = tn * C::BN;
+
+  const int64_t nkb = g.R / 128;
+  const int64_t kb_begin = split * kb_per_split;
+  const int64_t kb_end = (kb_begin + kb_per_split) < nkb ? (kb_begin + kb_per_split) : nkb;
+  const int64_t R = g.R;
+
+  // ---- global -> register staging of one reduction block's tiles
+  u32x4 ra[C::A_LOADS], rb[C::B_LOADS];
+  auto gload = [&](int64_t kb) {
+#pragma unroll
+    for (int u = 0; u < C::A_LOADS; ++u) {
+      const uint32_t c = tid + u * C::THREADS;
+      int64_t row = i0 + (c >> 3);
+      row = row < g.I ? row : g.I - 1;  // rows past the end of a half tile: valid memory, result unused
+      ra[u] = *reinterpret_cast<const u32x4*>(g.a + row * R + kb * 128 + (c & 7) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < C::B_LOADS; ++u) {
+      const uint32_t c = tid + u * C::THREADS;
+      int64_t row = j0 + (c >> 3);
+      row = row < g.J ? row : g.J - 1;
+      rb[u] = *reinterpret_cast<const u32x4*>(g.b + row * R + kb * 128 + (c & 7) * 16);
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint8_t* ta = tiles + buf * C::STAGE;
+    uint8_t* tb = ta + C::A_BYTES;
+#pragma unroll
+    for (int u = 0; u < C::A_LOADS; ++u) {
+      const uint32_t c = tid + u * C::THREADS;
+      const uint32_t row = c >> 3;
+      *reinterpret_cast<u32x4*>(ta + row * 128 + (((c & 7) ^ (row & 7)) << 4)) = ra[u];
+    }
+#pragma unroll
+    for (int u = 0; u < C::B_LOADS; ++u) {
+      const uint32_t c = tid + u * C::THREADS;
+      const uint32_t row = c >> 3;
+      *reinterpret_cast<u32x4*>(tb + row * 128 + (((c & 7) ^ (row & 7)) << 4)) = rb[u];
+    }
+  };
+  // ---- scales of reduction blocks [kb0, kb0 + n) -> LDS as E8M0 bytes.
+  // sa_lds[kbl][i % 16][i / 16]; row-mode B: promote keeps [kbl][j], the
+  // scaled MFMA wants [kbl][j % 16][j / 16]; block-mode B: [kbl][j / 128].
+  auto load_scales = [&](int64_t kb0, int64_t n) {
+    const int64_t nkb_all = nkb;
+    for (uint32_t idx = tid; idx < (uint32_t)(C::BM * kChunk); idx += C::THREADS) {
+      const uint32_t i = idx % C::BM, kbl = idx / C::BM;
+      if (kbl < n) {
+        int64_t row = i0 + i;
+        row = row < g.I ? row : g.I - 1;
+        sa_lds[kbl * C::BM + (i & 15) * (C::BM / 16) + (i >> 4)] = (uint8_t)e8_of(g.sa[row * nkb_all + kb0 + kbl]);
+      }
+    }
+    if constexpr (C::BROW) {
+      for (uint32_t idx = tid; idx < (uint32_t)(C::BN * kChunk); idx += C::THREADS) {
+        const uint32_t j = idx % C::BN, kbl = idx / C::BN;
+        if (kbl < n) {
+          int64_t row = j0 + j;
+          row = row < g.J ? row : g.J - 1;
+          const uint32_t pos = C::PROMOTE ? j : (j & 15) * (C::BN / 16) + (j >> 4);
+          sb_lds[kbl * C::BN + pos] = (uint8_t)e8_of(g.sb[row * nkb_all + kb0 + kbl]);
+        }
+      }
+    } else {
+      constexpr int NB = C::BN / 128;
+      for (uint32_t idx = tid; idx < (uint32_t)(NB * kChunk); idx += C::THREADS) {
+        const uint32_t jb = idx % NB, kbl = idx / NB;
+        if (kbl < n) {
+          int64_t jblk = (j0 >> 7) + jb;
+          jblk = jblk < (g.J >> 7) ? jblk : (g.J >> 7) - 1;
+          sb_lds[kbl * NB + jb] = (uint8_t)e8_of(g.sb[jblk * g.sb_j + (kb0 + kbl) * g.sb_r]);
+        }
+      }
+    }
+  };
+
+  v4f acc[C::TM][C::TN];
+#pragma unroll
+  for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+    for (int b = 0; b < C::TN; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t wm0 = wm * C::WM, wn0 = wn * C::WN;
+
+  if (kb_begin < kb_end) {
+    gload(kb_begin);
+    load_scales(kb_begin, (kb_end - kb_begin) < kChunk ? (kb_end - kb_begin) : kChunk);
+    lstore(0);
+    __syncthreads();
+  }
+  for (int64_t kb = kb_begin; kb < kb_end; ++kb) {
+    const int cur = (int)((kb - kb_begin) & 1);
+    const bool more = kb + 1 < kb_end;
+    if (more) gload(kb + 1);
+
+    const uint8_t* ta = tiles + cur * C::STAGE;
+    const uint8_t* tb = ta + C::A_BYTES;
+    const uint32_t kbl = (uint32_t)((kb - kb_begin) % kChunk);
+
+    // B fragments (the instruction's A operand) for the wave's TN sub-tiles
+    v8i bf[C::TN];
+#pragma unroll
+    for (int ns = 0; ns < C::TN; ++ns) bf[ns] = read_frag(tb, wn0 + ns * 16 + l16, g4);
+
+    // A-row scales for this lane's rows i = wm0 + ms*16 + l16, as bytes
+    uint32_t saw[(C::TM + 3) / 4];
+#pragma unroll
+    for (int w = 0; w < (C::TM + 3) / 4; ++w)
+      saw[w] = *reinterpret_cast<const uint32_t*>(sa_lds + kbl * C::BM + l16 * (C::BM / 16) + (wm0 >> 4) + 4 * w);
+
+    if constexpr (C::PROMOTE) {
+      // scale of the B side: one value (weight block) or 4 per sub-tile (rows)
+      float sbv[C::BROW ? C::TN : 1][C::BROW ? 4 : 1];
+      if constexpr (C::BROW) {
+#pragma unroll
+        for (int ns = 0; ns < C::TN; ++ns) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(sb_lds + kbl * C::BN + wn0 + ns * 16 + g4 * 4);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) sbv[ns][t] = f_of_e8((w >> (8 * t)) & 0xFF);
+        }
+      } else {
+        sbv[0][0] = f_of_e8(sb_lds[kbl * (C::BN / 128) + (wn0 >> 7)]);
+      }
+#pragma unroll
+      for (int ms = 0; ms < C::TM; ++ms) {
+        const v8i af = read_frag(ta, wm0 + ms * 16 + l16, g4);
+        const float sa = f_of_e8((saw[ms >> 2] >> (8 * (ms & 3))) & 0xFF);
+#pragma unroll
+        for (int ns = 0; ns < C::TN; ++ns) {
+          const v4f z = {0.f, 0.f, 0.f, 0.f};
+          const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[ns], af, z, 0, 0, 0, 0, 0, 0);
+          if constexpr (C::BROW) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[ms][ns][t] = __builtin_fmaf(p[t], sa * sbv[ns][t], acc[ms][ns][t]);
+          } else {
+            const float sc = sa * sbv[0][0];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[ms][ns][t] = __builtin_fmaf(p[t], sc, acc[ms][ns][t]);
+          }
+        }
+      }
+    } else {
+      // scaled MFMA: every lane passes the E8M0 byte of its own operand row
+      uint32_t sbw[(C::TN + 3) / 4];
+      if constexpr (C::BROW) {
+#pragma unroll
+        for (int w = 0; w < (C::TN + 3) / 4; ++w)
+          sbw[w] = *reinterpret_cast<const uint32_t*>(sb_lds + kbl * C::BN + l16 * (C::BN / 16) + (wn0 >> 4) + 4 * w);
+      } else {
+        const uint32_t e = sb_lds[kbl * (C::BN / 128) + (wn0 >> 7)];
+#pragma unroll
+        for (int w = 0; w < (C::TN + 3) / 4; ++w) sbw[w] = e * 0x01010101u;
+      }
+#pragma unroll
+      for (int ms = 0; ms < C::TM; ++ms) {
+        const v8i af = read_frag(ta, wm0 + ms * 16 + l16, g4);
+#pragma unroll
+        for (int ns = 0; ns < C::TN; ++ns) {
+#define FP8BLK_MFMA_SCALED(OA, OB)                                                                            \
+  acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[ns], af, acc[ms][ns], 0, 0, OA,           \
+                                                                  (int)sbw[ns >> 2], OB, (int)saw[ms >> 2])
+          // op_sel picks the byte of the scale word; it must be a constant
+          switch (((ns & 3) << 2) | (ms & 3)) {
+            case 0: FP8BLK_MFMA_SCALED(0, 0); break;
+            case 1: FP8BLK_MFMA_SCALED(0, 1); break;
+            case 2: FP8BLK_MFMA_SCALED(0, 2); break;
+            case 3: FP8BLK_MFMA_SCALED(0, 3); break;
+            case 4: FP8BLK_MFMA_SCALED(1, 0); break;
+            case 5: FP8BLK_MFMA_SCALED(1, 1); break;
+            case 6: FP8BLK_MFMA_SCALED(1, 2); break;
+            case 7: FP8BLK_MFMA_SCALED(1, 3); break;
+            case 8: FP8BLK_MFMA_SCALED(2, 0); break;
+            case 9: FP8BLK_MFMA_SCALED(2, 1); break;
+            case 10: FP8BLK_MFMA_SCALED(2, 2); break;
+            case 11: FP8BLK_MFMA_SCALED(2, 3); break;
+            case 12: FP8BLK_MFMA_SCALED(3, 0); break;
+            case 13: FP8BLK_MFMA_SCALED(3, 1); break;
+            case 14: FP8BLK_MFMA_SCALED(3, 2); break;
+            default: FP8BLK_MFMA_SCALED(3, 3); break;
+          }
+#undef FP8BLK_MFMA_SCALED
+        }
+      }
+    }
+
+    if (more) {
+      if ((kb + 1 - kb_begin) % kChunk == 0) {
+        __syncthreads();  // everyone is done with this chunk's scales
+        const int64_t rest = kb_end - (kb + 1);
+        load_scales(kb + 1, rest < kChunk ? rest : kChunk);
+      }
+      lstore(cur ^ 1);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds out[i0+wm0+ms*16+l16][j0+wn0+ns*16+g4*4 .. +3]
+#pragma unroll
+  for (int ms = 0; ms < C::TM; ++ms) {
+    const int64_t i = i0 + wm0 + ms * 16 + l16;
+    if (i >= g.I) continue;
+#pragma unroll
+    for (int ns = 0; ns < C::TN; ++ns) {
+      const int64_t j = j0 + wn0 + ns * 16 + g4 * 4;
+      if (j >= g.J) continue;
+      const v4f v = acc[ms][ns];
+      if (g.splits > 1) {
+        float* dst = g.ws + split * g.I * g.J + i * g.J + j;
+        *reinterpret_cast<v4f*>(dst) = v;
+      } else if (g.out_f32) {
+        *reinterpret_cast<v4f*>(static_cast<float*>(g.out) + i * g.J + j) = v;
+      } else {
+        uint2 o;
+        o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+        o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + i * g.J + j) = o;
+      }
+    }
+  }
+}
+
+// Deterministic split-K reduction: out[idx] = sum over s in order of ws[s][idx].
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int splits, int64_t n4,
+                                                            void* out, bool out_f32) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < n4; v += stride) {
+    v4f s = reinterpret_cast<const v4f*>(ws)[v];
+    for (int k = 1; k < splits; ++k) {
+      const v4f t = reinterpret_cast<const v4f*>(ws + (int64_t)k * n4 * 4)[v];
+      s[0] += t[0]; s[1] += t[1]; s[2] += t[2]; s[3] += t[3];
+    }
+    if (out_f32) {
+      reinterpret_cast<v4f*>(out)[v] = s;
+    } else {
+      uint2 o;
+      o.x = f32_to_bf16_rne(s[0]) | (f32_to_bf16_rne(s[1]) << 16);
+      o.y = f32_to_bf16_rne(s[2]) | (f32_to_bf16_rne(s[3]) << 16);
+      reinterpret_cast<uint2*>(out)[v] = o;
+    }
+  }
+}
+
+// ------------------------------------------------------------ dispatch ----
+
+using PromoteBlock = Cfg<256, 128, 2, 2, true, false>;
+using PromoteRow = Cfg<256, 128, 2, 2, true, true>;
+using ScaledBlock = Cfg<256, 128, 2, 2, false, false>;
+using ScaledRow = Cfg<256, 128, 2, 2, false, true>;
+
+constexpr int kCUs = 256;
+
+int gemm_splits(int64_t I, int64_t J, int64_t R, BScale bmode) {
+  if (bmode == BScale::Block) return 1;
+  const int64_t tiles = ((I + 255) / 256) * ((J + 255) / 256);
+  const int64_t nkb = R / 128;
+  int s = 1;
+  // split the reduction until the grid covers the CUs, keeping >= 8 blocks per slice
+  while (tiles * s < kCUs && nkb / (2 * s) >= 8) s *= 2;
+  return s;
+}
+
+size_t gemm_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode) {
+  const int s = gemm_splits(I, J, R, bmode);
+  return s > 1 ? (size_t)s * (size_t)I * (size_t)J * sizeof(float) : 0;
+}
+
+template <class C>
+static hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
+  const int64_t tiles_m = (g.I + C::BM - 1) / C::BM;
+  const int64_t tiles_n = (g.J + C::BN - 1) / C::BN;
+  const int64_t nkb = g.R / 128;
+  const int splits = g.splits > 0 ? g.splits : 1;
+  const int64_t kb_per_split = (nkb + splits - 1) / splits;
+  const int64_t blocks = tiles_m * tiles_n * splits;
+  static bool attr_set = false;  // idempotent; a race only repeats the same call
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<C>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(gemm_kernel<C>, dim3((uint32_t)blocks), dim3(C::THREADS), C::LDS, stream, g, tiles_m, tiles_n,
+                     kb_per_split);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t n4 = g.I * g.J / 4;
+  int64_t rblocks = (n4 + 255) / 256;
+  if (rblocks > 4096) rblocks = 4096;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)rblocks), dim3(256), 0, stream, g.ws, splits, n4, g.out,
+                     g.out_f32);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& g, GemmAlgo algo, hipStream_t stream) {
+  if (algo == GemmAlgo::Promote)
+    return g.bmode == BScale::Row ? launch_cfg<PromoteRow>(g, stream) : launch_cfg<PromoteBlock>(g, stream);
+  return g.bmode == BScale::Row ? launch_cfg<ScaledRow>(g, stream) : launch_cfg<ScaledBlock>(g, stream);
+}
+
+}  // namespace fp8blk

@@ -1,0 +1,241 @@
+// Quantizer kernels for gfx950: bf16 -> E4M3 codes + power-of-two fp32 scales.
+//
+// What is computed ("Puro-2B ... part 3/7", section 3.2, second and third
+// paragraphs): one scale per 128 consecutive values along the GEMM reduction
+// dimension for activations and gradients, one per 128x128 block for weights;
+// each scale a power of two.  The scale rule and the cast are the readings
+// stated in include/fp8blk.h.
+//
+// All three kernels are bound by HBM bandwidth (about 3 bytes moved per
+// element for 0.1 flop), so the design work is in the memory access pattern:
+// 16-byte loads, full 128-byte lines per store instruction where the layout
+// allows, and enough independent loads in flight per wave.  The amax is an
+// exact integer max over the bf16 magnitude bits, reduced across lanes with
+// DPP; the scale exponent comes from the amax bits with integer ops.
+#include "fp8blk_device.h"
+#include "fp8blk_launch.h"
+
+namespace fp8blk {
+
+// ---------------------------------------------------------------------------
+// Row groups.  A DPP row (16 lanes) owns one 128-element group: each lane
+// loads 8 bf16 (16 B), the row's 16 lanes cover the group's 256 B.  A wave
+// handles 4 groups per step and kRowUnroll steps, all loads issued first.
+// ---------------------------------------------------------------------------
+constexpr int kRowUnroll = 4;
+constexpr int kRowThreads = 256;
+constexpr int kGroupsPerWave = 4 * kRowUnroll;
+
+__global__ __launch_bounds__(kRowThreads) void quant_rowgroup_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q,
+    float* __restrict__ s, uint32_t groups_per_row, uint32_t total_groups) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t sub = lane >> 4;   // which of the wave's 4 groups in a step
+  const uint32_t l16 = lane & 15;   // 16-byte chunk within the group
+  const uint32_t wave = blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
+  const uint32_t g0 = wave * kGroupsPerWave;
+
+  u32x4 v[kRowUnroll];
+  uint32_t row[kRowUnroll], col[kRowUnroll];
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) {
+    uint32_t g = g0 + u * 4 + sub;
+    bool ok = g < total_groups;
+    uint32_t gg = ok ? g : 0;
+    row[u] = gg / groups_per_row;
+    col[u] = gg - row[u] * groups_per_row;
+    const u32x4* p = reinterpret_cast<const u32x4*>(x + (int64_t)row[u] * ld_x + col[u] * 128 + l16 * 8);
+    v[u] = ok ? __builtin_nontemporal_load(p) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) {
+    uint32_t g = g0 + u * 4 + sub;
+    uint32_t m = pk_max_u16(pk_max_u16(abs2(v[u].x), abs2(v[u].y)), pk_max_u16(abs2(v[u].z), abs2(v[u].w)));
+    m = max(m & 0xFFFFu, m >> 16);
+    m = row16_max(m);
+    int e = scale_exponent(m);
+    float inv = pow2f(-e);
+    uint2 out;
+    out.x = quant4(v[u].x, v[u].y, inv);
+    out.y = quant4(v[u].z, v[u].w, inv);
+    if (g < total_groups) {
+      *reinterpret_cast<uint2*>(q + (int64_t)row[u] * ld_q + col[u] * 128 + l16 * 8) = out;
+      if (l16 == 0) s[(int64_t)row[u] * groups_per_row + col[u]] = pow2f(e);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Column groups (groups of 128 consecutive rows of one column, written
+// transposed).  A workgroup takes a 128-row x 64-column tile: coalesced
+// 16-byte row loads into LDS, then each thread owns two adjacent columns
+// over 16 consecutive rows.  The 8 threads sharing a column pair reduce the
+// amax with DPP and each writes 16 codes, so a column's 128 codes leave as
+// one contiguous 128-byte line of qT.
+// LDS tile: 128 rows x 32 words (column pairs), the word index XOR-swizzled
+// by ((row / 16) & 3) * 8 so the column-pair reads hit distinct banks.
+// ---------------------------------------------------------------------------
+constexpr int kColTileRows = 128;
+constexpr int kColTileCols = 64;
+constexpr int kColThreads = 256;
+
+__device__ __forceinline__ uint32_t col_swz(uint32_t r) { return ((r >> 4) & 3) << 3; }
+
+__global__ __launch_bounds__(kColThreads) void quant_colgroup_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ qT, int64_t ld_qT,
+    float* __restrict__ sT, uint32_t row_tiles, uint32_t col_tiles) {
+  __shared__ uint32_t tile[kColTileRows * 32];
+  const uint32_t t = threadIdx.x;
+  const uint32_t logical = xcd_remap(blockIdx.x, row_tiles * col_tiles);
+  const uint32_t ct = logical / row_tiles;   // consecutive logical ids walk down the rows
+  const uint32_t rt = logical - ct * row_tiles;
+  const int64_t m0 = (int64_t)rt * kColTileRows;
+  const int64_t c0 = (int64_t)ct * kColTileCols;
+
+  // load: 8 threads per row (16 B = 4 column pairs each), 32 rows per pass
+  {
+    const uint32_t chunk = t & 7;
+    const uint32_t r0 = t >> 3;
+    u32x4 v[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t r = r0 + 32 * p;
+      v[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (m0 + r) * ld_x + c0 + chunk * 8));
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t r = r0 + 32 * p;
+      *reinterpret_cast<u32x4*>(&tile[r * 32 + ((chunk * 4) ^ col_swz(r))]) = v[p];
+    }
+  }
+  __syncthreads();
+
+  const uint32_t lane = t & 63;
+  const uint32_t rp = lane & 7;                       // row part: rows rp*16 .. +15
+  const uint32_t cp = (t >> 6) * 8 + (lane >> 3);     // column pair 0..31
+  uint32_t w[16];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t r = rp * 16 + i;
+    w[i] = tile[r * 32 + (cp ^ col_swz(r))];
+    m = pk_max_u16(m, abs2(w[i]));
+  }
+  m = lane8_max_pk(m);
+  const int e0 = scale_exponent(m & 0xFFFFu);
+  const int e1 = scale_exponent(m >> 16);
+  const float inv0 = pow2f(-e0), inv1 = pow2f(-e1);
+  u32x4 o0, o1;
+  o0.x = quant4_sel(bf16_lo(w[0]), bf16_lo(w[1]), bf16_lo(w[2]), bf16_lo(w[3]), inv0);
+  o0.y = quant4_sel(bf16_lo(w[4]), bf16_lo(w[5]), bf16_lo(w[6]), bf16_lo(w[7]), inv0);
+  o0.z = quant4_sel(bf16_lo(w[8]), bf16_lo(w[9]), bf16_lo(w[10]), bf16_lo(w[11]), inv0);
+  o0.w = quant4_sel(bf16_lo(w[12]), bf16_lo(w[13]), bf16_lo(w[14]), bf16_lo(w[15]), inv0);
+  o1.x = quant4_sel(bf16_hi(w[0]), bf16_hi(w[1]), bf16_hi(w[2]), bf16_hi(w[3]), inv1);
+  o1.y = quant4_sel(bf16_hi(w[4]), bf16_hi(w[5]), bf16_hi(w[6]), bf16_hi(w[7]), inv1);
+  o1.z = quant4_sel(bf16_hi(w[8]), bf16_hi(w[9]), bf16_hi(w[10]), bf16_hi(w[11]), inv1);
+  o1.w = quant4_sel(bf16_hi(w[12]), bf16_hi(w[13]), bf16_hi(w[14]), bf16_hi(w[15]), inv1);
+  const int64_t c = c0 + 2 * cp;
+  *reinterpret_cast<u32x4*>(qT + c * ld_qT + m0 + rp * 16) = o0;
+  *reinterpret_cast<u32x4*>(qT + (c + 1) * ld_qT + m0 + rp * 16) = o1;
+  if (rp == 0) {
+    const int64_t G = (int64_t)row_tiles;  // rows / 128 groups per column
+    sT[c * G + rt] = pow2f(e0);
+    sT[(c + 1) * G + rt] = pow2f(e1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 weight blocks.  One workgroup per block, 256 threads: thread
+// (rg, cg) owns rows rg*8 .. +7 and columns cg*8 .. +7 (one 16-byte load per
+// row).  The block amax is reduced over the wave with DPP/shuffles and over
+// the 4 waves through LDS.  Row-major codes leave 8 bytes per lane (16 lanes
+// = one 128-byte line per row); the optional transposed copy is built in
+// registers with byte permutes (8x8 per thread) and leaves 8 bytes per lane.
+// ---------------------------------------------------------------------------
+constexpr int kBlkThreads = 256;
+
+__global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
+    const uint16_t* __restrict__ w, int64_t ld_w, uint8_t* __restrict__ q, uint8_t* __restrict__ qT,
+    float* __restrict__ s, int64_t rows, int64_t cols, uint32_t row_blocks, uint32_t col_blocks) {
+  __shared__ uint32_t red[kBlkThreads / 64];
+  const uint32_t t = threadIdx.x;
+  const uint32_t logical = xcd_remap(blockIdx.x, row_blocks * col_blocks);
+  const uint32_t bi = logical / col_blocks;
+  const uint32_t bj = logical - bi * col_blocks;
+  const uint32_t cg = t & 15;
+  const uint32_t rg = t >> 4;                 // 0..15
+  const int64_t r0 = (int64_t)bi * 128 + rg * 8;
+  const int64_t cc0 = (int64_t)bj * 128 + cg * 8;
+
+  u32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w + (r0 + i) * ld_w + cc0));
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    m = pk_max_u16(m, pk_max_u16(pk_max_u16(abs2(v[i].x), abs2(v[i].y)), pk_max_u16(abs2(v[i].z), abs2(v[i].w))));
+  m = max(m & 0xFFFFu, m >> 16);
+  m = wave_max(m);
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  const int e = scale_exponent(m);
+  const float inv = pow2f(-e);
+
+  uint32_t lo[8], hi[8];  // codes of row i: columns 0..3 in lo[i], 4..7 in hi[i]
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    lo[i] = quant4(v[i].x, v[i].y, inv);
+    hi[i] = quant4(v[i].z, v[i].w, inv);
+    *reinterpret_cast<uint2*>(q + (r0 + i) * cols + cc0) = make_uint2(lo[i], hi[i]);
+  }
+  if (qT != nullptr) {
+    uint32_t a[4], b[4];
+    // columns 0..3: rows 0..3 then rows 4..7
+    transpose4x4(&lo[0], a);
+    transpose4x4(&lo[4], b);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<uint2*>(qT + (cc0 + c) * rows + r0) = make_uint2(a[c], b[c]);
+    transpose4x4(&hi[0], a);
+    transpose4x4(&hi[4], b);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<uint2*>(qT + (cc0 + 4 + c) * rows + r0) = make_uint2(a[c], b[c]);
+  }
+  if (t == 0) s[(int64_t)bi * col_blocks + bj] = pow2f(e);
+}
+
+// ------------------------------------------------------------- launchers ---
+
+hipError_t launch_quant_rowgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                                 int64_t ld_q, float* s, hipStream_t stream) {
+  const uint32_t gpr = (uint32_t)(cols / 128);
+  const uint32_t total = (uint32_t)(rows * gpr);
+  const uint32_t waves = (total + kGroupsPerWave - 1) / kGroupsPerWave;
+  const uint32_t blocks = (waves + (kRowThreads / 64) - 1) / (kRowThreads / 64);
+  hipLaunchKernelGGL(quant_rowgroup_kernel, dim3(blocks), dim3(kRowThreads), 0, stream, x, ld_x, q, ld_q, s, gpr,
+                     total);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_colgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qT,
+                                 int64_t ld_qT, float* sT, hipStream_t stream) {
+  const uint32_t rt = (uint32_t)(rows / kColTileRows);
+  const uint32_t ct = (uint32_t)(cols / kColTileCols);
+  hipLaunchKernelGGL(quant_colgroup_kernel, dim3(rt * ct), dim3(kColThreads), 0, stream, x, ld_x, qT, ld_qT, sT, rt,
+                     ct);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld_w, uint8_t* q, uint8_t* qT,
+                              float* s, hipStream_t stream) {
+  const uint32_t rb = (uint32_t)(rows / 128);
+  const uint32_t cb = (uint32_t)(cols / 128);
+  hipLaunchKernelGGL(quant_block_kernel, dim3(rb * cb), dim3(kBlkThreads), 0, stream, w, ld_w, q, qT, s, rows, cols,
+                     rb, cb);
+  return hipGetLastError();
+}
+
+}  // namespace fp8blk

@@ -1,0 +1,202 @@
+/*
+ * fp8blk.h -- C ABI of the blockwise-FP8 Transformer linear layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (sources, cited by title and section):
+ *   "Puro-2B: Poor Lab's Qwen2-1.5B Trained on RTX 5090 within $5090"
+ *   (arXiv HTML, part 3/7), section 3.2 "FP8 Mixed-Precision Training":
+ *     - Transformer linear layers take E4M3 operands; the BF16 inputs and
+ *       weights are quantized right before each GEMM and a BF16 output is
+ *       materialised (fourth paragraph);
+ *     - activations and activation gradients get one scale per 128
+ *       consecutive values along the GEMM reduction dimension, weights one
+ *       scale per 128x128 block (second paragraph);
+ *     - every block scale is a power of two, i.e. it has the expressiveness
+ *       of an E8M0 exponent (third paragraph);
+ *     - Fprop, Dgrad and Wgrad of the QKV, attention-output and MLP
+ *       projections all take this path, and the quantized input is kept for
+ *       Wgrad (fourth paragraph).
+ *   The Chinese study notes of the same paper, section 2.3 (table of the FP8
+ *   boundary), state the same grouping and power-of-two scales, with FP32
+ *   accumulation.
+ *
+ * Readings where the pages are silent (the same readings as the CPU oracle):
+ *   - E4M3 is the OCP "fn" variant (bias 7, max 448, no infinities).
+ *   - scale s = 2^e, e the smallest integer with amax <= 448 * 2^e, clamped to
+ *     [-126, 127]; an all-zero group has s = 1.  s is the dequantisation
+ *     multiplier (x ~ decode(q) * s) and is stored as fp32.
+ *   - q = round-to-nearest-even(x / s) to E4M3, saturating at +-448 (under
+ *     the rule above |x / s| never exceeds 448); the sign of zero is kept.
+ *   - out[i][j] = sum over 128-deep reduction blocks b of
+ *       sa(i, b) * sb(j, b) * sum_{r in b} dec(A[i][r]) * dec(B[j][r]),
+ *     accumulated in fp32, rounded to bf16 (RNE) or returned as fp32.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are row-major.  bf16 values are passed as their raw 16-bit
+ *     patterns (uint16_t), E4M3 codes as uint8_t, scales as float.
+ *   - Dimensions and leading dimensions are in elements, int64_t.
+ *   - Pointers are DEVICE pointers on the current HIP device.  The caller
+ *     owns every buffer; the library allocates nothing, keeps no pointer
+ *     after returning and holds no mutable global state.
+ *   - Every call only enqueues work on `stream` (0 = the null stream) and
+ *     never synchronises; results are valid once the stream has progressed
+ *     past the call.  Outputs must not alias inputs.
+ *   - Return value: FP8BLK_OK (0), or a negative FP8BLK_ERR_* code.  All
+ *     argument checks run on the host before any launch: on an error nothing
+ *     is enqueued and no output is touched.  No C++ exception crosses the ABI.
+ *   - Scales handed to the GEMMs must be exact powers of two in
+ *     [2^-126, 2^127], as the quantizers produce; the GEMMs use only their
+ *     exponent bits.
+ */
+#ifndef FP8BLK_H
+#define FP8BLK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Scale rule.  Only the power-of-two rule is implemented. */
+enum fp8blk_scale_mode { FP8BLK_SCALE_POW2 = 0 };
+
+/* GEMM output element type. */
+enum fp8blk_out_dtype { FP8BLK_OUT_BF16 = 0, FP8BLK_OUT_FP32 = 1 };
+
+/* Which contraction (for fp8_block_gemm and the workspace query). */
+enum fp8blk_op { FP8BLK_OP_FPROP = 0, FP8BLK_OP_DGRAD = 1, FP8BLK_OP_WGRAD = 2 };
+
+/* How the per-block scale product reaches the fp32 accumulators.
+ *   PROMOTE:     one MFMA per 128-deep reduction block starting from zero,
+ *                then acc += P * (sa * sb) on the vector ALU;
+ *   SCALED_MFMA: gfx950's block-scaled MFMA multiplies each operand row by
+ *                its power-of-two scale (E8M0) inside the matrix core and
+ *                accumulates in place.
+ * Both compute the same sum of exactly scaled block products in fp32; they
+ * differ only in rounding order.  DEFAULT picks the faster one. */
+enum fp8blk_gemm_algo { FP8BLK_ALGO_DEFAULT = 0, FP8BLK_ALGO_PROMOTE = 1, FP8BLK_ALGO_SCALED_MFMA = 2 };
+
+/* Status codes. */
+enum fp8blk_status {
+    FP8BLK_OK = 0,
+    FP8BLK_ERR_NULL = -1,      /* a required pointer is NULL */
+    FP8BLK_ERR_DIM = -2,       /* a dimension is <= 0 or not a multiple of 128 */
+    FP8BLK_ERR_ALIGN = -3,     /* a pointer or leading dimension is not 16-byte aligned */
+    FP8BLK_ERR_ARG = -4,       /* bad enum, leading dimension smaller than the row, or too large */
+    FP8BLK_ERR_WORKSPACE = -5, /* workspace smaller than fp8_block_gemm_workspace_size() */
+    FP8BLK_ERR_HIP = -6,       /* the HIP runtime reported an error at launch */
+    FP8BLK_ERR_DEVICE = -7     /* the current device is not gfx950 */
+};
+
+/*
+ * Row-group quantization (section 3.2, second paragraph: groups of 128 along
+ * the reduction dimension).  Used for X before Fprop and for dY before Dgrad.
+ *   x    [rows][cols] bf16, row stride ld_x (>= cols, multiple of 8)
+ *   q    [rows][cols] E4M3 codes, row stride ld_q (>= cols, multiple of 16)
+ *   s    [rows][cols/128] fp32 scales, dense
+ *   rows >= 1 (any value); cols a positive multiple of 128.
+ *   x and q 16-byte aligned, s 4-byte aligned.
+ */
+int fp8_quantize_rowgroup(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                          uint8_t *q, int64_t ld_q, float *s, int scale_mode,
+                          hipStream_t stream);
+
+/*
+ * Column-group quantization: the same rule with groups of 128 consecutive
+ * ROWS (tokens) of each column, the reduction dimension of Wgrad; the output
+ * is written transposed so that Wgrad reads it contiguously along tokens.
+ * This is the quantized copy of the input kept for Wgrad (section 3.2,
+ * fourth paragraph).  colgroup(x) equals rowgroup(x^T) bit for bit.
+ *   x    [rows][cols] bf16, row stride ld_x (>= cols, multiple of 8)
+ *   qT   [cols][rows] E4M3 codes, row stride ld_qT (>= rows, multiple of 16)
+ *   sT   [cols][rows/128] fp32 scales, dense
+ *   rows and cols positive multiples of 128.
+ */
+int fp8_quantize_colgroup(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                          uint8_t *qT, int64_t ld_qT, float *sT, int scale_mode,
+                          hipStream_t stream);
+
+/*
+ * Weight block quantization (section 3.2, second paragraph: 128x128 blocks).
+ *   w    [rows][cols] bf16 (rows = out features N, cols = in features K),
+ *        row stride ld_w (>= cols, multiple of 8)
+ *   q    [rows][cols] E4M3 codes, dense
+ *   qT   optional (NULL to skip): [cols][rows] E4M3 codes, dense -- the
+ *        transposed copy that Dgrad reads (block scales are the same)
+ *   s    [rows/128][cols/128] fp32 scales, dense
+ *   rows and cols positive multiples of 128.
+ */
+int fp8_quantize_block(const uint16_t *w, int64_t rows, int64_t cols, int64_t ld_w,
+                       uint8_t *q, uint8_t *qT, float *s, int scale_mode,
+                       hipStream_t stream);
+
+/*
+ * Fprop  Y = X W^T  (section 3.2, fourth paragraph).
+ *   qx [M][K] codes + sx [M][K/128]   (from fp8_quantize_rowgroup of X)
+ *   qw [N][K] codes + sw [N/128][K/128] (from fp8_quantize_block of W)
+ *   y  [M][N], bf16 bits (out_dtype FP8BLK_OUT_BF16) or fp32 (FP8BLK_OUT_FP32)
+ *   M, N, K positive multiples of 128; all operands dense.
+ */
+int fp8_block_gemm_fprop(int64_t M, int64_t N, int64_t K,
+                         const uint8_t *qx, const float *sx,
+                         const uint8_t *qw, const float *sw,
+                         void *y, int out_dtype, hipStream_t stream);
+
+/*
+ * Dgrad  dX = dY W  (section 3.2, fourth paragraph).
+ *   qdy [M][N] codes + sdy [M][N/128]  (from fp8_quantize_rowgroup of dY)
+ *   qwT [K][N] codes (the transposed copy from fp8_quantize_block of W)
+ *   sw  [N/128][K/128] the same block scales as Fprop
+ *   dx  [M][K], bf16 bits or fp32
+ */
+int fp8_block_gemm_dgrad(int64_t M, int64_t N, int64_t K,
+                         const uint8_t *qdy, const float *sdy,
+                         const uint8_t *qwT, const float *sw,
+                         void *dx, int out_dtype, hipStream_t stream);
+
+/*
+ * Wgrad  dW = dY^T X  (section 3.2, fourth paragraph); the reduction runs
+ * over the M tokens, so both operands are column-group quantized.
+ *   qdyT [N][M] codes + sdyT [N][M/128]  (fp8_quantize_colgroup of dY)
+ *   qxT  [K][M] codes + sxT  [K][M/128]  (fp8_quantize_colgroup of X)
+ *   dw   [N][K], bf16 bits or fp32
+ *   workspace: device memory of at least
+ *     fp8_block_gemm_workspace_size(FP8BLK_OP_WGRAD, M, N, K) bytes (fp32
+ *     split-K partials, reduced in a fixed order: results are deterministic);
+ *     may be NULL when that size is 0.
+ */
+int fp8_block_gemm_wgrad(int64_t M, int64_t N, int64_t K,
+                         const uint8_t *qdyT, const float *sdyT,
+                         const uint8_t *qxT, const float *sxT,
+                         void *dw, int out_dtype,
+                         void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * All three contractions through one entry point, with an explicit algorithm.
+ *   op = FP8BLK_OP_FPROP: (a, sa, b, sb) = (qx, sx, qw, sw),    out [M][N]
+ *   op = FP8BLK_OP_DGRAD: (a, sa, b, sb) = (qdy, sdy, qwT, sw), out [M][K]
+ *   op = FP8BLK_OP_WGRAD: (a, sa, b, sb) = (qdyT, sdyT, qxT, sxT), out [N][K]
+ * Operand layouts, workspace and errors are as for the named functions above
+ * (which are this call with FP8BLK_ALGO_DEFAULT); a bad op or algo gives
+ * FP8BLK_ERR_ARG.
+ */
+int fp8_block_gemm(int op, int64_t M, int64_t N, int64_t K,
+                   const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
+                   void *out, int out_dtype, int algo,
+                   void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes that the given contraction needs at this shape (0 if none;
+ * (size_t)-1 for an invalid op or shape). */
+size_t fp8_block_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K);
+
+/* Human-readable text for a status code (static storage). */
+const char *fp8_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BLK_H */

@@ -1,0 +1,120 @@
+"""The C ABI, checked without a GPU: the library loads, exports every
+function include/fp8blk.h declares, and every host-side argument check
+returns its documented status before anything is launched (the pointers
+below are never dereferenced: each call fails validation first)."""
+import ctypes
+
+import pytest
+
+import blockwise_fp8_linear_amd as fb
+
+OK, ENULL, EDIM, EALIGN, EARG, EWS, EHIP, EDEV = 0, -1, -2, -3, -4, -5, -6, -7
+P = 0x100000          # a fake, 16-byte aligned device address (never used)
+P2 = 0x200000
+P3 = 0x300000
+MIS = 0x100008        # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fb.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = fb.header_functions()
+    assert set(names) == {
+        "fp8_quantize_rowgroup", "fp8_quantize_colgroup", "fp8_quantize_block",
+        "fp8_block_gemm_fprop", "fp8_block_gemm_dgrad", "fp8_block_gemm_wgrad",
+        "fp8_block_gemm", "fp8_block_gemm_workspace_size", "fp8_status_string",
+    }
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for rc in (OK, ENULL, EDIM, EALIGN, EARG, EWS, EHIP, EDEV):
+        assert fb.fp8_status_string(rc)
+    assert "unknown" in fb.fp8_status_string(-99)
+
+
+def test_rowgroup_errors(lib):
+    f = lib.fp8_quantize_rowgroup
+    assert f(P, 4, 256, 256, P2, 256, P3, 1, None) == EARG      # scale mode
+    assert f(None, 4, 256, 256, P2, 256, P3, 0, None) == ENULL
+    assert f(P, 4, 256, 256, None, 256, P3, 0, None) == ENULL
+    assert f(P, 4, 256, 256, P2, 256, None, 0, None) == ENULL
+    assert f(P, 0, 256, 256, P2, 256, P3, 0, None) == EDIM      # empty
+    assert f(P, 4, 200, 256, P2, 256, P3, 0, None) == EDIM      # ragged cols
+    assert f(P, 4, 0, 256, P2, 256, P3, 0, None) == EDIM
+    assert f(P, 4, 256, 128, P2, 256, P3, 0, None) == EARG      # ld < cols
+    assert f(P, 4, 256, 256, P2, 128, P3, 0, None) == EARG
+    assert f(MIS, 4, 256, 256, P2, 256, P3, 0, None) == EALIGN
+    assert f(P, 4, 256, 260, P2, 256, P3, 0, None) == EALIGN    # ld_x not a multiple of 8
+    assert f(P, 4, 256, 256, P2, 264, P3, 0, None) == EALIGN    # ld_q not a multiple of 16
+    assert f(P, 4, 256, 256, P2, 256, P3 + 2, 0, None) == EALIGN
+
+
+def test_colgroup_and_block_errors(lib):
+    f = lib.fp8_quantize_colgroup
+    assert f(P, 200, 256, 256, P2, 256, P3, 0, None) == EDIM    # rows must be a multiple of 128
+    assert f(P, 256, 256, 256, P2, 128, P3, 0, None) == EARG    # ld_qT < rows
+    assert f(None, 256, 256, 256, P2, 256, P3, 0, None) == ENULL
+    assert f(P, 256, 256, 256, MIS, 256, P3, 0, None) == EALIGN
+    g = lib.fp8_quantize_block
+    assert g(P, 256, 384, 384, P2, None, P3, 0, None) != ENULL  # qT may be NULL (fails later: no GPU)
+    assert g(P, 256, 300, 384, P2, None, P3, 0, None) == EDIM
+    assert g(P, 256, 384, 256, P2, None, P3, 0, None) == EARG
+    assert g(P, 256, 384, 384, P2, MIS, P3, 0, None) == EALIGN
+    assert g(P, 256, 384, 384, P2, None, P3, 7, None) == EARG
+
+
+def test_gemm_errors(lib):
+    f = lib.fp8_block_gemm_fprop
+    assert f(256, 256, 256, P, P3, P2, P3, P, 5, None) == EARG           # out dtype
+    assert f(256, 256, 256, None, P3, P2, P3, P, 0, None) == ENULL
+    assert f(256, 256, 256, P, P3, P2, None, P, 0, None) == ENULL
+    assert f(256, 200, 256, P, P3, P2, P3, P, 0, None) == EDIM
+    assert f(0, 256, 256, P, P3, P2, P3, P, 0, None) == EDIM
+    assert f(256, 256, 256, MIS, P3, P2, P3, P, 0, None) == EALIGN
+    assert f(256, 256, 256, P, P3 + 1, P2, P3, P, 0, None) == EALIGN
+    g = lib.fp8_block_gemm
+    assert g(3, 256, 256, 256, P, P3, P2, P3, P, 0, 0, None, 0, None) == EARG   # op
+    assert g(0, 256, 256, 256, P, P3, P2, P3, P, 0, 9, None, 0, None) == EARG   # algo
+    # wgrad at a shape that splits the reduction needs a workspace
+    need = lib.fp8_block_gemm_workspace_size(2, 8192, 256, 256)
+    assert need > 0
+    w = lib.fp8_block_gemm_wgrad
+    assert w(8192, 256, 256, P, P3, P2, P3, P, 0, None, 0, None) == EWS
+    assert w(8192, 256, 256, P, P3, P2, P3, P, 0, P, need - 1, None) == EWS
+    assert w(8192, 256, 256, P, P3, P2, P3, P, 0, MIS, need, None) == EALIGN
+
+
+def test_workspace_query(lib):
+    q = lib.fp8_block_gemm_workspace_size
+    assert q(0, 8192, 12288, 2048) == 0                 # fprop never needs one
+    assert q(1, 8192, 4096, 2048) == 0
+    assert q(2, 100, 256, 256) == ctypes.c_size_t(-1).value
+    assert q(7, 256, 256, 256) == ctypes.c_size_t(-1).value
+    n = q(2, 8192, 2048, 2048)                          # O-projection wgrad: 64 tiles of 256x256
+    assert n % (2048 * 2048 * 4) == 0 and n >= 2 * 2048 * 2048 * 4
+
+
+def test_valid_call_without_gpu_reports_device_error(lib):
+    """With valid arguments the only remaining check is the device; on a
+    machine without a gfx950 it must fail cleanly, never launch."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    rc = lib.fp8_quantize_rowgroup(P, 4, 256, 256, P2, 256, P3, 0, None)
+    assert rc in (EHIP, EDEV)
+    rc = lib.fp8_block_gemm_fprop(256, 256, 256, P, P3, P2, P3, P, 0, None)
+    assert rc in (EHIP, EDEV)
+
+
+def test_binding_fails_loudly_when_library_missing(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        fb._lib = None
+        try:
+            fb.load_library(str(tmp_path / "nope.so"))
+        finally:
+            fb._lib = None

@@ -1,0 +1,232 @@
+"""GPU parity of the block-scaled Fprop / Dgrad / Wgrad GEMMs against the CPU
+oracle, through the C ABI, for both accumulation algorithms.
+
+Tolerance -- the reading of "within max relative error 1e-3 of the oracle's
+fp32-accumulated result computed from the same quantized operands":
+  * fp32 output: per element |y - y32| <= 1e-3 * D, with D the sum of the
+    absolute values of all scaled products (the quantity any summation-order
+    error is proportional to), and normwise max|y - y32| <= 1e-3 * max|y32|.
+    An elementwise |y - y32| / |y32| bound cannot hold for any summation order
+    near cancellation, so it is not gated.
+  * bf16 output: bit-equal to the round-to-nearest-even of the same kernel's
+    fp32 result, and within half a bf16 ulp (<= 2^-8 |y32|) plus the fp32
+    gate above of the oracle's result.
+Exact cases: integer-valued operands in [-16, 16] quantize losslessly and
+every partial sum is an integer below 2^24, so the GPU result must equal an
+int64 matmul exactly (and its bf16 rounding, bit for bit).
+
+The GPU path quantizes its own operands; the oracle quantizes the same seeded
+bf16 inputs on the host (the quantizers are checked bit-exact separately).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import blockwise_fp8_linear_amd as fb
+from blockwise_fp8_linear_amd import synth
+from gpu_util import check_bf16, check_f32, dev_bf16, host, host_f32, note, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+ALGOS = {"promote": fb.FP8BLK_ALGO_PROMOTE, "scaled": fb.FP8BLK_ALGO_SCALED_MFMA}
+OPS = ("fprop", "dgrad", "wgrad")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def varied(shape, std, key):
+    """N(0, std^2) with each 128x128 block scaled by its own power of two, so
+    that row-group, column-group and block scales all vary."""
+    rng = synth.rng_for(*key)
+    x = rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
+    R, C = shape
+    f = 2.0 ** rng.integers(-5, 6, size=((R + 127) // 128, (C + 127) // 128))
+    x *= np.repeat(np.repeat(f, 128, 0)[:R], 128, 1)[:, :C].astype(np.float32)
+    return synth.bf16_bits_from_f32(x)
+
+
+class Layer:
+    """One linear's operands, quantized on the GPU and by the oracle."""
+
+    def __init__(self, x, w, dy):
+        import torch
+        self.M, self.K = x.shape
+        self.N = w.shape[0]
+        xt, wt, dyt = dev_bf16(x), dev_bf16(w), dev_bf16(dy)
+        self.g = {}
+        self.g["qx"], self.g["sx"] = fb.fp8_quantize_rowgroup(xt)
+        self.g["qxT"], self.g["sxT"] = fb.fp8_quantize_colgroup(xt)
+        self.g["qw"], self.g["qwT"], self.g["sw"] = fb.fp8_quantize_block(wt)
+        self.g["qdy"], self.g["sdy"] = fb.fp8_quantize_rowgroup(dyt)
+        self.g["qdyT"], self.g["sdyT"] = fb.fp8_quantize_colgroup(dyt)
+        torch.cuda.synchronize()
+        self.o = {}
+        self.o["qx"], self.o["sx"] = oracle.quantize_rowgroup(x)
+        self.o["qxT"], self.o["sxT"] = oracle.quantize_colgroup(x)
+        self.o["qw"], _, self.o["sw"] = oracle.quantize_block(w, transpose=False)
+        self.o["qdy"], self.o["sdy"] = oracle.quantize_rowgroup(dy)
+        self.o["qdyT"], self.o["sdyT"] = oracle.quantize_colgroup(dy)
+
+    def gpu(self, op, algo, out_dtype):
+        g = self.g
+        args = {"fprop": (g["qx"], g["sx"], g["qw"], g["sw"]),
+                "dgrad": (g["qdy"], g["sdy"], g["qwT"], g["sw"]),
+                "wgrad": (g["qdyT"], g["sdyT"], g["qxT"], g["sxT"])}[op]
+        opc = {"fprop": fb.FP8BLK_OP_FPROP, "dgrad": fb.FP8BLK_OP_DGRAD, "wgrad": fb.FP8BLK_OP_WGRAD}[op]
+        return fb.fp8_block_gemm(opc, *args, self.M, self.N, self.K, out_dtype=out_dtype, algo=algo)
+
+    def ref(self, op, rows):
+        o = self.o
+        if op == "fprop":
+            return oracle.gemm_fprop(o["qx"], o["sx"], o["qw"], o["sw"], rows=rows)
+        if op == "dgrad":
+            return oracle.gemm_dgrad(o["qdy"], o["sdy"], o["qw"], o["sw"], rows=rows)
+        return oracle.gemm_wgrad(o["qdyT"], o["sdyT"], o["qxT"], o["sxT"], rows=rows)
+
+    def out_rows(self, op):
+        return self.N if op == "wgrad" else self.M
+
+
+def check_op(layer, op, algo_name, rows=None, what=""):
+    import torch
+    algo = ALGOS[algo_name]
+    nrows = layer.out_rows(op)
+    rows = np.arange(nrows) if rows is None else np.asarray(rows)
+    y32, _, bound = layer.ref(op, rows)
+    yf = layer.gpu(op, algo, torch.float32)
+    yb = layer.gpu(op, algo, torch.bfloat16)
+    torch.cuda.synchronize()
+    yf_h = host_f32(yf)[rows]
+    yb_h = host(yb)[rows]
+    tag = f"{what} {op} {algo_name} M={layer.M} N={layer.N} K={layer.K}"
+    stats = check_f32(yf_h, y32, bound, tag)
+    check_bf16(yb_h, yf_h, y32, bound, tag)
+    note(f"{tag}: err/bound {stats['err/bound']:.2e} normwise {stats['normwise']:.2e} "
+         f"bit-exact-vs-oracle-fp32 {stats['exact_frac']:.3f}")
+    return stats
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+@pytest.mark.parametrize("shape", [(384, 640, 384), (256, 128, 640), (128, 384, 256), (640, 256, 1152)])
+def test_small_shapes_all_ops(algo, shape):
+    M, N, K = shape
+    key = (60, M, N, K)
+    layer = Layer(varied((M, K), 1.0, key + (0,)), varied((N, K), 0.02, key + (1,)),
+                  varied((M, N), 1e-3, key + (2,)))
+    for op in OPS:
+        check_op(layer, op, algo, what="small")
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+def test_exact_integer_products(algo):
+    import torch
+    M, N, K = 256, 384, 640
+    x = synth.integer_valued_bf16((M, K), -16, 16, 61, 0)
+    w = synth.integer_valued_bf16((N, K), -16, 16, 61, 1)
+    dy = synth.integer_valued_bf16((M, N), -16, 16, 61, 2)
+    layer = Layer(x, w, dy)
+    X, W, DY = (oracle.bf16_to_f64(a).astype(np.int64) for a in (x, w, dy))
+    exact = {"fprop": X @ W.T, "dgrad": DY @ W, "wgrad": DY.T @ X}
+    for op in OPS:
+        yf = host_f32(layer.gpu(op, ALGOS[algo], torch.float32))
+        yb = host(layer.gpu(op, ALGOS[algo], torch.bfloat16))
+        assert np.array_equal(yf.astype(np.int64), exact[op]), f"{op} {algo}: not exact"
+        assert np.array_equal(yf, exact[op].astype(np.float32))
+        rne = oracle.bf16_rne(exact[op].astype(np.float32))
+        assert np.array_equal(yb, rne), f"{op} {algo}: bf16 rounding of the exact result differs"
+
+
+def test_tiny_fprop_config():
+    """The 256x256 fprop workload, every output element."""
+    import torch
+    x, w = synth.tiny_fprop()
+    layer = Layer(x, w, synth.normal_bf16((256, 256), 1e-3, 0, 1, 2))
+    for algo in ALGOS:
+        check_op(layer, "fprop", algo, what="tiny")
+
+
+def _sample_rows(n, key, k=24):
+    rng = synth.rng_for(*key)
+    fixed = [0, 1, 127, 128, 255, 256, n // 2 + 17, n - 129, n - 1]
+    return np.unique(np.concatenate([fixed, rng.choice(n, k, replace=False)]))
+
+
+def test_single_linear_fprop_full_size():
+    """8192 x 12288 x 2048 fprop in the benchmark's launch configuration, on
+    sampled output rows (every column of each)."""
+    import torch
+    x, w = synth.single_linear()
+    xt, wt = dev_bf16(x), dev_bf16(w)
+    qx, sx = fb.fp8_quantize_rowgroup(xt)
+    qw, _, sw = fb.fp8_quantize_block(wt, transpose=False)
+    ox, osx = oracle.quantize_rowgroup(x)
+    ow, _, osw = oracle.quantize_block(w, transpose=False)
+    rows = _sample_rows(8192, (62, 0))
+    y32, _, bound = oracle.gemm_fprop(ox, osx, ow, osw, rows=rows)
+    for algo_name, algo in ALGOS.items():
+        yf = fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, qx, sx, qw, sw, 8192, 12288, 2048, out_dtype=torch.float32, algo=algo)
+        yb = fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, qx, sx, qw, sw, 8192, 12288, 2048, algo=algo)
+        torch.cuda.synchronize()
+        yf_h, yb_h = host_f32(yf)[rows], host(yb)[rows]
+        st = check_f32(yf_h, y32, bound, f"single linear {algo_name}")
+        check_bf16(yb_h, yf_h, y32, bound, f"single linear {algo_name}")
+        note(f"single linear fprop {algo_name}: {st}")
+
+
+def test_outlier_stress_fprop_full_size():
+    import torch
+    x, w, _ = synth.outlier_stress()
+    xt, wt = dev_bf16(x), dev_bf16(w)
+    qx, sx = fb.fp8_quantize_rowgroup(xt)
+    qw, _, sw = fb.fp8_quantize_block(wt, transpose=False)
+    ox, osx = oracle.quantize_rowgroup(x)
+    ow, _, osw = oracle.quantize_block(w, transpose=False)
+    rows = _sample_rows(8192, (63, 0))
+    y32, _, bound = oracle.gemm_fprop(ox, osx, ow, osw, rows=rows)
+    for algo_name, algo in ALGOS.items():
+        yf = fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, qx, sx, qw, sw, 8192, 12288, 2048, out_dtype=torch.float32, algo=algo)
+        yb = fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, qx, sx, qw, sw, 8192, 12288, 2048, algo=algo)
+        torch.cuda.synchronize()
+        yf_h, yb_h = host_f32(yf)[rows], host(yb)[rows]
+        st = check_f32(yf_h, y32, bound, f"outlier {algo_name}")
+        check_bf16(yb_h, yf_h, y32, bound, f"outlier {algo_name}")
+        note(f"outlier fprop {algo_name}: {st}")
+
+
+@pytest.mark.parametrize("li", range(4))
+def test_decoder_layer_full_size(li):
+    """Each linear of the decoder layer at 8192 tokens: fprop, dgrad and wgrad
+    on sampled output rows, both algorithms."""
+    lin = synth.decoder_layer(linears=(synth.LAYER_LINEARS[li],))[0]
+    layer = Layer(lin["x"], lin["w"], lin["dy"])
+    for op in OPS:
+        rows = _sample_rows(layer.out_rows(op), (64, li, OPS.index(op)), k=8)
+        for algo in ALGOS:
+            check_op(layer, op, algo, rows=rows, what=f"layer {lin['name']}")
+
+
+def test_named_entry_points_and_determinism():
+    """The named C entry points (default algorithm) equal the generic one, and
+    repeated runs -- including split-K Wgrad -- are bit-identical."""
+    import torch
+    M, N, K = 8192, 2048, 256
+    layer = Layer(synth.normal_bf16((M, K), 1.0, 65, 0), synth.normal_bf16((N, K), 0.02, 65, 1),
+                  synth.normal_bf16((M, N), 1e-3, 65, 2))
+    g = layer.g
+    assert fb.fp8_block_gemm_workspace_size(fb.FP8BLK_OP_WGRAD, M, N, K) > 0
+    a = fb.fp8_block_gemm_wgrad(g["qdyT"], g["sdyT"], g["qxT"], g["sxT"])
+    b = fb.fp8_block_gemm_wgrad(g["qdyT"], g["sdyT"], g["qxT"], g["sxT"])
+    c = layer.gpu("wgrad", fb.FP8BLK_ALGO_DEFAULT, torch.bfloat16)
+    f1 = fb.fp8_block_gemm_fprop(g["qx"], g["sx"], g["qw"], g["sw"])
+    f2 = layer.gpu("fprop", fb.FP8BLK_ALGO_DEFAULT, torch.bfloat16)
+    d1 = fb.fp8_block_gemm_dgrad(g["qdy"], g["sdy"], g["qwT"], g["sw"])
+    d2 = layer.gpu("dgrad", fb.FP8BLK_ALGO_DEFAULT, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, c)
+    assert torch.equal(f1, f2) and torch.equal(d1, d2)
+    rows = _sample_rows(N, (65, 3), k=8)
+    check_op(layer, "wgrad", "promote", rows=rows, what="split-K")
+    check_op(layer, "wgrad", "scaled", rows=rows, what="split-K")
