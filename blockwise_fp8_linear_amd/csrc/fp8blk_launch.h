@@ -46,4 +46,8 @@ enum class GemmAlgo { Promote, ScaledMfma };
 
 hipError_t launch_gemm(const GemmArgs& g, GemmAlgo algo, hipStream_t stream);
 
+// The 256x256 block-scaled-MFMA kernel (gemm_mx.hip) and the shapes it takes.
+bool gemm_mx_eligible(const GemmArgs& g);
+hipError_t launch_gemm_mx(const GemmArgs& g, hipStream_t stream);
+
 }  // namespace fp8blk

@@ -385,20 +385,28 @@ static hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
   }
   hipLaunchKernelGGL(gemm_kernel<C>, dim3((uint32_t)blocks), dim3(C::THREADS), C::LDS, stream, g, tiles_m, tiles_n,
                      kb_per_split);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
+  return hipGetLastError();
+}
+
+static hipError_t launch_splitk_reduce(const GemmArgs& g, hipStream_t stream) {
   const int64_t n4 = g.I * g.J / 4;
   int64_t rblocks = (n4 + 255) / 256;
   if (rblocks > 4096) rblocks = 4096;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)rblocks), dim3(256), 0, stream, g.ws, splits, n4, g.out,
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)rblocks), dim3(256), 0, stream, g.ws, g.splits, n4, g.out,
                      g.out_f32);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs& g, GemmAlgo algo, hipStream_t stream) {
+  hipError_t e;
   if (algo == GemmAlgo::Promote)
-    return g.bmode == BScale::Row ? launch_cfg<PromoteRow>(g, stream) : launch_cfg<PromoteBlock>(g, stream);
-  return g.bmode == BScale::Row ? launch_cfg<ScaledRow>(g, stream) : launch_cfg<ScaledBlock>(g, stream);
+    e = g.bmode == BScale::Row ? launch_cfg<PromoteRow>(g, stream) : launch_cfg<PromoteBlock>(g, stream);
+  else if (gemm_mx_eligible(g))
+    e = launch_gemm_mx(g, stream);
+  else
+    e = g.bmode == BScale::Row ? launch_cfg<ScaledRow>(g, stream) : launch_cfg<ScaledBlock>(g, stream);
+  if (e != hipSuccess || g.splits <= 1) return e;
+  return launch_splitk_reduce(g, stream);
 }
 
 }  // namespace fp8blk

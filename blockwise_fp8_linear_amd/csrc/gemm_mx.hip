@@ -1,0 +1,387 @@
+// Block-scaled FP8 GEMM for gfx950 on the block-scaled MFMA -- the fast path.
+//
+// Same contraction as gemm.hip (out[i][j] = sum over 128-deep reduction
+// blocks b of sa(i,b) * sb(j,b) * sum_r A[i][r] B[j][r]; Fprop, Dgrad and Wgrad
+// of the FP8 linear layer, "Puro-2B ... part 3/7", section 3.2), built for
+// throughput:
+//   * 256 x 256 output tile per workgroup, 4 waves of 128 x 128;
+//   * v_mfma_scale_f32_32x32x64_f8f6f4: each operand row carries its
+//     power-of-two scale as an E8M0 byte (the fp32 scale's exponent field),
+//     applied inside the matrix core; products accumulate in place, in fp32,
+//     so the accumulators never leave the matrix registers;
+//   * the reduction advances in 64-deep stages (two per 128-deep scale
+//     block) through a 4-deep LDS ring filled by direct global->LDS 16-byte
+//     loads (no staging registers), three stages in flight;
+//   * a row's 64 bytes are four 16-byte chunks, XOR-swizzled by
+//     ((row >> 1) & 3) so that the fragment reads are free of bank conflicts;
+//   * MFMA fragments are double-buffered in registers: the LDS reads of the
+//     next stage overlap the MFMAs of the current one;
+//   * the scale bytes of four consecutive 128-blocks are packed in one
+//     register per operand row and picked by the instruction's op_sel;
+//     weight-block scales are wave-uniform scalar loads.
+// Requirements (else the caller falls back to gemm.hip): the number of
+// 128-blocks per split-K slice is a multiple of 4 and the scale arrays are
+// 16-byte aligned.
+#include "fp8blk_device.h"
+#include "fp8blk_launch.h"
+
+namespace fp8blk {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 256, BN = 256, BK = 64, STAGES = 4, THREADS = 256;
+constexpr int WM = 128, WN = 128;          // wave tile
+constexpr int TM = WM / 32, TN = WN / 32;  // 32x32 MFMA tiles per wave
+constexpr int A_STAGE = BM * BK, B_STAGE = BN * BK, STAGE = A_STAGE + B_STAGE;
+constexpr int SC_BYTES = 8192;            // one group of raw scales: A rows, then B rows
+constexpr int LDS_BYTES = STAGES * STAGE + 2 * SC_BYTES;  // 144 KiB
+constexpr int LOADS_A = A_STAGE / 1024 / (THREADS / 64);  // 1 KiB per wave instruction
+constexpr int LOADS_B = B_STAGE / 1024 / (THREADS / 64);
+constexpr int LOADS_PER_STAGE = LOADS_A + LOADS_B;          // per wave
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16-byte direct global->LDS load: lane p's 16 bytes from base + voff land at
+// LDS offset lds_addr + 16 p (lds_addr wave-uniform, in M0).  Written as
+// inline assembly on purpose: the compiler would otherwise treat every
+// later LDS read as depending on every such load and drain them all
+// (vmcnt(0)) before it, which defeats the prefetch ring.  The kernel waits for
+// these loads itself with explicit vmcnt counts.  The block has no register
+// outputs; it sets M0 itself and the kernel has no other M0 users.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds_addr) {
+  // the base is wave-uniform but may have been computed in vector registers
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  // (readfirstlane returns int: go through uint32_t so the low half is not
+  // sign-extended into the high half)
+  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
+}
+
+// Workgroup barrier that orders LDS only.  (__syncthreads() also waits for
+// every outstanding global access, which would drain the prefetched stages;
+// the direct loads are waited for explicitly with vmcnt instead.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+__device__ __forceinline__ uint32_t swz(uint32_t row) { return (row >> 1) & 3; }
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt low 4 bits and
+// bits 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// fp32 power-of-two scales -> E8M0 bytes (their exponent fields), 4 packed.
+__device__ __forceinline__ uint32_t pack_e8(u32x4 s) {
+  return ((s[0] >> 23) & 0xFF) | (((s[1] >> 23) & 0xFF) << 8) | (((s[2] >> 23) & 0xFF) << 16) |
+         (((s[3] >> 23) & 0xFF) << 24);
+}
+
+template <bool BROW>
+__global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t tiles_m, int64_t tiles_n,
+                                                          int64_t kb_per_split) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t wm = wave >> 1, wn = wave & 1;
+  const uint32_t lds0 = lds_offset(lds);
+  const uint32_t l32 = lane & 31, g2 = lane >> 5;
+
+  // ---- tile / split owned by this workgroup (XCD-aware, grouped along M)
+  const int64_t ntiles = tiles_m * tiles_n;
+  const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t split = L / ntiles;
+  const int64_t tile = L - split * ntiles;
+  constexpr int64_t GM = 8;
+  const int64_t group = tile / (GM * tiles_n);
+  const int64_t first_m = group * GM;
+  const int64_t gsize = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+  const int64_t in_group = tile - group * GM * tiles_n;
+  const int64_t i0 = (first_m + in_group % gsize) * BM;
+  const int64_t j0 = (in_group / gsize) * BN;
+
+  const int64_t R = g.R, nkb = R / 128;
+  const int64_t kb_begin = split * kb_per_split;
+  const int nstage = (int)(2 * kb_per_split);   // 64-deep stages of this slice (a multiple of 8)
+  const int ngroup = (int)(kb_per_split / 4);  // groups of four 128-blocks
+
+  // ---- direct loads of the tiles.  Wave instruction u fills 16 rows x 64 B;
+  // lane p writes LDS bytes p*16..+15 of that KiB: row p/4, physical chunk
+  // p%4, which holds logical chunk (p%4) ^ swz(row).  Per-lane 32-bit offsets
+  // from wave-uniform bases; rows past a ragged edge read the last row (valid
+  // memory, results never stored).
+  const uint8_t* baseA = g.a + i0 * R + kb_begin * 128;
+  const uint8_t* baseB = g.b + j0 * R + kb_begin * 128;
+  uint32_t offLA[LOADS_A], offLB[LOADS_B];
+#pragma unroll
+  for (int u = 0; u < LOADS_A; ++u) {
+    const uint32_t row = (wave * LOADS_A + u) * 16 + (lane >> 2);
+    int64_t gr = i0 + row;
+    gr = gr < g.I ? gr : g.I - 1;
+    offLA[u] = (uint32_t)((gr - i0) * R) + (((lane & 3) ^ swz(row)) << 4);
+  }
+#pragma unroll
+  for (int u = 0; u < LOADS_B; ++u) {
+    const uint32_t row = (wave * LOADS_B + u) * 16 + (lane >> 2);
+    int64_t gr = j0 + row;
+    gr = gr < g.J ? gr : g.J - 1;
+    offLB[u] = (uint32_t)((gr - j0) * R) + (((lane & 3) ^ swz(row)) << 4);
+  }
+  // stage s -> ring slot s % STAGES; a stage past the end reloads the last
+  // one into a slot that is never read again (keeps the waits uniform).
+  // issue_one(s, u): the wave's u-th direct load of stage s (u < LOADS_A: A
+  // tile, else B tile).
+  auto issue_one = [&](int s, int u) {
+    const int sc = s < nstage ? s : nstage - 1;
+    const uint32_t slot = lds0 + (uint32_t)(s % STAGES) * STAGE;
+    if (u < LOADS_A)
+      dma16(baseA + (int64_t)sc * BK, offLA[u], slot + (wave * LOADS_A + u) * 1024);
+    else
+      dma16(baseB + (int64_t)sc * BK, offLB[u - LOADS_A], slot + A_STAGE + (wave * LOADS_B + u - LOADS_A) * 1024);
+  };
+  auto issue_stage = [&](int s) {
+#pragma unroll
+    for (int u = 0; u < LOADS_PER_STAGE; ++u) issue_one(s, u);
+  };
+
+  // ---- direct loads of the raw fp32 scales of a group (four 128-blocks):
+  // lane of wave w handles operand row 64w + lane, 16 bytes (blocks kb..kb+3).
+  // Double buffered in LDS behind the tile ring.
+  uint8_t* const sc_lds = lds + STAGES * STAGE;
+  // byte offsets of this lane's scale row from the tile's first row, block kb_begin
+  uint32_t offSA, offSB = 0;
+  const uint8_t* baseSA = reinterpret_cast<const uint8_t*>(g.sa + i0 * nkb + kb_begin);
+  const uint8_t* baseSB = reinterpret_cast<const uint8_t*>(g.sb + j0 * nkb + kb_begin);
+  {
+    int64_t r = i0 + wave * 64 + lane;
+    r = r < g.I ? r : g.I - 1;
+    offSA = (uint32_t)((r - i0) * nkb * 4);
+  }
+  if constexpr (BROW) {
+    int64_t r = j0 + wave * 64 + lane;
+    r = r < g.J ? r : g.J - 1;
+    offSB = (uint32_t)((r - j0) * nkb * 4);
+  }
+  const uint32_t sc0 = lds0 + STAGES * STAGE;
+  auto issue_scales = [&](int q) {  // group q -> scale buffer q & 1
+    const int qc = q < ngroup ? q : ngroup - 1;
+    const uint32_t buf = sc0 + (uint32_t)(q & 1) * SC_BYTES;
+    dma16(baseSA + 16 * qc, offSA, buf + wave * 1024);
+    if constexpr (BROW) dma16(baseSB + 16 * qc, offSB, buf + 4096 + wave * 1024);
+  };
+  constexpr int SC_LOADS = BROW ? 2 : 1;  // per wave per group
+
+  // ---- fragment reads: lane l holds row l%32 of a 32-row MFMA tile and the
+  // stage's logical chunks 2*(l/32), 2*(l/32)+1 (A and B use the same K order).
+  const uint32_t wm0 = wm * WM, wn0 = wn * WN;
+  const uint32_t swzl = swz(l32);  // fragment rows start at multiples of 32: same swizzle
+  const uint32_t fragA = (wm0 + l32) * BK + (((2 * g2) ^ swzl) << 4);
+  const uint32_t fragB = A_STAGE + (wn0 + l32) * BK + (((2 * g2) ^ swzl) << 4);
+  // the second chunk sits 16 bytes after or before the first (signed!)
+  const int32_t hiOff = ((int32_t)((2 * g2 + 1) ^ swzl) - (int32_t)((2 * g2) ^ swzl)) * 16;
+  auto read_frag = [&](int s, uint32_t off) {
+    const uint8_t* p = lds + (s % STAGES) * STAGE + off;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(p + hiOff);
+    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto read_frags = [&](int s, v8i* fa, v8i* fb) {
+#pragma unroll
+    for (int t = 0; t < TM; ++t) fa[t] = read_frag(s, fragA + t * 32 * BK);
+#pragma unroll
+    for (int t = 0; t < TN; ++t) fb[t] = read_frag(s, fragB + t * 32 * BK);
+  };
+  // packed E8M0 scale bytes of group q for this lane's operand rows
+  // (row wm0 + 32t + l%32 of A, of B in row mode); weight-block scales are
+  // uniform over the wave's 128 columns (clamped on a ragged edge, where the
+  // columns are computed but not stored).
+  const int64_t jblk = ((j0 + wn0) >> 7) < (g.J >> 7) ? ((j0 + wn0) >> 7) : (g.J >> 7) - 1;
+  auto read_scales = [&](int q, uint32_t* pa, uint32_t* pb) {
+    const uint8_t* buf = sc_lds + (q & 1) * SC_BYTES;
+#pragma unroll
+    for (int t = 0; t < TM; ++t) pa[t] = pack_e8(*reinterpret_cast<const u32x4*>(buf + (wm0 + t * 32 + l32) * 16));
+    if constexpr (BROW) {
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+        pb[t] = pack_e8(*reinterpret_cast<const u32x4*>(buf + 4096 + (wn0 + t * 32 + l32) * 16));
+    } else {
+      // wave-uniform: read through the constant address space so that these
+      // become scalar loads (a vector load here would make the compiler drain
+      // the in-flight direct loads before using it)
+      const int64_t qc = q < ngroup ? q : ngroup - 1;
+      const int64_t kb = kb_begin + 4 * qc;
+      const __attribute__((address_space(4))) uint32_t* p =
+          (const __attribute__((address_space(4))) uint32_t*)(g.sb + jblk * g.sb_j + kb * g.sb_r);
+      u32x4 v;
+      v[0] = p[0];
+      v[1] = p[g.sb_r];
+      v[2] = p[2 * g.sb_r];
+      v[3] = p[3 * g.sb_r];
+      const uint32_t e = pack_e8(v);
+#pragma unroll
+      for (int t = 0; t < TN; ++t) pb[t] = e;
+    }
+  };
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = v16f{};
+
+  uint32_t sa_cur[TM], sb_cur[TN];
+  v8i fa[2][TM], fb[2][TN];
+
+  // Per 8-stage group the vector-memory queue of a wave holds, in order: the
+  // next group's scales (issued with stage 8q), then one tile stage per step.
+  // Waiting for stage s+1 therefore leaves at most the two newer tile stages
+  // and possibly one scale group outstanding; waiting with the smaller count
+  // (tiles only) is always safe, just stricter on the step that issues scales.
+  constexpr int WAIT_TILES = 2 * LOADS_PER_STAGE;
+
+  // prologue: scales of group 0, tile stages 0..2, then stage 0 and group 0 visible
+  issue_scales(0);
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) issue_stage(s);
+  wait_vmcnt<WAIT_TILES>();  // scales of group 0 and stage 0 have landed
+  lds_barrier();
+  read_frags(0, fa[0], fb[0]);
+  read_scales(0, sa_cur, sb_cur);
+
+  // One 64-deep stage.  Entry: stage s's fragments are in registers (set
+  // BUF), stage s+1 was issued two stages ago.  After the barrier that makes
+  // stage s+1 visible, the 16 MFMAs of stage s are issued in pairs, and
+  // between pairs the wave reads one fragment of stage s+1 (into the other
+  // register set) and issues one direct load of stage s+3 (into the slot of
+  // stage s-1, whose fragments every wave read before this barrier).  The
+  // sched_barrier fences pin that interleaving so the matrix pipe is never
+  // left waiting on LDS.
+  static_assert(TM == 4 && TN == 4 && LOADS_PER_STAGE == 8, "one read + one load per MFMA pair");
+  auto stage_step = [&](int s, auto buf_tag, auto opsel_tag) {
+    constexpr int OPSEL = decltype(opsel_tag)::value;
+    constexpr int BUF = decltype(buf_tag)::value;
+    constexpr int NXT = BUF ^ 1;
+    wait_vmcnt<LOADS_PER_STAGE>();  // this wave's part of stage s+1 has landed
+    lds_barrier();                  // ... and every wave's
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int a = p >> 1, b0 = 2 * (p & 1);
+      acc[a][b0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[BUF][b0], fa[BUF][a], acc[a][b0], 0, 0, OPSEL,
+                                                                   (int)sb_cur[b0], OPSEL, (int)sa_cur[a]);
+      acc[a][b0 + 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          fb[BUF][b0 + 1], fa[BUF][a], acc[a][b0 + 1], 0, 0, OPSEL, (int)sb_cur[b0 + 1], OPSEL, (int)sa_cur[a]);
+      // next stage's fragments in the order its MFMAs consume them
+      if (p == 0) fa[NXT][0] = read_frag(s + 1, fragA);
+      else if (p <= 4) fb[NXT][p - 1] = read_frag(s + 1, fragB + (p - 1) * 32 * BK);
+      else fa[NXT][p - 4] = read_frag(s + 1, fragA + (p - 4) * 32 * BK);
+      issue_one(s + STAGES - 1, p);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // One loop iteration = one group = four 128-blocks = eight 64-deep stages;
+  // op_sel (the byte of the packed scales) is a constant in each step.
+  for (int q = 0; q < ngroup; ++q) {
+    const int s = 8 * q;
+    issue_scales(q + 1);  // buffer (q+1)&1 was last read at the start of group q-1
+    stage_step(s + 0, IntC<0>{}, IntC<0>{});
+    stage_step(s + 1, IntC<1>{}, IntC<0>{});
+    stage_step(s + 2, IntC<0>{}, IntC<1>{});
+    stage_step(s + 3, IntC<1>{}, IntC<1>{});
+    stage_step(s + 4, IntC<0>{}, IntC<2>{});
+    stage_step(s + 5, IntC<1>{}, IntC<2>{});
+    stage_step(s + 6, IntC<0>{}, IntC<3>{});
+    stage_step(s + 7, IntC<1>{}, IntC<3>{});
+    // group q+1's scales: issued before stage s+8's tiles, which the last
+    // step waited for, so they have landed; every wave passed that barrier
+    read_scales(q + 1, sa_cur, sb_cur);
+  }
+  wait_vmcnt<0>();  // no direct load may still target this workgroup's LDS at exit
+
+  // ---- epilogue.  acc[a][b] lane l, element e: row i = wm0 + 32a + l%32,
+  // columns j = wn0 + 32b + 8*(e/4) + 4*(l/32) + (e%4).
+#pragma unroll
+  for (int a = 0; a < TM; ++a) {
+    const int64_t i = i0 + wm0 + a * 32 + l32;
+    if (i >= g.I) continue;
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t j = j0 + wn0 + b * 32 + q * 8 + g2 * 4;
+        if (j >= g.J) continue;
+        const v4f v = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
+        if (g.splits > 1) {
+          *reinterpret_cast<v4f*>(g.ws + split * g.I * g.J + i * g.J + j) = v;
+        } else if (g.out_f32) {
+          *reinterpret_cast<v4f*>(static_cast<float*>(g.out) + i * g.J + j) = v;
+        } else {
+          uint2 o;
+          o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+          o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + i * g.J + j) = o;
+        }
+      }
+    }
+  }
+}
+
+template <bool BROW>
+hipError_t launch_mx(const GemmArgs& g, int64_t kb_per_split, hipStream_t stream) {
+  const int64_t tiles_m = (g.I + BM - 1) / BM;
+  const int64_t tiles_n = (g.J + BN - 1) / BN;
+  const int splits = g.splits > 0 ? g.splits : 1;
+  static bool attr_set = false;  // idempotent; a race only repeats the same call
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mx_kernel<BROW>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(gemm_mx_kernel<BROW>, dim3((uint32_t)(tiles_m * tiles_n * splits)), dim3(THREADS), LDS_BYTES,
+                     stream, g, tiles_m, tiles_n, kb_per_split);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_mx_eligible(const GemmArgs& g) {
+  const int64_t nkb = g.R / 128;
+  const int splits = g.splits > 0 ? g.splits : 1;
+  if (nkb % 4 != 0 || nkb % splits != 0 || (nkb / splits) % 4 != 0) return false;
+  // per-lane 32-bit offsets: 256 rows x R bytes of codes, 256 rows of scales
+  if (g.R > (int64_t(1) << 22)) return false;
+  if ((reinterpret_cast<uintptr_t>(g.sa) & 15) != 0) return false;
+  if (g.bmode == BScale::Row && (reinterpret_cast<uintptr_t>(g.sb) & 15) != 0) return false;
+  return true;
+}
+
+hipError_t launch_gemm_mx(const GemmArgs& g, hipStream_t stream) {
+  const int64_t nkb = g.R / 128;
+  const int splits = g.splits > 0 ? g.splits : 1;
+  const int64_t kb_per_split = nkb / splits;
+  return g.bmode == BScale::Row ? launch_mx<true>(g, kb_per_split, stream) : launch_mx<false>(g, kb_per_split, stream);
+}
+
+}  // namespace fp8blk

@@ -110,7 +110,11 @@ def check_op(layer, op, algo_name, rows=None, what=""):
 
 
 @pytest.mark.parametrize("algo", list(ALGOS))
-@pytest.mark.parametrize("shape", [(384, 640, 384), (256, 128, 640), (128, 384, 256), (640, 256, 1152)])
+# (M, N, K): ragged edges against 256-wide tiles; reductions whose block count
+# is / is not a multiple of 4 (the 256x256 block-scaled-MFMA kernel takes the
+# former, the general kernel the latter)
+@pytest.mark.parametrize("shape", [(384, 640, 512), (640, 384, 1024), (1024, 512, 384), (256, 128, 640),
+                                   (128, 384, 256), (640, 256, 1152)])
 def test_small_shapes_all_ops(algo, shape):
     M, N, K = shape
     key = (60, M, N, K)
