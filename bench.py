@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (a known-size reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -357,6 +359,13 @@ def main():
         out["bf16_baseline"] = {"ms_per_step": round(dt * 1e3, 3), "TFLOP/s": round(tf, 1),
                                 "fp8_over_bf16": round(dt * 1e3 / ms, 3),
                                 "what": "the same GEMMs in bf16 via torch.matmul (hipBLASLt), no quantization"}
+    if args.copy_calibration:
+        src = torch.empty(256 * 1024 * 1024, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration"] = {"bytes_read": src.numel() * 2, "bytes_written": dst.numel() * 2, "launches": 3}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_budget_s)
     print(json.dumps(out), flush=True)

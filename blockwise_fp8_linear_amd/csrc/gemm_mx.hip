@@ -37,7 +37,9 @@ constexpr int WM = 128, WN = 128;          // wave tile
 constexpr int TM = WM / 32, TN = WN / 32;  // 32x32 MFMA tiles per wave
 constexpr int A_STAGE = BM * BK, B_STAGE = BN * BK, STAGE = A_STAGE + B_STAGE;
 constexpr int SC_BYTES = 8192;            // one group of raw scales: A rows, then B rows
-constexpr int LDS_BYTES = STAGES * STAGE + 2 * SC_BYTES;  // 144 KiB
+constexpr int MAX_KB = 128;               // 128-blocks per split-K slice (weight-block scales in LDS)
+constexpr int BS_BYTES = 4 * MAX_KB * 4;  // per wave: this slice's weight-block scales, fp32
+constexpr int LDS_BYTES = STAGES * STAGE + 2 * SC_BYTES + BS_BYTES;  // 146 KiB
 constexpr int LOADS_A = A_STAGE / 1024 / (THREADS / 64);  // 1 KiB per wave instruction
 constexpr int LOADS_B = B_STAGE / 1024 / (THREADS / 64);
 constexpr int LOADS_PER_STAGE = LOADS_A + LOADS_B;          // per wave
@@ -59,6 +61,16 @@ __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32
   const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
                       (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+// 4-byte variant: lane p's dword lands at lds_addr + 4 p.
+__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sb),
                "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory", "m0");
 }
@@ -216,6 +228,20 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
   // uniform over the wave's 128 columns (clamped on a ragged edge, where the
   // columns are computed but not stored).
   const int64_t jblk = ((j0 + wn0) >> 7) < (g.J >> 7) ? ((j0 + wn0) >> 7) : (g.J >> 7) - 1;
+  // weight-block mode: every scale this wave needs (its block column, all
+  // kb_per_split <= MAX_KB blocks of the slice) is loaded once, up front, into
+  // LDS -- no scalar loads in the main loop (their shared lgkmcnt would make
+  // the LDS waits drain them)
+  constexpr uint32_t bs_area = STAGES * STAGE + 2 * SC_BYTES;
+  auto issue_block_scales = [&]() {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(g.sb + jblk * g.sb_j + kb_begin * g.sb_r);
+#pragma unroll
+    for (int h = 0; h < MAX_KB / 64; ++h) {
+      int64_t k = h * 64 + lane;
+      k = k < kb_per_split ? k : kb_per_split - 1;
+      dma4(base, (uint32_t)(k * g.sb_r * 4), lds0 + bs_area + wave * (MAX_KB * 4) + h * 256);
+    }
+  };
   auto read_scales = [&](int q, uint32_t* pa, uint32_t* pb) {
     const uint8_t* buf = sc_lds + (q & 1) * SC_BYTES;
 #pragma unroll
@@ -225,19 +251,10 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
       for (int t = 0; t < TN; ++t)
         pb[t] = pack_e8(*reinterpret_cast<const u32x4*>(buf + 4096 + (wn0 + t * 32 + l32) * 16));
     } else {
-      // wave-uniform: read through the constant address space so that these
-      // become scalar loads (a vector load here would make the compiler drain
-      // the in-flight direct loads before using it)
-      const int64_t qc = q < ngroup ? q : ngroup - 1;
-      const int64_t kb = kb_begin + 4 * qc;
-      const __attribute__((address_space(4))) uint32_t* p =
-          (const __attribute__((address_space(4))) uint32_t*)(g.sb + jblk * g.sb_j + kb * g.sb_r);
-      u32x4 v;
-      v[0] = p[0];
-      v[1] = p[g.sb_r];
-      v[2] = p[2 * g.sb_r];
-      v[3] = p[3 * g.sb_r];
-      const uint32_t e = pack_e8(v);
+      // this wave's weight block, blocks 4q..4q+3 of the slice (same
+      // address in every lane: a broadcast read)
+      const int qc = q < ngroup ? q : ngroup - 1;
+      const uint32_t e = pack_e8(*reinterpret_cast<const u32x4*>(lds + bs_area + wave * (MAX_KB * 4) + 16 * qc));
 #pragma unroll
       for (int t = 0; t < TN; ++t) pb[t] = e;
     }
@@ -260,6 +277,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
   constexpr int WAIT_TILES = 2 * LOADS_PER_STAGE;
 
   // prologue: scales of group 0, tile stages 0..2, then stage 0 and group 0 visible
+  if constexpr (!BROW) issue_block_scales();
   issue_scales(0);
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue_stage(s);
@@ -319,28 +337,72 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
   }
   wait_vmcnt<0>();  // no direct load may still target this workgroup's LDS at exit
 
-  // ---- epilogue.  acc[a][b] lane l, element e: row i = wm0 + 32a + l%32,
-  // columns j = wn0 + 32b + 8*(e/4) + 4*(l/32) + (e%4).
+  // ---- epilogue, staged through LDS so that global stores are whole rows.
+  // acc[a][b] lane l, element e holds row i = wm0 + 32a + l%32 and column
+  // j = wn0 + 32b + 8*(e/4) + 4*(l/32) + e%4.  Each wave writes its 128 x 128
+  // tile to its own 32 KiB of LDS in units of 4 consecutive columns, the unit
+  // index XOR-swizzled by (row & 31) (conflict-free: the 32 lanes of a write
+  // hit 32 different units of their rows), then reads back 16-byte pieces of
+  // whole rows and stores them coalesced.  fp32 output goes in two halves of
+  // 64 rows.
+  lds_barrier();  // every wave is done reading the tile ring
+  {
+    uint8_t* stage_area = lds + wave * 32768;
+    const bool f32 = g.splits > 1 || g.out_f32;
+    float* const outf = g.splits > 1 ? g.ws + split * g.I * g.J : static_cast<float*>(g.out);
+    uint16_t* const outh = static_cast<uint16_t*>(g.out);
+    const int64_t col0 = j0 + wn0;
+    if (!f32) {
+      // bf16: unit = 8 bytes, row = 256 bytes, all 128 rows at once
 #pragma unroll
-  for (int a = 0; a < TM; ++a) {
-    const int64_t i = i0 + wm0 + a * 32 + l32;
-    if (i >= g.I) continue;
+      for (int a = 0; a < TM; ++a)
 #pragma unroll
-    for (int b = 0; b < TN; ++b) {
+        for (int b = 0; b < TN; ++b)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t j = j0 + wn0 + b * 32 + q * 8 + g2 * 4;
-        if (j >= g.J) continue;
-        const v4f v = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
-        if (g.splits > 1) {
-          *reinterpret_cast<v4f*>(g.ws + split * g.I * g.J + i * g.J + j) = v;
-        } else if (g.out_f32) {
-          *reinterpret_cast<v4f*>(static_cast<float*>(g.out) + i * g.J + j) = v;
-        } else {
-          uint2 o;
-          o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-          o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + i * g.J + j) = o;
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t row = a * 32 + l32;
+            const uint32_t unit = (8 * b + 2 * q + g2) ^ (row & 31);
+            uint2 o;
+            o.x = f32_to_bf16_rne(acc[a][b][4 * q]) | (f32_to_bf16_rne(acc[a][b][4 * q + 1]) << 16);
+            o.y = f32_to_bf16_rne(acc[a][b][4 * q + 2]) | (f32_to_bf16_rne(acc[a][b][4 * q + 3]) << 16);
+            *reinterpret_cast<uint2*>(stage_area + row * 256 + unit * 8) = o;
+          }
+      // read: 16 lanes per row (16 bytes = units 2k, 2k+1 each), 4 rows per pass
+#pragma unroll 4
+      for (int pass = 0; pass < 32; ++pass) {
+        const uint32_t row = pass * 4 + (lane >> 4), k = lane & 15;
+        const uint32_t x = row & 31;
+        const uint32_t pu = (2 * k) ^ x;  // physical unit of logical unit 2k
+        u32x4 v = *reinterpret_cast<const u32x4*>(stage_area + row * 256 + (pu & ~1u) * 8);
+        if (pu & 1) v = u32x4{v[2], v[3], v[0], v[1]};  // the pair is stored swapped
+        const int64_t i = i0 + wm0 + row;
+        if (i < g.I && col0 < g.J)
+          *reinterpret_cast<u32x4*>(outh + i * g.J + col0 + 8 * k) = v;
+      }
+    } else {
+      // fp32: unit = 16 bytes, row = 512 bytes, two halves of 64 rows
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2) {
+          const int a = 2 * h + a2;
+#pragma unroll
+          for (int b = 0; b < TN; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t row = a2 * 32 + l32;
+              const uint32_t unit = (8 * b + 2 * q + g2) ^ (row & 31);
+              const v4f v = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
+              *reinterpret_cast<v4f*>(stage_area + row * 512 + unit * 16) = v;
+            }
+        }
+        // read: 32 lanes per row (one unit each), 2 rows per pass
+#pragma unroll 4
+        for (int pass = 0; pass < 32; ++pass) {
+          const uint32_t row = pass * 2 + (lane >> 5), k = lane & 31;
+          const v4f v = *reinterpret_cast<const v4f*>(stage_area + row * 512 + ((k ^ (row & 31)) * 16));
+          const int64_t i = i0 + wm0 + 64 * h + row;
+          if (i < g.I && col0 < g.J) *reinterpret_cast<v4f*>(outf + i * g.J + col0 + 4 * k) = v;
         }
       }
     }
@@ -369,7 +431,7 @@ hipError_t launch_mx(const GemmArgs& g, int64_t kb_per_split, hipStream_t stream
 bool gemm_mx_eligible(const GemmArgs& g) {
   const int64_t nkb = g.R / 128;
   const int splits = g.splits > 0 ? g.splits : 1;
-  if (nkb % 4 != 0 || nkb % splits != 0 || (nkb / splits) % 4 != 0) return false;
+  if (nkb % 4 != 0 || nkb % splits != 0 || (nkb / splits) % 4 != 0 || nkb / splits > MAX_KB) return false;
   // per-lane 32-bit offsets: 256 rows x R bytes of codes, 256 rows of scales
   if (g.R > (int64_t(1) << 22)) return false;
   if ((reinterpret_cast<uintptr_t>(g.sa) & 15) != 0) return false;
