@@ -264,7 +264,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
-              "the data-parallel sharding is described in DESIGN.md", file=sys.stderr)
+              "across GPUs only the Wgrad gradients would need an all-reduce; it is not implemented", file=sys.stderr)
         sys.exit(2)
     import torch
     import blockwise_fp8_linear_amd as fb

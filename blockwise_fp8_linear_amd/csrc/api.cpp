@@ -109,7 +109,7 @@ static int check_gemm_common(int64_t M, int64_t N, int64_t K, const void* a, con
 }
 
 // The algorithm FP8BLK_ALGO_DEFAULT resolves to.
-constexpr fp8blk::GemmAlgo kDefaultAlgo = fp8blk::GemmAlgo::Promote;
+constexpr fp8blk::GemmAlgo kDefaultAlgo = fp8blk::GemmAlgo::ScaledMfma;
 
 int fp8_block_gemm(int op, int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa, const uint8_t* b,
                    const float* sb, void* out, int out_dtype, int algo, void* workspace, size_t ws_bytes,
