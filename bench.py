@@ -34,6 +34,43 @@ PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 TOKENS = 8192
 LINEARS = (("qkv", 4096, 2048), ("o", 2048, 2048), ("gate_up", 12288, 2048), ("down", 2048, 6144))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+KERNEL_SOURCES = ("blockwise_fp8_linear_amd/csrc/gemm_mx.hip", "blockwise_fp8_linear_amd/csrc/gemm.hip",
+                  "blockwise_fp8_linear_amd/csrc/quant.hip", "blockwise_fp8_linear_amd/csrc/fp8blk_device.h")
+
+
+def kernel_of(kind, algo):
+    """The kernel function a timed launch runs (Fprop and Dgrad share one)."""
+    fast = algo in ("default", "scaled")
+    if kind in ("gemm_fprop", "gemm_dgrad"):
+        return "gemm_mx_kernel<false>" if fast else "gemm_kernel<promote, weight-block scales>"
+    if kind == "gemm_wgrad":
+        return ("gemm_mx_kernel<true> (+ splitk_reduce_kernel)" if fast
+                else "gemm_kernel<promote, row scales> (+ splitk_reduce_kernel)")
+    return kind + "_kernel"
+
+
+def sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload, algo):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when there is none or the kernels changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.loads(f.read().split("BEGIN-JSON", 1)[1].split("END-JSON", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("sources_digest") != sources_digest() or rec.get("workload") != workload or rec.get("algo") != algo:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
 
 
 def parse():
@@ -323,16 +360,25 @@ def main():
     gemm_kinds = [k for k in agg if k.startswith("gemm")]
     gemm_ms = sum(agg[k]["ms"] for k in gemm_kinds)
     gemm_flops_t = sum(agg[k]["flops"] for k in gemm_kinds)
-    dom = max(agg, key=lambda k: agg[k]["ms"])
-    a = agg[dom]
+    by_kernel = {}
+    for kind, a in agg.items():
+        b = by_kernel.setdefault(kernel_of(kind, args.algo), {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+        for f in b:
+            b[f] += a[f]
+    dom = max(by_kernel, key=lambda k: by_kernel[k]["ms"])
+    a = by_kernel[dom]
+    avg_s = a["ms"] / a["launches"] * 1e-3
+    traffic = measured_traffic(dom, args.workload, args.algo)
     if a["flops"]:
-        ach = a["flops"] / a["launches"] / (a["ms"] / a["launches"] * 1e-3) / 1e12
+        ach = a["flops"] / a["launches"] / avg_s / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+                "avg_launch_ms": round(avg_s * 1e3, 5), "launches": a["launches"]}
     else:
-        ach = a["bytes"] / a["launches"] / (a["ms"] / a["launches"] * 1e-3) / 1e9
+        ach = a["bytes"] / a["launches"] / avg_s / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "avg_launch_ms": round(avg_s * 1e3, 5), "launches": a["launches"]}
 
     out = {
         "metric": METRIC,
@@ -347,12 +393,13 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8e4m3",
         "data": "synthetic",
-        "config": {"workload": desc, "tokens": TOKENS, "algo": args.algo,
+        "config": {"workload": desc, "name": args.workload, "tokens": TOKENS, "algo": args.algo,
                    "gemm_tflop_per_step": round(step_flops / 1e12, 4)},
         "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
         "gemm_only_TFLOP/s": round(gemm_flops_t / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
         "roofline": roof,
         "breakdown": breakdown,
+        "sources_digest": sources_digest(),
     }
     if linears is not None and not args.no_bf16_baseline:
         dt, tf = bf16_baseline(torch, linears, reps if args.workload != "stack28" else 28)
