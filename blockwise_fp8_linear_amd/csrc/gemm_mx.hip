@@ -32,17 +32,22 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 256, BK = 64, STAGES = 4, THREADS = 256;
+constexpr int BM = 256, BN = 256, BK = 64, THREADS = 256;
 constexpr int WM = 128, WN = 128;          // wave tile
 constexpr int TM = WM / 32, TN = WN / 32;  // 32x32 MFMA tiles per wave
-constexpr int A_STAGE = BM * BK, B_STAGE = BN * BK, STAGE = A_STAGE + B_STAGE;
+// The LDS ring holds two "pair slots"; a pair slot holds two consecutive
+// 64-deep stages (one 128-deep scale block) of both tiles as whole 128-byte
+// rows, so every direct load reads whole cache lines.
+constexpr int PK = 2 * BK;                         // bytes of a row in a pair slot
+constexpr int A_SLOT = BM * PK, B_SLOT = BN * PK, SLOT = A_SLOT + B_SLOT;  // 64 KiB
+constexpr int SLOTS = 2;
 constexpr int SC_BYTES = 8192;            // one group of raw scales: A rows, then B rows
 constexpr int MAX_KB = 128;               // 128-blocks per split-K slice (weight-block scales in LDS)
 constexpr int BS_BYTES = 4 * MAX_KB * 4;  // per wave: this slice's weight-block scales, fp32
-constexpr int LDS_BYTES = STAGES * STAGE + 2 * SC_BYTES + BS_BYTES;  // 146 KiB
-constexpr int LOADS_A = A_STAGE / 1024 / (THREADS / 64);  // 1 KiB per wave instruction
-constexpr int LOADS_B = B_STAGE / 1024 / (THREADS / 64);
-constexpr int LOADS_PER_STAGE = LOADS_A + LOADS_B;          // per wave
+constexpr int LDS_BYTES = SLOTS * SLOT + 2 * SC_BYTES + BS_BYTES;  // 146 KiB
+constexpr int LOADS_A = A_SLOT / 1024 / (THREADS / 64);  // 1 KiB per wave instruction
+constexpr int LOADS_B = B_SLOT / 1024 / (THREADS / 64);
+constexpr int LOADS_PER_PAIR = LOADS_A + LOADS_B;          // per wave
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -93,7 +98,11 @@ struct IntC {
   static constexpr int value = V;
 };
 
-__device__ __forceinline__ uint32_t swz(uint32_t row) { return (row >> 1) & 3; }
+// 16-byte chunk swizzle of a 128-byte row: physical chunk = logical ^ swz(row).
+// Within any 8 (or 16) consecutive rows read with one logical chunk, the
+// physical chunks cover distinct banks for both 32- and 64-bank LDS.  It
+// depends on row & 31 only, so it is the same for every 32-row MFMA tile.
+__device__ __forceinline__ uint32_t swz(uint32_t row) { return ((row & 31) ^ ((row & 31) >> 3)) & 7; }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt low 4 bits and
 // bits 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -134,52 +143,51 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
 
   const int64_t R = g.R, nkb = R / 128;
   const int64_t kb_begin = split * kb_per_split;
-  const int nstage = (int)(2 * kb_per_split);   // 64-deep stages of this slice (a multiple of 8)
   const int ngroup = (int)(kb_per_split / 4);  // groups of four 128-blocks
 
-  // ---- direct loads of the tiles.  Wave instruction u fills 16 rows x 64 B;
-  // lane p writes LDS bytes p*16..+15 of that KiB: row p/4, physical chunk
-  // p%4, which holds logical chunk (p%4) ^ swz(row).  Per-lane 32-bit offsets
-  // from wave-uniform bases; rows past a ragged edge read the last row (valid
-  // memory, results never stored).
+  // ---- direct loads of the tiles, one pair slot (128-deep) at a time.  Wave
+  // instruction u fills 8 rows x 128 B; lane p writes LDS bytes p*16..+15 of
+  // that KiB: row p/8, physical chunk p%8, which holds logical chunk
+  // (p%8) ^ swz(row).  Per-lane 32-bit offsets from wave-uniform bases; rows
+  // past a ragged edge read the last row (valid memory, results never stored).
+  const int npair = (int)kb_per_split;
   const uint8_t* baseA = g.a + i0 * R + kb_begin * 128;
   const uint8_t* baseB = g.b + j0 * R + kb_begin * 128;
   uint32_t offLA[LOADS_A], offLB[LOADS_B];
 #pragma unroll
   for (int u = 0; u < LOADS_A; ++u) {
-    const uint32_t row = (wave * LOADS_A + u) * 16 + (lane >> 2);
+    const uint32_t row = (wave * LOADS_A + u) * 8 + (lane >> 3);
     int64_t gr = i0 + row;
     gr = gr < g.I ? gr : g.I - 1;
-    offLA[u] = (uint32_t)((gr - i0) * R) + (((lane & 3) ^ swz(row)) << 4);
+    offLA[u] = (uint32_t)((gr - i0) * R) + (((lane & 7) ^ swz(row)) << 4);
   }
 #pragma unroll
   for (int u = 0; u < LOADS_B; ++u) {
-    const uint32_t row = (wave * LOADS_B + u) * 16 + (lane >> 2);
+    const uint32_t row = (wave * LOADS_B + u) * 8 + (lane >> 3);
     int64_t gr = j0 + row;
     gr = gr < g.J ? gr : g.J - 1;
-    offLB[u] = (uint32_t)((gr - j0) * R) + (((lane & 3) ^ swz(row)) << 4);
+    offLB[u] = (uint32_t)((gr - j0) * R) + (((lane & 7) ^ swz(row)) << 4);
   }
-  // stage s -> ring slot s % STAGES; a stage past the end reloads the last
-  // one into a slot that is never read again (keeps the waits uniform).
-  // issue_one(s, u): the wave's u-th direct load of stage s (u < LOADS_A: A
-  // tile, else B tile).
-  auto issue_one = [&](int s, int u) {
-    const int sc = s < nstage ? s : nstage - 1;
-    const uint32_t slot = lds0 + (uint32_t)(s % STAGES) * STAGE;
+  // pair p -> slot p % SLOTS; a pair past the end reloads the last one into a
+  // slot that is never read again (keeps the waits uniform).
+  // issue_one(p, u): the wave's u-th direct load of pair p (u < LOADS_A: A).
+  auto issue_one = [&](int pr, int u) {
+    const int pc = pr < npair ? pr : npair - 1;
+    const uint32_t slot = lds0 + (uint32_t)(pr % SLOTS) * SLOT;
     if (u < LOADS_A)
-      dma16(baseA + (int64_t)sc * BK, offLA[u], slot + (wave * LOADS_A + u) * 1024);
+      dma16(baseA + (int64_t)pc * PK, offLA[u], slot + (wave * LOADS_A + u) * 1024);
     else
-      dma16(baseB + (int64_t)sc * BK, offLB[u - LOADS_A], slot + A_STAGE + (wave * LOADS_B + u - LOADS_A) * 1024);
+      dma16(baseB + (int64_t)pc * PK, offLB[u - LOADS_A], slot + A_SLOT + (wave * LOADS_B + u - LOADS_A) * 1024);
   };
-  auto issue_stage = [&](int s) {
+  auto issue_pair = [&](int pr) {
 #pragma unroll
-    for (int u = 0; u < LOADS_PER_STAGE; ++u) issue_one(s, u);
+    for (int u = 0; u < LOADS_PER_PAIR; ++u) issue_one(pr, u);
   };
 
   // ---- direct loads of the raw fp32 scales of a group (four 128-blocks):
   // lane of wave w handles operand row 64w + lane, 16 bytes (blocks kb..kb+3).
   // Double buffered in LDS behind the tile ring.
-  uint8_t* const sc_lds = lds + STAGES * STAGE;
+  uint8_t* const sc_lds = lds + SLOTS * SLOT;
   // byte offsets of this lane's scale row from the tile's first row, block kb_begin
   uint32_t offSA, offSB = 0;
   const uint8_t* baseSA = reinterpret_cast<const uint8_t*>(g.sa + i0 * nkb + kb_begin);
@@ -194,7 +202,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
     r = r < g.J ? r : g.J - 1;
     offSB = (uint32_t)((r - j0) * nkb * 4);
   }
-  const uint32_t sc0 = lds0 + STAGES * STAGE;
+  const uint32_t sc0 = lds0 + SLOTS * SLOT;
   auto issue_scales = [&](int q) {  // group q -> scale buffer q & 1
     const int qc = q < ngroup ? q : ngroup - 1;
     const uint32_t buf = sc0 + (uint32_t)(q & 1) * SC_BYTES;
@@ -203,25 +211,26 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
   };
   constexpr int SC_LOADS = BROW ? 2 : 1;  // per wave per group
 
-  // ---- fragment reads: lane l holds row l%32 of a 32-row MFMA tile and the
-  // stage's logical chunks 2*(l/32), 2*(l/32)+1 (A and B use the same K order).
+  // ---- fragment reads: lane l holds row l%32 of a 32-row MFMA tile and, of
+  // stage s (half s%2 of its pair slot), logical chunks 4*(s%2) + 2*(l/32) and
+  // the next one (A and B use the same K order).
   const uint32_t wm0 = wm * WM, wn0 = wn * WN;
-  const uint32_t swzl = swz(l32);  // fragment rows start at multiples of 32: same swizzle
-  const uint32_t fragA = (wm0 + l32) * BK + (((2 * g2) ^ swzl) << 4);
-  const uint32_t fragB = A_STAGE + (wn0 + l32) * BK + (((2 * g2) ^ swzl) << 4);
+  const uint32_t swzl = swz(l32);
+  const uint32_t cA0 = (((0 + 2 * g2) ^ swzl) << 4), cA1 = (((4 + 2 * g2) ^ swzl) << 4);
+  const uint32_t rowA = (wm0 + l32) * PK, rowB = A_SLOT + (wn0 + l32) * PK;
   // the second chunk sits 16 bytes after or before the first (signed!)
-  const int32_t hiOff = ((int32_t)((2 * g2 + 1) ^ swzl) - (int32_t)((2 * g2) ^ swzl)) * 16;
-  auto read_frag = [&](int s, uint32_t off) {
-    const uint8_t* p = lds + (s % STAGES) * STAGE + off;
+  const int32_t hiOff = ((swzl & 1) ? -16 : 16);
+  auto read_frag = [&](int st, uint32_t off) {
+    const uint8_t* p = lds + ((st >> 1) % SLOTS) * SLOT + off + ((st & 1) ? cA1 : cA0);
     const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
     const u32x4 hi = *reinterpret_cast<const u32x4*>(p + hiOff);
     return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
-  auto read_frags = [&](int s, v8i* fa, v8i* fb) {
+  auto read_frags = [&](int st, v8i* fa, v8i* fb) {
 #pragma unroll
-    for (int t = 0; t < TM; ++t) fa[t] = read_frag(s, fragA + t * 32 * BK);
+    for (int t = 0; t < TM; ++t) fa[t] = read_frag(st, rowA + t * 32 * PK);
 #pragma unroll
-    for (int t = 0; t < TN; ++t) fb[t] = read_frag(s, fragB + t * 32 * BK);
+    for (int t = 0; t < TN; ++t) fb[t] = read_frag(st, rowB + t * 32 * PK);
   };
   // packed E8M0 scale bytes of group q for this lane's operand rows
   // (row wm0 + 32t + l%32 of A, of B in row mode); weight-block scales are
@@ -232,7 +241,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
   // kb_per_split <= MAX_KB blocks of the slice) is loaded once, up front, into
   // LDS -- no scalar loads in the main loop (their shared lgkmcnt would make
   // the LDS waits drain them)
-  constexpr uint32_t bs_area = STAGES * STAGE + 2 * SC_BYTES;
+  constexpr uint32_t bs_area = SLOTS * SLOT + 2 * SC_BYTES;
   auto issue_block_scales = [&]() {
     const uint8_t* base = reinterpret_cast<const uint8_t*>(g.sb + jblk * g.sb_j + kb_begin * g.sb_r);
 #pragma unroll
@@ -269,38 +278,35 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
   uint32_t sa_cur[TM], sb_cur[TN];
   v8i fa[2][TM], fb[2][TN];
 
-  // Per 8-stage group the vector-memory queue of a wave holds, in order: the
-  // next group's scales (issued with stage 8q), then one tile stage per step.
-  // Waiting for stage s+1 therefore leaves at most the two newer tile stages
-  // and possibly one scale group outstanding; waiting with the smaller count
-  // (tiles only) is always safe, just stricter on the step that issues scales.
-  constexpr int WAIT_TILES = 2 * LOADS_PER_STAGE;
-
-  // prologue: scales of group 0, tile stages 0..2, then stage 0 and group 0 visible
+  // prologue: every weight-block scale of the slice, the scales of group 0,
+  // pairs 0 and 1; then pair 0 and group 0 visible
   if constexpr (!BROW) issue_block_scales();
   issue_scales(0);
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue_stage(s);
-  wait_vmcnt<WAIT_TILES>();  // scales of group 0 and stage 0 have landed
+  issue_pair(0);
+  issue_pair(1);
+  wait_vmcnt<LOADS_PER_PAIR>();  // everything but pair 1 has landed
   lds_barrier();
   read_frags(0, fa[0], fb[0]);
   read_scales(0, sa_cur, sb_cur);
 
-  // One 64-deep stage.  Entry: stage s's fragments are in registers (set
-  // BUF), stage s+1 was issued two stages ago.  After the barrier that makes
-  // stage s+1 visible, the 16 MFMAs of stage s are issued in pairs, and
-  // between pairs the wave reads one fragment of stage s+1 (into the other
-  // register set) and issues one direct load of stage s+3 (into the slot of
-  // stage s-1, whose fragments every wave read before this barrier).  The
-  // sched_barrier fences pin that interleaving so the matrix pipe is never
-  // left waiting on LDS.
-  static_assert(TM == 4 && TN == 4 && LOADS_PER_STAGE == 8, "one read + one load per MFMA pair");
-  auto stage_step = [&](int s, auto buf_tag, auto opsel_tag) {
+  // One 64-deep stage s.  Entry: stage s's fragments are in registers (set
+  // BUF).  The 16 MFMAs of stage s are issued in pairs; between pairs the wave
+  // reads one fragment of stage s+1 (into the other register set).  An odd
+  // stage s = 2p-1 first waits for pair p (stage s+1's slot, issued two stages
+  // ago), passes a barrier -- after which no wave reads the slot of pair p-1
+  // any more (stage s's fragments were read during stage s-1) -- and refills
+  // that slot with pair p+1, two direct loads per MFMA pair.  Even stages
+  // need no wait and no barrier: stage s+1 is in the same pair.  The
+  // sched_barrier fences pin the interleaving.
+  static_assert(TM == 4 && TN == 4 && LOADS_PER_PAIR == 16, "one read + two loads per MFMA pair");
+  auto stage_step = [&](int st, auto buf_tag, auto opsel_tag) {
     constexpr int OPSEL = decltype(opsel_tag)::value;
-    constexpr int BUF = decltype(buf_tag)::value;
+    constexpr int BUF = decltype(buf_tag)::value;  // also the parity of st
     constexpr int NXT = BUF ^ 1;
-    wait_vmcnt<LOADS_PER_STAGE>();  // this wave's part of stage s+1 has landed
-    lds_barrier();                  // ... and every wave's
+    if constexpr (BUF == 1) {
+      wait_vmcnt<0>();  // this wave's part of pair (st+1)/2 (and older) has landed
+      lds_barrier();    // ... and every wave's
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
@@ -310,10 +316,13 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
       acc[a][b0 + 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
           fb[BUF][b0 + 1], fa[BUF][a], acc[a][b0 + 1], 0, 0, OPSEL, (int)sb_cur[b0 + 1], OPSEL, (int)sa_cur[a]);
       // next stage's fragments in the order its MFMAs consume them
-      if (p == 0) fa[NXT][0] = read_frag(s + 1, fragA);
-      else if (p <= 4) fb[NXT][p - 1] = read_frag(s + 1, fragB + (p - 1) * 32 * BK);
-      else fa[NXT][p - 4] = read_frag(s + 1, fragA + (p - 4) * 32 * BK);
-      issue_one(s + STAGES - 1, p);
+      if (p == 0) fa[NXT][0] = read_frag(st + 1, rowA);
+      else if (p <= 4) fb[NXT][p - 1] = read_frag(st + 1, rowB + (p - 1) * 32 * PK);
+      else fa[NXT][p - 4] = read_frag(st + 1, rowA + (p - 4) * 32 * PK);
+      if constexpr (BUF == 1) {
+        issue_one((st + 3) >> 1, 2 * p);
+        issue_one((st + 3) >> 1, 2 * p + 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -321,18 +330,18 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
   // One loop iteration = one group = four 128-blocks = eight 64-deep stages;
   // op_sel (the byte of the packed scales) is a constant in each step.
   for (int q = 0; q < ngroup; ++q) {
-    const int s = 8 * q;
-    issue_scales(q + 1);  // buffer (q+1)&1 was last read at the start of group q-1
-    stage_step(s + 0, IntC<0>{}, IntC<0>{});
-    stage_step(s + 1, IntC<1>{}, IntC<0>{});
-    stage_step(s + 2, IntC<0>{}, IntC<1>{});
-    stage_step(s + 3, IntC<1>{}, IntC<1>{});
-    stage_step(s + 4, IntC<0>{}, IntC<2>{});
-    stage_step(s + 5, IntC<1>{}, IntC<2>{});
-    stage_step(s + 6, IntC<0>{}, IntC<3>{});
-    stage_step(s + 7, IntC<1>{}, IntC<3>{});
-    // group q+1's scales: issued before stage s+8's tiles, which the last
-    // step waited for, so they have landed; every wave passed that barrier
+    const int st = 8 * q;
+    issue_scales(q + 1);  // buffer (q+1)&1 was last read at the end of group q-2
+    stage_step(st + 0, IntC<0>{}, IntC<0>{});
+    stage_step(st + 1, IntC<1>{}, IntC<0>{});
+    stage_step(st + 2, IntC<0>{}, IntC<1>{});
+    stage_step(st + 3, IntC<1>{}, IntC<1>{});
+    stage_step(st + 4, IntC<0>{}, IntC<2>{});
+    stage_step(st + 5, IntC<1>{}, IntC<2>{});
+    stage_step(st + 6, IntC<0>{}, IntC<3>{});
+    stage_step(st + 7, IntC<1>{}, IntC<3>{});
+    // group q+1's scales were issued before the waits of this group's odd
+    // stages and every wave passed their barriers
     read_scales(q + 1, sa_cur, sb_cur);
   }
   wait_vmcnt<0>();  // no direct load may still target this workgroup's LDS at exit
