@@ -80,6 +80,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=("layer", "linear", "stack28"), default="layer")
     ap.add_argument("--algo", choices=("default", "promote", "scaled"), default="default")
+    ap.add_argument("--separate-quant", action="store_true",
+                    help="quantize X and dY with the separate row-group and column-group kernels "
+                         "instead of the one-pass kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
@@ -152,11 +155,28 @@ def qbytes(rows, cols):
     return rows * cols * 3 + rows * (cols // 128) * 4
 
 
+def dual_bytes(rows, cols):
+    return rows * cols * 4 + 2 * rows * (cols // 128) * 4
+
+
+# True: one pass writes both the row-group and the column-group copy of X and
+# of dY; False: two passes (the separate row-group and column-group kernels).
+DUAL = True
+
+
+def quantize_both(fb, T, x, q, s, qT, sT):
+    rows, cols = x.shape
+    if DUAL:
+        T.run("quant_dual", 0, dual_bytes(rows, cols), lambda: fb.fp8_quantize_dual(x, q=q, s=s, qT=qT, sT=sT))
+    else:
+        T.run("quant_rowgroup", 0, qbytes(rows, cols), lambda: fb.fp8_quantize_rowgroup(x, q=q, s=s))
+        T.run("quant_colgroup", 0, qbytes(rows, cols), lambda: fb.fp8_quantize_colgroup(x, qT=qT, sT=sT))
+
+
 def fwd_linear(fb, T, d, algo, x=None):
     n, k = d["N"], d["K"]
     x = d["x"] if x is None else x
-    T.run("quant_rowgroup", 0, qbytes(TOKENS, k), lambda: fb.fp8_quantize_rowgroup(x, q=d["qx"], s=d["sx"]))
-    T.run("quant_colgroup", 0, qbytes(TOKENS, k), lambda: fb.fp8_quantize_colgroup(x, qT=d["qxT"], sT=d["sxT"]))
+    quantize_both(fb, T, x, d["qx"], d["sx"], d["qxT"], d["sxT"])
     T.run("quant_block", 0, n * k * 4 + (n // 128) * (k // 128) * 4,
           lambda: fb.fp8_quantize_block(d["w"], q=d["qw"], qT=d["qwT"], s=d["sw"]))
     T.run("gemm_fprop", 2.0 * TOKENS * n * k, 0,
@@ -167,9 +187,7 @@ def fwd_linear(fb, T, d, algo, x=None):
 
 def bwd_linear(fb, T, d, algo):
     n, k = d["N"], d["K"]
-    T.run("quant_rowgroup", 0, qbytes(TOKENS, n), lambda: fb.fp8_quantize_rowgroup(d["dy"], q=d["qdy"], s=d["sdy"]))
-    T.run("quant_colgroup", 0, qbytes(TOKENS, n),
-          lambda: fb.fp8_quantize_colgroup(d["dy"], qT=d["qdyT"], sT=d["sdyT"]))
+    quantize_both(fb, T, d["dy"], d["qdy"], d["sdy"], d["qdyT"], d["sdyT"])
     T.run("gemm_dgrad", 2.0 * TOKENS * n * k, 0,
           lambda: fb.fp8_block_gemm(fb.FP8BLK_OP_DGRAD, d["qdy"], d["sdy"], d["qwT"], d["sw"], TOKENS, n, k,
                                     algo=algo, out=d["dx"]))
@@ -244,10 +262,11 @@ def bf16_baseline(torch, linears, reps, steps=5):
 
 def cpu_baseline(budget_s):
     """The CPU oracle, as it stands, on a bounded sample of the layer
-    workload, scaled to a whole-step rate: per linear, the oracle quantizes
-    all five operands at full size (timed), then computes a few output rows
-    of each GEMM (timed, scaled by total rows / sampled rows).  Stops after
-    the linear that crosses the time budget."""
+    workload, scaled to a whole-step rate: the oracle quantizes every
+    operand of the four linears at full size (timed), then computes sampled
+    output rows of each linear's fprop, dgrad and wgrad (timed) in rounds
+    until the time budget is spent; GEMM time is scaled by total rows /
+    sampled rows."""
     import numpy as np
     import oracle
     from blockwise_fp8_linear_amd import synth
@@ -255,8 +274,8 @@ def cpu_baseline(budget_s):
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     rows_per = max(8, threads)
     rng = np.random.default_rng(7)
-    flops = t_est = t_spent = 0.0
-    done = []
+    t_q = 0.0
+    ops = []
     for li, (name, n, k) in enumerate(LINEARS):
         x = synth.normal_bf16((TOKENS, k), 1.0, 0, 3, 3 * li)
         w = synth.normal_bf16((n, k), 0.02, 0, 3, 3 * li + 1)
@@ -267,33 +286,38 @@ def cpu_baseline(budget_s):
         qw, _, sw = oracle.quantize_block(w, transpose=False)
         qdy, sdy = oracle.quantize_rowgroup(dy)
         qdyT, sdyT = oracle.quantize_colgroup(dy)
-        t_q = time.perf_counter() - t0
-        rows_m = rng.choice(TOKENS, rows_per, replace=False)
-        rows_n = rng.choice(n, rows_per, replace=False)
-        t0 = time.perf_counter()
-        oracle.gemm_fprop(qx, sx, qw, sw, rows=rows_m)
-        t_f = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        oracle.gemm_dgrad(qdy, sdy, qw, sw, rows=rows_m)
-        t_d = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        oracle.gemm_wgrad(qdyT, sdyT, qxT, sxT, rows=rows_n)
-        t_w = time.perf_counter() - t0
-        t_spent += t_q + t_f + t_d + t_w
-        t_est += t_q + (t_f + t_d) * TOKENS / rows_per + t_w * n / rows_per
-        flops += 3 * 2.0 * TOKENS * n * k
-        done.append(name)
+        t_q += time.perf_counter() - t0
+        ops.append({"rows": TOKENS, "t": 0.0, "done": 0, "flops": 2.0 * TOKENS * n * k,
+                    "fn": lambda r, a=(qx, sx, qw, sw): oracle.gemm_fprop(*a, rows=r)})
+        ops.append({"rows": TOKENS, "t": 0.0, "done": 0, "flops": 2.0 * TOKENS * n * k,
+                    "fn": lambda r, a=(qdy, sdy, qw, sw): oracle.gemm_dgrad(*a, rows=r)})
+        ops.append({"rows": n, "t": 0.0, "done": 0, "flops": 2.0 * TOKENS * n * k,
+                    "fn": lambda r, a=(qdyT, sdyT, qxT, sxT): oracle.gemm_wgrad(*a, rows=r)})
+    t_spent = t_q
+    rounds = 0
+    while True:
+        for op in ops:
+            r = rng.choice(op["rows"], rows_per, replace=False)
+            t0 = time.perf_counter()
+            op["fn"](r)
+            op["t"] += time.perf_counter() - t0
+            op["done"] += rows_per
+        rounds += 1
+        t_spent = t_q + sum(op["t"] for op in ops)
         if t_spent > budget_s:
             break
+    t_est = t_q + sum(op["t"] * op["rows"] / op["done"] for op in ops)
+    flops = sum(op["flops"] for op in ops)
     return {
         "value": round(flops / t_est / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"linears {done}: full-size oracle quantization of X, W and dY (row, column and block "
-                   f"groups) plus {rows_per} output rows of each of fprop/dgrad/wgrad, GEMM time scaled to all "
-                   f"rows; {t_spent:.1f} s of CPU work, est. {t_est:.0f} s per full step, "
-                   f"{platform.processor() or platform.machine()}, {os.cpu_count()} logical CPUs"),
+        "sample": (f"one decoder layer's four linears at 8192 tokens: full-size oracle quantization of X, W and "
+                   f"dY (row, column and block groups), plus {rounds} x {rows_per} sampled output rows of each "
+                   f"fprop/dgrad/wgrad, GEMM time scaled to all rows; {t_spent:.1f} s of CPU work, est. "
+                   f"{t_est:.0f} s per full step, {platform.processor() or platform.machine()}, "
+                   f"{os.cpu_count()} logical CPUs"),
     }
 
 
@@ -309,6 +333,8 @@ def main():
 
     fb.load_library()
     torch.cuda.set_device(0)
+    global DUAL
+    DUAL = not args.separate_quant
     algo = {"default": fb.FP8BLK_ALGO_DEFAULT, "promote": fb.FP8BLK_ALGO_PROMOTE,
             "scaled": fb.FP8BLK_ALGO_SCALED_MFMA}[args.algo]
 
@@ -394,6 +420,7 @@ def main():
         "dtype": "fp8e4m3",
         "data": "synthetic",
         "config": {"workload": desc, "name": args.workload, "tokens": TOKENS, "algo": args.algo,
+                   "quantizer": "separate" if args.separate_quant else "one-pass",
                    "gemm_tflop_per_step": round(step_flops / 1e12, 4)},
         "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
         "gemm_only_TFLOP/s": round(gemm_flops_t / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,

@@ -47,6 +47,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fp8_quantize_rowgroup": [vp, i64, i64, i64, vp, i64, vp, i32, vp],
         "fp8_quantize_colgroup": [vp, i64, i64, i64, vp, i64, vp, i32, vp],
         "fp8_quantize_block": [vp, i64, i64, i64, vp, vp, vp, i32, vp],
+        "fp8_quantize_dual": [vp, i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp],
         "fp8_block_gemm_fprop": [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp],
         "fp8_block_gemm_dgrad": [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp],
         "fp8_block_gemm_wgrad": [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, sz, vp],
@@ -134,6 +135,23 @@ def fp8_quantize_colgroup(x, qT=None, sT=None, stream=None):
     _check(load_library().fp8_quantize_colgroup(x.data_ptr(), rows, cols, x.stride(0), qT.data_ptr(), qT.stride(0),
                                                 sT.data_ptr(), FP8BLK_SCALE_POW2, _stream(stream)))
     return qT, sT
+
+
+def fp8_quantize_dual(x, q=None, s=None, qT=None, sT=None, stream=None):
+    """Row groups and column groups in one pass.  Returns (q, s, qT, sT) equal
+    to fp8_quantize_rowgroup(x) + fp8_quantize_colgroup(x)."""
+    import torch
+    _dev(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else _dev(q, torch.uint8, "q")
+    s = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device) if s is None else _dense(s, torch.float32, "s")
+    qT = torch.empty((cols, rows), dtype=torch.uint8, device=x.device) if qT is None else _dev(qT, torch.uint8, "qT")
+    sT = (torch.empty((cols, rows // 128), dtype=torch.float32, device=x.device) if sT is None
+          else _dense(sT, torch.float32, "sT"))
+    _check(load_library().fp8_quantize_dual(x.data_ptr(), rows, cols, x.stride(0), q.data_ptr(), q.stride(0),
+                                            s.data_ptr(), qT.data_ptr(), qT.stride(0), sT.data_ptr(),
+                                            FP8BLK_SCALE_POW2, _stream(stream)))
+    return q, s, qT, sT
 
 
 def fp8_quantize_block(w, transpose=True, q=None, qT=None, s=None, stream=None):

@@ -83,6 +83,22 @@ int fp8_quantize_colgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   return finish(fp8blk::launch_quant_colgroup(x, rows, cols, ld_x, qT, ld_qT, sT, stream));
 }
 
+int fp8_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q, float* s,
+                      uint8_t* qT, int64_t ld_qT, float* sT, int scale_mode, hipStream_t stream) {
+  if (scale_mode != FP8BLK_SCALE_POW2) return FP8BLK_ERR_ARG;
+  if (!x || !q || !s || !qT || !sT) return FP8BLK_ERR_NULL;
+  if (!mult128(rows) || !mult128(cols)) return FP8BLK_ERR_DIM;
+  if (ld_x < cols || ld_q < cols || ld_qT < rows) return FP8BLK_ERR_ARG;
+  if ((rows / 128) * (cols / 128) >= (int64_t(1) << 31) || rows * ld_x > kMaxElems || rows * ld_q > kMaxElems ||
+      cols * ld_qT > kMaxElems)
+    return FP8BLK_ERR_ARG;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(qT) || !aligned4(s) || !aligned4(sT) || ld_x % 8 || ld_q % 16 ||
+      ld_qT % 16)
+    return FP8BLK_ERR_ALIGN;
+  if (int rc = check_device()) return rc;
+  return finish(fp8blk::launch_quant_dual(x, rows, cols, ld_x, q, ld_q, s, qT, ld_qT, sT, stream));
+}
+
 int fp8_quantize_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld_w, uint8_t* q, uint8_t* qT,
                        float* s, int scale_mode, hipStream_t stream) {
   if (scale_mode != FP8BLK_SCALE_POW2) return FP8BLK_ERR_ARG;

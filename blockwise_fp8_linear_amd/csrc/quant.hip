@@ -207,6 +207,116 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
   if (t == 0) s[(int64_t)bi * col_blocks + bj] = pow2f(e);
 }
 
+
+// ---------------------------------------------------------------------------
+// Row groups and column groups of the same tensor in one pass.  The pages
+// keep the quantized input for Wgrad ("Puro-2B ... part 3/7", section 3.2,
+// fourth paragraph); producing both orientations from one read of the bf16
+// tensor saves a whole second read.  Results are identical to
+// quant_rowgroup_kernel + quant_colgroup_kernel.
+// A workgroup takes a 128 x 128 tile; thread t owns rows 8*(t/16) .. +7 and
+// columns 8*(t%16) .. +7 (one 16-byte load per row; 16 lanes = a 256-byte
+// row).  Row groups: the 16 lanes of a DPP row share the rows, so the row
+// amax is a DPP reduction and each lane stores 8 codes per row.  Column
+// groups: a packed per-column max over the thread's rows, then over the 16
+// row blocks (wave shuffles, then LDS across the 4 waves); the thread's 8x8
+// codes are transposed in registers and each column's 8 codes stored.
+// ---------------------------------------------------------------------------
+constexpr int kDualThreads = 256;
+
+// Four codes, each value with its own inverse scale (four columns).
+__device__ __forceinline__ uint32_t quant4_cols(uint32_t w0, uint32_t w1, const float* inv) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w0) * inv[0], bf16_hi(w0) * inv[1], 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w1) * inv[2], bf16_hi(w1) * inv[3], r, true);
+  return (uint32_t)r;
+}
+
+__global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ s,
+    uint8_t* __restrict__ qT, int64_t ld_qT, float* __restrict__ sT, uint32_t row_tiles, uint32_t col_tiles) {
+  __shared__ uint32_t red[kDualThreads / 64][16][4];
+  const uint32_t t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const uint32_t logical = xcd_remap(blockIdx.x, row_tiles * col_tiles);
+  const uint32_t ct = logical / row_tiles;  // consecutive logical ids walk down the rows
+  const uint32_t rt = logical - ct * row_tiles;
+  const int64_t m0 = (int64_t)rt * 128, c0 = (int64_t)ct * 128;
+  const uint32_t rb = t >> 4, cb = t & 15;
+  const int64_t r0 = m0 + rb * 8;
+
+  u32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (r0 + i) * ld_x + c0 + cb * 8));
+
+  // ---- row groups (this tile's 128 columns are exactly one group per row)
+  const uint32_t G = col_tiles;  // groups per row
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t m = pk_max_u16(pk_max_u16(abs2(v[i].x), abs2(v[i].y)), pk_max_u16(abs2(v[i].z), abs2(v[i].w)));
+    m = max(m & 0xFFFFu, m >> 16);
+    m = row16_max(m);
+    const int e = scale_exponent(m);
+    const float inv = pow2f(-e);
+    uint2 o;
+    o.x = quant4(v[i].x, v[i].y, inv);
+    o.y = quant4(v[i].z, v[i].w, inv);
+    *reinterpret_cast<uint2*>(q + (r0 + i) * ld_q + c0 + cb * 8) = o;
+    if (cb == 0) s[(r0 + i) * G + ct] = pow2f(e);
+  }
+
+  // ---- column groups: packed (two columns per word) max over the 128 rows
+  uint32_t cm[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    cm[0] = pk_max_u16(cm[0], abs2(v[i].x));
+    cm[1] = pk_max_u16(cm[1], abs2(v[i].y));
+    cm[2] = pk_max_u16(cm[2], abs2(v[i].z));
+    cm[3] = pk_max_u16(cm[3], abs2(v[i].w));
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {  // the wave's 4 row blocks of this column block: lanes cb, cb+16, +32, +48
+    cm[w] = pk_max_u16(cm[w], (uint32_t)__shfl_xor((int)cm[w], 16, 64));
+    cm[w] = pk_max_u16(cm[w], (uint32_t)__shfl_xor((int)cm[w], 32, 64));
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) red[wave][cb][w] = cm[w];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    cm[w] = pk_max_u16(pk_max_u16(red[0][cb][w], red[1][cb][w]), pk_max_u16(red[2][cb][w], red[3][cb][w]));
+  float inv[8];
+  int ec[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t a = (j & 1) ? (cm[j >> 1] >> 16) : (cm[j >> 1] & 0xFFFFu);
+    ec[j] = scale_exponent(a);
+    inv[j] = pow2f(-ec[j]);
+  }
+  // codes of row i, columns 0..3 in lo[i] and 4..7 in hi[i], each column with its own scale
+  uint32_t lo[8], hi[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    lo[i] = quant4_cols(v[i].x, v[i].y, &inv[0]);
+    hi[i] = quant4_cols(v[i].z, v[i].w, &inv[4]);
+  }
+  uint32_t ta[4], tb[4];
+  const int64_t cc = c0 + cb * 8;
+  transpose4x4(&lo[0], ta);
+  transpose4x4(&lo[4], tb);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2*>(qT + (cc + j) * ld_qT + r0) = make_uint2(ta[j], tb[j]);
+  transpose4x4(&hi[0], ta);
+  transpose4x4(&hi[4], tb);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2*>(qT + (cc + 4 + j) * ld_qT + r0) = make_uint2(ta[j], tb[j]);
+  if (rb == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sT[(cc + j) * row_tiles + rt] = pow2f(ec[j]);
+  }
+}
+
 // ------------------------------------------------------------- launchers ---
 
 hipError_t launch_quant_rowgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
@@ -235,6 +345,15 @@ hipError_t launch_quant_block(const uint16_t* w, int64_t rows, int64_t cols, int
   const uint32_t cb = (uint32_t)(cols / 128);
   hipLaunchKernelGGL(quant_block_kernel, dim3(rb * cb), dim3(kBlkThreads), 0, stream, w, ld_w, q, qT, s, rows, cols,
                      rb, cb);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                             float* s, uint8_t* qT, int64_t ld_qT, float* sT, hipStream_t stream) {
+  const uint32_t rt = (uint32_t)(rows / 128);
+  const uint32_t ct = (uint32_t)(cols / 128);
+  hipLaunchKernelGGL(quant_dual_kernel, dim3(rt * ct), dim3(kDualThreads), 0, stream, x, ld_x, q, ld_q, s, qT, ld_qT,
+                     sT, rt, ct);
   return hipGetLastError();
 }
 

@@ -120,6 +120,22 @@ int fp8_quantize_colgroup(const uint16_t *x, int64_t rows, int64_t cols, int64_t
                           hipStream_t stream);
 
 /*
+ * Row groups and column groups of the same tensor in one pass: the outputs
+ * of fp8_quantize_rowgroup (q, s) and of fp8_quantize_colgroup (qT, sT),
+ * bit for bit, from a single read of x.  Section 3.2 (fourth paragraph) keeps
+ * the quantized input for Wgrad, so both orientations of X (and of dY) are
+ * needed; one read instead of two saves a third of the quantizer traffic.
+ *   x    [rows][cols] bf16, row stride ld_x (>= cols, multiple of 8)
+ *   q    [rows][cols] codes, row stride ld_q (>= cols, multiple of 16); s [rows][cols/128]
+ *   qT   [cols][rows] codes, row stride ld_qT (>= rows, multiple of 16); sT [cols][rows/128]
+ *   rows and cols positive multiples of 128.
+ */
+int fp8_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                      uint8_t *q, int64_t ld_q, float *s,
+                      uint8_t *qT, int64_t ld_qT, float *sT, int scale_mode,
+                      hipStream_t stream);
+
+/*
  * Weight block quantization (section 3.2, second paragraph: 128x128 blocks).
  *   w    [rows][cols] bf16 (rows = out features N, cols = in features K),
  *        row stride ld_w (>= cols, multiple of 8)

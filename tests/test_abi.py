@@ -23,7 +23,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = fb.header_functions()
     assert set(names) == {
-        "fp8_quantize_rowgroup", "fp8_quantize_colgroup", "fp8_quantize_block",
+        "fp8_quantize_rowgroup", "fp8_quantize_colgroup", "fp8_quantize_block", "fp8_quantize_dual",
         "fp8_block_gemm_fprop", "fp8_block_gemm_dgrad", "fp8_block_gemm_wgrad",
         "fp8_block_gemm", "fp8_block_gemm_workspace_size", "fp8_status_string",
     }
@@ -66,6 +66,33 @@ def test_colgroup_and_block_errors(lib):
     assert g(P, 256, 384, 256, P2, None, P3, 0, None) == EARG
     assert g(P, 256, 384, 384, P2, MIS, P3, 0, None) == EALIGN
     assert g(P, 256, 384, 384, P2, None, P3, 7, None) == EARG
+
+
+def test_dual_errors(lib):
+    f = lib.fp8_quantize_dual
+    P4, P5 = 0x400000, 0x500000
+    ok = (P, 256, 384, 384, P2, 384, P3, P4, 256, P5, 0, None)
+    assert f(*ok) in (EHIP, EDEV)                                 # valid arguments, no GPU here
+
+    def call(**kw):
+        names = ("x", "rows", "cols", "ld_x", "q", "ld_q", "s", "qT", "ld_qT", "sT", "mode", "stream")
+        a = dict(zip(names, ok))
+        a.update(kw)
+        return f(*[a[n] for n in names])
+    assert call(mode=1) == EARG
+    for n in ("x", "q", "s", "qT", "sT"):
+        assert call(**{n: None}) == ENULL, n
+    assert call(rows=200) == EDIM                                 # both dims multiples of 128
+    assert call(cols=200, ld_x=256, ld_q=256) == EDIM
+    assert call(rows=0) == EDIM
+    assert call(ld_x=256) == EARG                                 # ld < cols
+    assert call(ld_q=256) == EARG
+    assert call(ld_qT=128) == EARG                                # ld_qT < rows
+    assert call(x=MIS) == EALIGN
+    assert call(qT=MIS) == EALIGN
+    assert call(sT=P5 + 2) == EALIGN
+    assert call(ld_x=388) == EALIGN                               # not a multiple of 8
+    assert call(ld_qT=264) == EALIGN                              # not a multiple of 16
 
 
 def test_gemm_errors(lib):

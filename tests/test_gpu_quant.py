@@ -181,12 +181,91 @@ def test_block_decoder_layer():
         _assert_block(lin["w"], f"W {lin['name']}")
 
 
+def _assert_dual(x_bits, what, cols=None, pad_q=0, pad_qT=0):
+    """The one-pass quantizer against the oracle's row-group and column-group
+    quantizers, bit for bit; optional strided input and padded outputs (the
+    padding must stay untouched)."""
+    import torch
+    import blockwise_fp8_linear_amd as fb
+    note(f"dual {what} {x_bits.shape} cols={cols} pad={pad_q},{pad_qT}")
+    xt = dev_bf16(x_bits)
+    if cols is not None:
+        xt = xt[:, :cols]
+    rows, c = xt.shape
+    qbuf = torch.full((rows, c + pad_q), 0xAB, dtype=torch.uint8, device="cuda")
+    qTbuf = torch.full((c, rows + pad_qT), 0xCD, dtype=torch.uint8, device="cuda")
+    q, s, qT, sT = fb.fp8_quantize_dual(xt, q=qbuf[:, :c], qT=qTbuf[:, :rows])
+    torch.cuda.synchronize()
+    q0, s0 = oracle.quantize_rowgroup(x_bits, cols=cols)
+    qT0, sT0 = oracle.quantize_colgroup(x_bits, cols=cols)
+    qh, qTh = host(qbuf), host(qTbuf)
+    assert np.array_equal(host(s), s0), f"{what}: row scales differ ({int((host(s) != s0).sum())})"
+    assert np.array_equal(qh[:, :c], q0), f"{what}: row codes differ ({int((qh[:, :c] != q0).sum())})"
+    assert np.array_equal(host(sT), sT0), f"{what}: column scales differ ({int((host(sT) != sT0).sum())})"
+    assert np.array_equal(qTh[:, :rows], qT0), f"{what}: column codes differ ({int((qTh[:, :rows] != qT0).sum())})"
+    assert np.all(qh[:, c:] == 0xAB) and np.all(qTh[:, rows:] == 0xCD), f"{what}: wrote past the end"
+
+
+def test_dual_small_and_edges():
+    x, _ = synth.tiny_fprop()
+    _assert_dual(x, "tiny X")
+    x = synth.normal_bf16((384, 640), 1.0, 47, 0)
+    x[3, 128:256] = 0                                            # zero row group
+    x[128:256, 5] = 0                                            # zero column group
+    x[:128, 7] = np.arange(128, dtype=np.uint16)                 # subnormal column group
+    x[200, 256:384] = (np.arange(128, dtype=np.uint16) | 0x8000)  # subnormal row group
+    x[300, :128] = synth.bf16_bits_from_f32(np.full(128, 3.0e38, np.float32))
+    x[256:384, 639] = synth.bf16_bits_from_f32(np.full(128, -3.0e38, np.float32))
+    _assert_dual(x, "384x640 edges")
+
+
+def test_dual_exhaustive_cast_both_orientations():
+    """The exhaustive cast sweep of the row-group test, padded to whole
+    tiles, through both the row-group side (as is) and the column-group side
+    (transposed)."""
+    mags = (np.arange(0x8000, dtype=np.uint32) << 16).view(np.float32)
+    mags = mags[np.isfinite(mags) & (mags <= 448.0)]
+    vals = np.concatenate([mags, -mags]).astype(np.float32)
+    per = 127
+    ng = (vals.size + per - 1) // per
+    vals = np.concatenate([vals, np.zeros(ng * per - vals.size, np.float32)]).reshape(ng, per)
+    blocks = []
+    for e in range(-126, 119, 3):
+        blk = np.empty((ng, 128), np.float32)
+        blk[:, 0] = 448.0 * np.float32(2.0 ** e)
+        blk[:, 1:] = vals * np.float32(2.0 ** e)
+        blocks.append(blk)
+    x = np.concatenate(blocks).reshape(-1, 128)
+    x = np.concatenate([x, np.zeros(((-x.shape[0]) % 128, 128), np.float32)])
+    xb = synth.bf16_bits_from_f32(x)
+    _assert_dual(xb, "exhaustive cast, row side")
+    _assert_dual(np.ascontiguousarray(xb.T), "exhaustive cast, column side")
+
+
+def test_dual_strided_input_padded_outputs():
+    wide = synth.normal_bf16((1024, 4096), 1.0, 48, 0)
+    _assert_dual(wide, "column slice, padded outputs", cols=2048, pad_q=256, pad_qT=128)
+
+
+def test_dual_decoder_layer():
+    for lin in synth.decoder_layer():
+        _assert_dual(lin["x"], f"X {lin['name']}")
+        _assert_dual(lin["dy"], f"dY {lin['name']}")
+
+
+def test_dual_outlier_stress():
+    x, _, _ = synth.outlier_stress()
+    _assert_dual(x, "outlier X")
+
+
 def test_quantizers_repeatable():
     import torch
     import blockwise_fp8_linear_amd as fb
     x = dev_bf16(synth.normal_bf16((2048, 2048), 1.0, 46, 0))
-    a = [fb.fp8_quantize_rowgroup(x), fb.fp8_quantize_colgroup(x), fb.fp8_quantize_block(x)[::2]]
-    b = [fb.fp8_quantize_rowgroup(x), fb.fp8_quantize_colgroup(x), fb.fp8_quantize_block(x)[::2]]
+    a = [fb.fp8_quantize_rowgroup(x), fb.fp8_quantize_colgroup(x), fb.fp8_quantize_block(x)[::2],
+         fb.fp8_quantize_dual(x)]
+    b = [fb.fp8_quantize_rowgroup(x), fb.fp8_quantize_colgroup(x), fb.fp8_quantize_block(x)[::2],
+         fb.fp8_quantize_dual(x)]
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         for s, t in zip(u, v):
