@@ -134,4 +134,13 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
   return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
 }
 
+// Workgroup barrier that orders LDS only.  (__syncthreads() also waits for
+// every outstanding global access, which would drain loads issued ahead of
+// time; those are waited for where their data is used.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace fp8blk

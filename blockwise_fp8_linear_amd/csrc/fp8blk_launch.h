@@ -32,7 +32,7 @@ struct GemmArgs {
   BScale bmode;
   void* out;                // [I][J]
   bool out_f32;
-  float* ws;                // split-K partials (may be null when splits == 1)
+  float* ws;                // split-K or stream-K workspace (may be null when none is needed)
   int splits;
 };
 
@@ -48,8 +48,10 @@ enum class GemmAlgo { Promote, ScaledMfma };
 
 hipError_t launch_gemm(const GemmArgs& g, GemmAlgo algo, hipStream_t stream);
 
-// The 256x256 block-scaled-MFMA kernel (gemm_mx.hip) and the shapes it takes.
+// The 256x256 block-scaled-MFMA kernel (gemm_mx.hip), the shapes it takes
+// and the workspace its stream-K form (B_ROW, i.e. Wgrad) needs.
 bool gemm_mx_eligible(const GemmArgs& g);
+size_t gemm_mx_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode);
 hipError_t launch_gemm_mx(const GemmArgs& g, hipStream_t stream);
 
 }  // namespace fp8blk

@@ -364,8 +364,12 @@ int gemm_splits(int64_t I, int64_t J, int64_t R, BScale bmode) {
 }
 
 size_t gemm_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode) {
+  // enough for either path: split-K partials of this kernel, or the
+  // stream-K counters and partial tiles of the block-scaled-MFMA kernel
   const int s = gemm_splits(I, J, R, bmode);
-  return s > 1 ? (size_t)s * (size_t)I * (size_t)J * sizeof(float) : 0;
+  const size_t split_bytes = s > 1 ? (size_t)s * (size_t)I * (size_t)J * sizeof(float) : 0;
+  const size_t mx_bytes = gemm_mx_workspace_bytes(I, J, R, bmode);
+  return split_bytes > mx_bytes ? split_bytes : mx_bytes;
 }
 
 template <class C>
@@ -398,11 +402,11 @@ static hipError_t launch_splitk_reduce(const GemmArgs& g, hipStream_t stream) {
 }
 
 hipError_t launch_gemm(const GemmArgs& g, GemmAlgo algo, hipStream_t stream) {
+  // the 256x256 kernel needs no split-K reduction (Wgrad runs stream-K)
+  if (algo == GemmAlgo::ScaledMfma && gemm_mx_eligible(g)) return launch_gemm_mx(g, stream);
   hipError_t e;
   if (algo == GemmAlgo::Promote)
     e = g.bmode == BScale::Row ? launch_cfg<PromoteRow>(g, stream) : launch_cfg<PromoteBlock>(g, stream);
-  else if (gemm_mx_eligible(g))
-    e = launch_gemm_mx(g, stream);
   else
     e = g.bmode == BScale::Row ? launch_cfg<ScaledRow>(g, stream) : launch_cfg<ScaledBlock>(g, stream);
   if (e != hipSuccess || g.splits <= 1) return e;

@@ -4,24 +4,29 @@
 // blocks b of sa(i,b) * sb(j,b) * sum_r A[i][r] B[j][r]; Fprop, Dgrad and Wgrad
 // of the FP8 linear layer, "Puro-2B ... part 3/7", section 3.2), built for
 // throughput:
-//   * 256 x 256 output tile per workgroup, 4 waves of 128 x 128;
+//   * 256 x 256 output tile per workgroup, 4 waves of 128 x 128, one
+//     workgroup per CU (146 KiB of LDS);
 //   * v_mfma_scale_f32_32x32x64_f8f6f4: each operand row carries its
 //     power-of-two scale as an E8M0 byte (the fp32 scale's exponent field),
 //     applied inside the matrix core; products accumulate in place, in fp32,
 //     so the accumulators never leave the matrix registers;
-//   * the reduction advances in 64-deep stages (two per 128-deep scale
-//     block) through a 4-deep LDS ring filled by direct global->LDS 16-byte
-//     loads (no staging registers), three stages in flight;
-//   * a row's 64 bytes are four 16-byte chunks, XOR-swizzled by
-//     ((row >> 1) & 3) so that the fragment reads are free of bank conflicts;
-//   * MFMA fragments are double-buffered in registers: the LDS reads of the
-//     next stage overlap the MFMAs of the current one;
+//   * the reduction advances in 64-deep stages through two LDS "pair slots"
+//     of 128-deep (one scale block) whole-cache-line rows, filled by direct
+//     global->LDS 16-byte loads (no staging registers) issued between the
+//     MFMAs, one pair slot in flight while the other is consumed;
+//   * 16-byte chunks of a row are XOR-swizzled so that fragment reads are
+//     free of bank conflicts; fragments are double-buffered in registers;
 //   * the scale bytes of four consecutive 128-blocks are packed in one
-//     register per operand row and picked by the instruction's op_sel;
-//     weight-block scales are wave-uniform scalar loads.
+//     register per operand row and picked by the instruction's op_sel; the
+//     weight-block scales of a tile are staged in LDS once;
+//   * the epilogue stages each wave's tile through LDS and stores whole rows;
+//   * Wgrad (long reduction over tokens, few output tiles) runs stream-K:
+//     a persistent grid in which every workgroup does the same number of
+//     512-deep reduction units, tiles shared by several workgroups being
+//     summed, in a fixed order, by the last of them to finish.
 // Requirements (else the caller falls back to gemm.hip): the number of
-// 128-blocks per split-K slice is a multiple of 4 and the scale arrays are
-// 16-byte aligned.
+// 128-blocks of the reduction is a multiple of 4 (at most 128 for
+// weight-block scales) and the per-row scale arrays are 16-byte aligned.
 #include "fp8blk_device.h"
 #include "fp8blk_launch.h"
 
@@ -84,14 +89,6 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
 }
 
-// Workgroup barrier that orders LDS only.  (__syncthreads() also waits for
-// every outstanding global access, which would drain the prefetched stages;
-// the direct loads are waited for explicitly with vmcnt instead.)
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 template <int V>
 struct IntC {
@@ -118,39 +115,41 @@ __device__ __forceinline__ uint32_t pack_e8(u32x4 s) {
          (((s[3] >> 23) & 0xFF) << 24);
 }
 
-template <bool BROW>
-__global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t tiles_m, int64_t tiles_n,
-                                                          int64_t kb_per_split) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
-  const uint32_t tid = threadIdx.x, lane = tid & 63;
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t wm = wave >> 1, wn = wave & 1;
-  const uint32_t lds0 = lds_offset(lds);
-  const uint32_t l32 = lane & 31, g2 = lane >> 5;
-
-  // ---- tile / split owned by this workgroup (XCD-aware, grouped along M)
-  const int64_t ntiles = tiles_m * tiles_n;
-  const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t split = L / ntiles;
-  const int64_t tile = L - split * ntiles;
+// Output tile t -> its first row and column: consecutive tiles walk down a
+// group of GM tile rows before moving right, so that tiles in flight
+// together share operand panels in L2.
+__device__ __forceinline__ void tile_origin(int64_t tile, int64_t tiles_m, int64_t tiles_n, int64_t& i0,
+                                            int64_t& j0) {
   constexpr int64_t GM = 8;
   const int64_t group = tile / (GM * tiles_n);
   const int64_t first_m = group * GM;
   const int64_t gsize = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
   const int64_t in_group = tile - group * GM * tiles_n;
-  const int64_t i0 = (first_m + in_group % gsize) * BM;
-  const int64_t j0 = (in_group / gsize) * BN;
+  i0 = (first_m + in_group % gsize) * BM;
+  j0 = (in_group / gsize) * BN;
+}
 
+// The contraction of one output tile over the 128-blocks
+// [kb_begin, kb_begin + nkb_seg) (nkb_seg a multiple of 4) into acc, which it
+// zeroes first.  On return every direct load has landed; the LDS ring may
+// still be read by other waves until the next barrier.
+template <bool BROW>
+__device__ __forceinline__ void mma_segment(const GemmArgs& g, uint8_t* lds, int64_t i0, int64_t j0, int64_t kb_begin,
+                                            int64_t nkb_seg, v16f (&acc)[TM][TN]) {
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t wm = wave >> 1, wn = wave & 1;
+  const uint32_t lds0 = lds_offset(lds);
+  const uint32_t l32 = lane & 31, g2 = lane >> 5;
   const int64_t R = g.R, nkb = R / 128;
-  const int64_t kb_begin = split * kb_per_split;
-  const int ngroup = (int)(kb_per_split / 4);  // groups of four 128-blocks
+  const int ngroup = (int)(nkb_seg / 4);  // groups of four 128-blocks
 
   // ---- direct loads of the tiles, one pair slot (128-deep) at a time.  Wave
   // instruction u fills 8 rows x 128 B; lane p writes LDS bytes p*16..+15 of
   // that KiB: row p/8, physical chunk p%8, which holds logical chunk
   // (p%8) ^ swz(row).  Per-lane 32-bit offsets from wave-uniform bases; rows
   // past a ragged edge read the last row (valid memory, results never stored).
-  const int npair = (int)kb_per_split;
+  const int npair = (int)nkb_seg;
   const uint8_t* baseA = g.a + i0 * R + kb_begin * 128;
   const uint8_t* baseB = g.b + j0 * R + kb_begin * 128;
   uint32_t offLA[LOADS_A], offLB[LOADS_B];
@@ -209,7 +208,6 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
     dma16(baseSA + 16 * qc, offSA, buf + wave * 1024);
     if constexpr (BROW) dma16(baseSB + 16 * qc, offSB, buf + 4096 + wave * 1024);
   };
-  constexpr int SC_LOADS = BROW ? 2 : 1;  // per wave per group
 
   // ---- fragment reads: lane l holds row l%32 of a 32-row MFMA tile and, of
   // stage s (half s%2 of its pair slot), logical chunks 4*(s%2) + 2*(l/32) and
@@ -238,7 +236,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
   // columns are computed but not stored).
   const int64_t jblk = ((j0 + wn0) >> 7) < (g.J >> 7) ? ((j0 + wn0) >> 7) : (g.J >> 7) - 1;
   // weight-block mode: every scale this wave needs (its block column, all
-  // kb_per_split <= MAX_KB blocks of the slice) is loaded once, up front, into
+  // nkb_seg <= MAX_KB blocks of the segment) is loaded once, up front, into
   // LDS -- no scalar loads in the main loop (their shared lgkmcnt would make
   // the LDS waits drain them)
   constexpr uint32_t bs_area = SLOTS * SLOT + 2 * SC_BYTES;
@@ -247,7 +245,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
 #pragma unroll
     for (int h = 0; h < MAX_KB / 64; ++h) {
       int64_t k = h * 64 + lane;
-      k = k < kb_per_split ? k : kb_per_split - 1;
+      k = k < nkb_seg ? k : nkb_seg - 1;
       dma4(base, (uint32_t)(k * g.sb_r * 4), lds0 + bs_area + wave * (MAX_KB * 4) + h * 256);
     }
   };
@@ -269,7 +267,6 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
     }
   };
 
-  v16f acc[TM][TN];
 #pragma unroll
   for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -278,7 +275,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
   uint32_t sa_cur[TM], sb_cur[TN];
   v8i fa[2][TM], fb[2][TN];
 
-  // prologue: every weight-block scale of the slice, the scales of group 0,
+  // prologue: every weight-block scale of the segment, the scales of group 0,
   // pairs 0 and 1; then pair 0 and group 0 visible
   if constexpr (!BROW) issue_block_scales();
   issue_scales(0);
@@ -345,37 +342,58 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
     read_scales(q + 1, sa_cur, sb_cur);
   }
   wait_vmcnt<0>();  // no direct load may still target this workgroup's LDS at exit
+}
 
+// Where a tile goes: a row-major matrix (bf16 bits or fp32) of rows x cols,
+// row stride ld elements; rows and columns past the edge are not stored.
+struct Dst {
+  void* out;
+  int64_t ld, rows, cols;
+  bool f32;
+};
+
+// Store a finished 256 x 256 tile at (i0, j0) of d.  src(a, b) yields the
+// wave's 32x32 accumulator tile (a, b) in the MFMA register layout; it is
+// called once per tile, in (a, b) order.  Starts with a barrier, so the LDS
+// ring and any earlier staging are free.
+template <class Src>
+__device__ __forceinline__ void store_tile_from(const Dst& d, uint8_t* lds, int64_t i0, int64_t j0, Src src) {
   // ---- epilogue, staged through LDS so that global stores are whole rows.
-  // acc[a][b] lane l, element e holds row i = wm0 + 32a + l%32 and column
+  // src(a, b) lane l, element e holds row i = wm0 + 32a + l%32 and column
   // j = wn0 + 32b + 8*(e/4) + 4*(l/32) + e%4.  Each wave writes its 128 x 128
   // tile to its own 32 KiB of LDS in units of 4 consecutive columns, the unit
   // index XOR-swizzled by (row & 31) (conflict-free: the 32 lanes of a write
   // hit 32 different units of their rows), then reads back 16-byte pieces of
   // whole rows and stores them coalesced.  fp32 output goes in two halves of
   // 64 rows.
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  const uint32_t l32 = lane & 31, g2 = lane >> 5;
   lds_barrier();  // every wave is done reading the tile ring
   {
     uint8_t* stage_area = lds + wave * 32768;
-    const bool f32 = g.splits > 1 || g.out_f32;
-    float* const outf = g.splits > 1 ? g.ws + split * g.I * g.J : static_cast<float*>(g.out);
-    uint16_t* const outh = static_cast<uint16_t*>(g.out);
+    const bool f32 = d.f32;
+    float* const outf = static_cast<float*>(d.out);
+    uint16_t* const outh = static_cast<uint16_t*>(d.out);
     const int64_t col0 = j0 + wn0;
     if (!f32) {
       // bf16: unit = 8 bytes, row = 256 bytes, all 128 rows at once
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < TN; ++b)
+        for (int b = 0; b < TN; ++b) {
+          const v16f v = src(a, b);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const uint32_t row = a * 32 + l32;
             const uint32_t unit = (8 * b + 2 * q + g2) ^ (row & 31);
             uint2 o;
-            o.x = f32_to_bf16_rne(acc[a][b][4 * q]) | (f32_to_bf16_rne(acc[a][b][4 * q + 1]) << 16);
-            o.y = f32_to_bf16_rne(acc[a][b][4 * q + 2]) | (f32_to_bf16_rne(acc[a][b][4 * q + 3]) << 16);
+            o.x = f32_to_bf16_rne(v[4 * q]) | (f32_to_bf16_rne(v[4 * q + 1]) << 16);
+            o.y = f32_to_bf16_rne(v[4 * q + 2]) | (f32_to_bf16_rne(v[4 * q + 3]) << 16);
             *reinterpret_cast<uint2*>(stage_area + row * 256 + unit * 8) = o;
           }
+        }
       // read: 16 lanes per row (16 bytes = units 2k, 2k+1 each), 4 rows per pass
 #pragma unroll 4
       for (int pass = 0; pass < 32; ++pass) {
@@ -385,8 +403,8 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
         u32x4 v = *reinterpret_cast<const u32x4*>(stage_area + row * 256 + (pu & ~1u) * 8);
         if (pu & 1) v = u32x4{v[2], v[3], v[0], v[1]};  // the pair is stored swapped
         const int64_t i = i0 + wm0 + row;
-        if (i < g.I && col0 < g.J)
-          *reinterpret_cast<u32x4*>(outh + i * g.J + col0 + 8 * k) = v;
+        if (i < d.rows && col0 < d.cols)
+          *reinterpret_cast<u32x4*>(outh + i * d.ld + col0 + 8 * k) = v;
       }
     } else {
       // fp32: unit = 16 bytes, row = 512 bytes, two halves of 64 rows
@@ -396,14 +414,16 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
         for (int a2 = 0; a2 < 2; ++a2) {
           const int a = 2 * h + a2;
 #pragma unroll
-          for (int b = 0; b < TN; ++b)
+          for (int b = 0; b < TN; ++b) {
+            const v16f t = src(a, b);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const uint32_t row = a2 * 32 + l32;
               const uint32_t unit = (8 * b + 2 * q + g2) ^ (row & 31);
-              const v4f v = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
+              const v4f v = {t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]};
               *reinterpret_cast<v4f*>(stage_area + row * 512 + unit * 16) = v;
             }
+          }
         }
         // read: 32 lanes per row (one unit each), 2 rows per pass
 #pragma unroll 4
@@ -411,27 +431,213 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
           const uint32_t row = pass * 2 + (lane >> 5), k = lane & 31;
           const v4f v = *reinterpret_cast<const v4f*>(stage_area + row * 512 + ((k ^ (row & 31)) * 16));
           const int64_t i = i0 + wm0 + 64 * h + row;
-          if (i < g.I && col0 < g.J) *reinterpret_cast<v4f*>(outf + i * g.J + col0 + 4 * k) = v;
+          if (i < d.rows && col0 < d.cols) *reinterpret_cast<v4f*>(outf + i * d.ld + col0 + 4 * k) = v;
         }
       }
     }
   }
 }
 
+// Store a tile from registers.  (A local copy: reading the caller's array
+// through the reference while storing to LDS makes the compiler keep it in
+// memory -- hundreds of spilled registers.)
+__device__ __forceinline__ void store_tile(const Dst& d, uint8_t* lds, int64_t i0, int64_t j0,
+                                           const v16f (&acc_in)[TM][TN]) {
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = acc_in[a][b];
+  store_tile_from(d, lds, i0, j0, [&](int a, int b) { return acc[a][b]; });
+}
+
+// One output tile per workgroup, the whole reduction (Fprop and Dgrad).
 template <bool BROW>
-hipError_t launch_mx(const GemmArgs& g, int64_t kb_per_split, hipStream_t stream) {
+__global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t tiles_m, int64_t tiles_n) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
+  int64_t i0, j0;
+  tile_origin(tile, tiles_m, tiles_n, i0, j0);
+  v16f acc[TM][TN];
+  mma_segment<BROW>(g, lds, i0, j0, 0, g.R / 128, acc);
+  store_tile(Dst{g.out, g.J, g.I, g.J, g.out_f32}, lds, i0, j0, acc);
+}
+
+// Wgrad (long reduction over tokens, few output tiles) on a persistent grid
+// of G workgroups.  Whole waves of tiles are data-parallel: workgroup w
+// takes tiles w, w + G, ... below dp_tiles = G * floor(T / G).  The
+// remaining tiles run stream-K: their reductions are cut into units of four
+// 128-blocks and workgroup w < Gs = min(G, W) takes units
+// [w W / Gs, (w + 1) W / Gs) of the W = (T - dp_tiles) * U of them, in tile
+// order, so every such workgroup does the same work.  When every tile splits
+// into p equal ranges (Gs divides W, the range length divides U), workgroup
+// w takes range (w mod T') p + w div T' of the T' stream-K tiles instead:
+// the workgroups of one XCD (consecutive w) then cover different tiles at
+// the same depth, sharing operand panels in L2, as a split-K launch would.  A stream-K range is a run of segments: whole tiles are stored
+// directly; a piece of a tile shared by several workgroups is stored, in
+// fp32, to a tile-sized slot of the workspace -- slot 2w for the first
+// segment of range r, 2r + 1 for its last one (the only segments that can
+// be partial) -- and a second kernel adds the pieces of every shared
+// tile in reduction order (deterministic) and stores it.  No workgroup ever
+// waits for another.
+struct SkGeom {
+  int64_t tiles_m, tiles_n;
+  int64_t dp_tiles;  // tiles [0, dp_tiles) are data-parallel
+  int64_t units;     // W: stream-K units (of the tiles from dp_tiles on)
+  int64_t sk_grid;   // Gs = min(G, W): workgroups with stream-K work
+  int64_t sk_tiles;  // T' when the ranges are permuted as above, else 0
+};
+
+__device__ __forceinline__ int64_t sk_start(int64_t w, int64_t W, int64_t G) { return w * W / G; }
+// the workgroup whose range holds unit u: the largest w with start(w) <= u
+__device__ __forceinline__ int64_t sk_owner(int64_t u, int64_t W, int64_t G) { return ((u + 1) * G - 1) / W; }
+
+template <bool BROW>
+__global__ __launch_bounds__(THREADS) void gemm_mx_streamk_kernel(GemmArgs g, SkGeom sg, float* partials) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int64_t G = gridDim.x;
+  const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t U = g.R / 512;  // units per tile
+  const Dst out{g.out, g.J, g.I, g.J, g.out_f32};
+  v16f acc[TM][TN];
+  for (int64_t t = w; t < sg.dp_tiles; t += G) {
+    int64_t i0, j0;
+    tile_origin(t, sg.tiles_m, sg.tiles_n, i0, j0);
+    lds_barrier();  // the previous tile's epilogue is done with LDS
+    mma_segment<BROW>(g, lds, i0, j0, 0, U * 4, acc);
+    store_tile(out, lds, i0, j0, acc);
+  }
+  const int64_t W = sg.units, Gs = sg.sk_grid;
+  // r: this workgroup's range (and slot pair) index
+  const int64_t r = sg.sk_tiles > 0 ? (w % sg.sk_tiles) * (Gs / sg.sk_tiles) + w / sg.sk_tiles : w;
+  const int64_t ubeg = w < Gs ? sk_start(r, W, Gs) : 0, uend = w < Gs ? sk_start(r + 1, W, Gs) : 0;
+  for (int64_t u = ubeg; u < uend;) {
+    const int64_t ts = u / U;                                    // stream-K tile index
+    const int64_t lo = u - ts * U;                               // first unit of the segment, within the tile
+    const int64_t hi = (uend - ts * U) < U ? (uend - ts * U) : U;  // one past its last
+    int64_t i0, j0;
+    tile_origin(sg.dp_tiles + ts, sg.tiles_m, sg.tiles_n, i0, j0);
+    lds_barrier();
+    mma_segment<BROW>(g, lds, i0, j0, lo * 4, (hi - lo) * 4, acc);
+    if (lo == 0 && hi == U) {
+      store_tile(out, lds, i0, j0, acc);
+    } else {
+      float* const slot = partials + (2 * r + (u == ubeg ? 0 : 1)) * (int64_t)(BM * BN);
+      store_tile(Dst{slot, BN, BM, BN, true}, lds, 0, 0, acc);
+    }
+    u = ts * U + hi;
+  }
+}
+
+// The shared stream-K tiles: block (ts, r) sums rows 16r..16r+15 of
+// stream-K tile ts over its pieces in reduction order and stores them.
+// Piece 0 sits in slot 2 f + 1 if range f (the tile's first) started in an
+// earlier tile (the piece is its last segment), else in slot 2 f; piece
+// k >= 1 is the first segment of range f + k, slot 2 (f + k).
+constexpr int FIX_ROWS = 16;
+
+__global__ __launch_bounds__(256) void sk_fixup_kernel(GemmArgs g, SkGeom sg, const float* __restrict__ partials) {
+  const int64_t ts = blockIdx.x / (BM / FIX_ROWS);
+  const int64_t r0 = (blockIdx.x % (BM / FIX_ROWS)) * FIX_ROWS;
+  const int64_t U = g.R / 512, W = sg.units, G = sg.sk_grid;
+  const int64_t f = sk_owner(ts * U, W, G);
+  const int pieces = (int)(sk_owner(ts * U + U - 1, W, G) - f + 1);
+  if (pieces == 1) return;  // stored by the GEMM itself
+  const int64_t first_slot = 2 * f + (sk_start(f, W, G) < ts * U ? 1 : 0);
+  int64_t i0, j0;
+  tile_origin(sg.dp_tiles + ts, sg.tiles_m, sg.tiles_n, i0, j0);
+  constexpr int PER = FIX_ROWS * BN / 4 / 256;  // float4 per thread
+  v4f sum[PER];
+  for (int pc = 0; pc < pieces; ++pc) {
+    const int64_t slot = pc == 0 ? first_slot : 2 * (f + pc);
+    const v4f* src = reinterpret_cast<const v4f*>(partials + slot * (int64_t)(BM * BN) + r0 * BN);
+    v4f v[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) v[k] = __builtin_nontemporal_load(src + threadIdx.x + 256 * k);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      if (pc == 0) sum[k] = v[k];
+      else sum[k] = v4f{sum[k][0] + v[k][0], sum[k][1] + v[k][1], sum[k][2] + v[k][2], sum[k][3] + v[k][3]};
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    const int64_t i = i0 + r0 + idx / (BN / 4), j = j0 + (idx % (BN / 4)) * 4;
+    if (i >= g.I || j >= g.J) continue;
+    if (g.out_f32) {
+      *reinterpret_cast<v4f*>(static_cast<float*>(g.out) + i * g.J + j) = sum[k];
+    } else {
+      uint2 o;
+      o.x = f32_to_bf16_rne(sum[k][0]) | (f32_to_bf16_rne(sum[k][1]) << 16);
+      o.y = f32_to_bf16_rne(sum[k][2]) | (f32_to_bf16_rne(sum[k][3]) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + i * g.J + j) = o;
+    }
+  }
+}
+
+// Persistent grid: one workgroup per CU of an MI355X (fewer for tiny shapes).
+constexpr int64_t kSkGrid = 256;
+
+struct SkPlan {
+  SkGeom geom;
+  int64_t grid;
+  bool partial;  // some stream-K tile is shared by several workgroups (workspace needed)
+  size_t bytes;
+};
+
+SkPlan sk_plan(int64_t I, int64_t J, int64_t R) {
+  SkPlan p{};
+  p.geom.tiles_m = (I + BM - 1) / BM;
+  p.geom.tiles_n = (J + BN - 1) / BN;
+  const int64_t T = p.geom.tiles_m * p.geom.tiles_n, U = R / 512;
+  p.grid = T * U < kSkGrid ? T * U : kSkGrid;
+  p.geom.dp_tiles = (T / p.grid) * p.grid;
+  const int64_t W = (T - p.geom.dp_tiles) * U;
+  const int64_t Gs = W < p.grid ? W : p.grid;
+  p.geom.units = W;
+  p.geom.sk_grid = Gs;
+  // no tile is shared when there is no stream-K part, when a tile is one
+  // unit, or when Gs divides W and U divides W / Gs (whole tiles per workgroup)
+  p.partial = !(W == 0 || U == 1 || (W % Gs == 0 && (W / Gs) % U == 0));
+  p.geom.sk_tiles = (W > 0 && W % Gs == 0 && U % (W / Gs) == 0) ? T - p.geom.dp_tiles : 0;
+  p.bytes = p.partial ? (size_t)(2 * p.grid) * BM * BN * sizeof(float) : 0;
+  return p;
+}
+
+template <class K>
+hipError_t set_lds_attr(K* kernel, bool& done) {  // idempotent; a race only repeats the same call
+  if (done) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     LDS_BYTES);
+  if (e == hipSuccess) done = true;
+  return e;
+}
+
+template <bool BROW>
+hipError_t launch_mx(const GemmArgs& g, hipStream_t stream) {
   const int64_t tiles_m = (g.I + BM - 1) / BM;
   const int64_t tiles_n = (g.J + BN - 1) / BN;
-  const int splits = g.splits > 0 ? g.splits : 1;
-  static bool attr_set = false;  // idempotent; a race only repeats the same call
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mx_kernel<BROW>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(gemm_mx_kernel<BROW>, dim3((uint32_t)(tiles_m * tiles_n * splits)), dim3(THREADS), LDS_BYTES,
-                     stream, g, tiles_m, tiles_n, kb_per_split);
+  static bool attr_set = false;
+  if (hipError_t e = set_lds_attr(&gemm_mx_kernel<BROW>, attr_set)) return e;
+  hipLaunchKernelGGL(gemm_mx_kernel<BROW>, dim3((uint32_t)(tiles_m * tiles_n)), dim3(THREADS), LDS_BYTES, stream, g,
+                     tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+template <bool BROW>
+hipError_t launch_mx_streamk(const GemmArgs& g, hipStream_t stream) {
+  const SkPlan p = sk_plan(g.I, g.J, g.R);
+  static bool attr_set = false;
+  if (hipError_t e = set_lds_attr(&gemm_mx_streamk_kernel<BROW>, attr_set)) return e;
+  float* const partials = p.partial ? g.ws : nullptr;
+  hipLaunchKernelGGL(gemm_mx_streamk_kernel<BROW>, dim3((uint32_t)p.grid), dim3(THREADS), LDS_BYTES, stream, g, p.geom,
+                     partials);
+  if (hipError_t e = hipGetLastError()) return e;
+  if (!p.partial) return hipSuccess;
+  const int64_t sk_tiles = p.geom.tiles_m * p.geom.tiles_n - p.geom.dp_tiles;
+  hipLaunchKernelGGL(sk_fixup_kernel, dim3((uint32_t)(sk_tiles * (BM / FIX_ROWS))), dim3(256), 0, stream, g, p.geom,
+                     partials);
   return hipGetLastError();
 }
 
@@ -439,8 +645,9 @@ hipError_t launch_mx(const GemmArgs& g, int64_t kb_per_split, hipStream_t stream
 
 bool gemm_mx_eligible(const GemmArgs& g) {
   const int64_t nkb = g.R / 128;
-  const int splits = g.splits > 0 ? g.splits : 1;
-  if (nkb % 4 != 0 || nkb % splits != 0 || (nkb / splits) % 4 != 0 || nkb / splits > MAX_KB) return false;
+  if (nkb % 4 != 0) return false;
+  // weight-block mode keeps the tile's whole column of block scales in LDS
+  if (g.bmode == BScale::Block && nkb > MAX_KB) return false;
   // per-lane 32-bit offsets: 256 rows x R bytes of codes, 256 rows of scales
   if (g.R > (int64_t(1) << 22)) return false;
   if ((reinterpret_cast<uintptr_t>(g.sa) & 15) != 0) return false;
@@ -448,11 +655,14 @@ bool gemm_mx_eligible(const GemmArgs& g) {
   return true;
 }
 
+size_t gemm_mx_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode) {
+  if (bmode != BScale::Row || (R / 128) % 4 != 0) return 0;
+  return sk_plan(I, J, R).bytes;
+}
+
 hipError_t launch_gemm_mx(const GemmArgs& g, hipStream_t stream) {
-  const int64_t nkb = g.R / 128;
-  const int splits = g.splits > 0 ? g.splits : 1;
-  const int64_t kb_per_split = nkb / splits;
-  return g.bmode == BScale::Row ? launch_mx<true>(g, kb_per_split, stream) : launch_mx<false>(g, kb_per_split, stream);
+  if (g.bmode == BScale::Row) return launch_mx_streamk<true>(g, stream);
+  return launch_mx<false>(g, stream);
 }
 
 }  // namespace fp8blk

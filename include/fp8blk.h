@@ -180,9 +180,13 @@ int fp8_block_gemm_dgrad(int64_t M, int64_t N, int64_t K,
  *   qxT  [K][M] codes + sxT  [K][M/128]  (fp8_quantize_colgroup of X)
  *   dw   [N][K], bf16 bits or fp32
  *   workspace: device memory of at least
- *     fp8_block_gemm_workspace_size(FP8BLK_OP_WGRAD, M, N, K) bytes (fp32
- *     split-K partials, reduced in a fixed order: results are deterministic);
- *     may be NULL when that size is 0.
+ *     fp8_block_gemm_workspace_size(FP8BLK_OP_WGRAD, M, N, K) bytes, 16-byte
+ *     aligned, contents on entry irrelevant (the library clears what it
+ *     needs): fp32 partial tiles of output tiles whose reduction is shared
+ *     by several workgroups, and their arrival counters.  Partials are
+ *     summed in a fixed order, so results are deterministic.  May be NULL
+ *     when that size is 0.  Two calls that run at the same time need
+ *     separate workspaces.
  */
 int fp8_block_gemm_wgrad(int64_t M, int64_t N, int64_t K,
                          const uint8_t *qdyT, const float *sdyT,

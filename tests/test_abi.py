@@ -122,8 +122,14 @@ def test_workspace_query(lib):
     assert q(1, 8192, 4096, 2048) == 0
     assert q(2, 100, 256, 256) == ctypes.c_size_t(-1).value
     assert q(7, 256, 256, 256) == ctypes.c_size_t(-1).value
-    n = q(2, 8192, 2048, 2048)                          # O-projection wgrad: 64 tiles of 256x256
-    assert n % (2048 * 2048 * 4) == 0 and n >= 2 * 2048 * 2048 * 4
+    # O-projection wgrad: 64 output tiles of 256x256 whose 8192-token
+    # reduction is shared by several workgroups: enough for the stream-K
+    # partial tiles (two 256x256 fp32 slots per workgroup of at most 256)
+    # and for the general kernel's split-K partials
+    n = q(2, 8192, 2048, 2048)
+    assert n >= 2 * 256 * 256 * 256 * 4 and n >= 2 * 2048 * 2048 * 4
+    # a 512-token reduction is one unit per tile: no tile is shared
+    assert q(2, 512, 5120, 7680) == 0
 
 
 def test_valid_call_without_gpu_reports_device_error(lib):

@@ -154,8 +154,8 @@ def test_tiny_fprop_config():
 
 def _sample_rows(n, key, k=24):
     rng = synth.rng_for(*key)
-    fixed = [0, 1, 127, 128, 255, 256, n // 2 + 17, n - 129, n - 1]
-    return np.unique(np.concatenate([fixed, rng.choice(n, k, replace=False)]))
+    fixed = [r for r in (0, 1, 127, 128, 255, 256, n // 2 + 17, n - 129, n - 1) if 0 <= r < n]
+    return np.unique(np.concatenate([fixed, rng.choice(n, min(k, n), replace=False)]))
 
 
 def test_single_linear_fprop_full_size():
@@ -234,3 +234,27 @@ def test_named_entry_points_and_determinism():
     rows = _sample_rows(N, (65, 3), k=8)
     check_op(layer, "wgrad", "promote", rows=rows, what="split-K")
     check_op(layer, "wgrad", "scaled", rows=rows, what="split-K")
+
+
+# Wgrad shapes (M, N, K) that exercise the persistent Wgrad kernel of the
+# 256x256 path (a data-parallel wave of whole tiles, then stream-K over the
+# rest): one output tile shared by 4 workgroups; 15 tiles with a ragged edge
+# shared by up to 18 workgroups of 1-2 reduction units each (some pieces
+# being a workgroup's last segment); 256 whole tiles, then 128 tiles split
+# in two; one unit per tile (several whole tiles per workgroup, no
+# workspace); 256 whole tiles, then 16 tiles in 4 pieces on 64 of the 256
+# workgroups.
+@pytest.mark.parametrize("shape", [(2048, 256, 256), (9216, 1152, 768), (1024, 4096, 6144), (512, 5120, 7680),
+                                   (2048, 4352, 4096)])
+def test_wgrad_streamk_partitions(shape):
+    import torch
+    M, N, K = shape
+    key = (66, M, N, K)
+    layer = Layer(varied((M, K), 1.0, key + (0,)), varied((N, K), 0.02, key + (1,)),
+                  varied((M, N), 1e-3, key + (2,)))
+    rows = _sample_rows(N, key, k=16)
+    check_op(layer, "wgrad", "scaled", rows=rows, what="stream-K")
+    a = layer.gpu("wgrad", fb.FP8BLK_ALGO_SCALED_MFMA, torch.float32)
+    b = layer.gpu("wgrad", fb.FP8BLK_ALGO_SCALED_MFMA, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "stream-K Wgrad is not deterministic"
