@@ -118,11 +118,13 @@ __device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[
   out[3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
 }
 
-// Round fp32 to bf16 (nearest even) for finite values.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 values rounded to bf16 (nearest even), packed: lo in bits 15:0.
+// One v_cvt_pk_bf16_f32 on gfx950.
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const v2bf_t b = __builtin_convertvector((v2f_t{lo, hi}), v2bf_t);
+  return __builtin_bit_cast(uint32_t, b);
 }
 
 // XCD-aware remap of a linear workgroup id.  Consecutive ids are dealt to the

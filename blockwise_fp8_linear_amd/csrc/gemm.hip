@@ -315,8 +315,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
         *reinterpret_cast<v4f*>(static_cast<float*>(g.out) + i * g.J + j) = v;
       } else {
         uint2 o;
-        o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-        o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+        o.x = bf16x2_rne(v[0], v[1]);
+        o.y = bf16x2_rne(v[2], v[3]);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + i * g.J + j) = o;
       }
     }
@@ -337,8 +337,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
       reinterpret_cast<v4f*>(out)[v] = s;
     } else {
       uint2 o;
-      o.x = f32_to_bf16_rne(s[0]) | (f32_to_bf16_rne(s[1]) << 16);
-      o.y = f32_to_bf16_rne(s[2]) | (f32_to_bf16_rne(s[3]) << 16);
+      o.x = bf16x2_rne(s[0], s[1]);
+      o.y = bf16x2_rne(s[2], s[3]);
       reinterpret_cast<uint2*>(out)[v] = o;
     }
   }

@@ -389,8 +389,8 @@ __device__ __forceinline__ void store_tile_from(const Dst& d, uint8_t* lds, int6
             const uint32_t row = a * 32 + l32;
             const uint32_t unit = (8 * b + 2 * q + g2) ^ (row & 31);
             uint2 o;
-            o.x = f32_to_bf16_rne(v[4 * q]) | (f32_to_bf16_rne(v[4 * q + 1]) << 16);
-            o.y = f32_to_bf16_rne(v[4 * q + 2]) | (f32_to_bf16_rne(v[4 * q + 3]) << 16);
+            o.x = bf16x2_rne(v[4 * q], v[4 * q + 1]);
+            o.y = bf16x2_rne(v[4 * q + 2], v[4 * q + 3]);
             *reinterpret_cast<uint2*>(stage_area + row * 256 + unit * 8) = o;
           }
         }
@@ -569,8 +569,8 @@ __global__ __launch_bounds__(256) void sk_fixup_kernel(GemmArgs g, SkGeom sg, co
       *reinterpret_cast<v4f*>(static_cast<float*>(g.out) + i * g.J + j) = sum[k];
     } else {
       uint2 o;
-      o.x = f32_to_bf16_rne(sum[k][0]) | (f32_to_bf16_rne(sum[k][1]) << 16);
-      o.y = f32_to_bf16_rne(sum[k][2]) | (f32_to_bf16_rne(sum[k][3]) << 16);
+      o.x = bf16x2_rne(sum[k][0], sum[k][1]);
+      o.y = bf16x2_rne(sum[k][2], sum[k][3]);
       *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + i * g.J + j) = o;
     }
   }

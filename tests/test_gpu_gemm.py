@@ -258,3 +258,21 @@ def test_wgrad_streamk_partitions(shape):
     b = layer.gpu("wgrad", fb.FP8BLK_ALGO_SCALED_MFMA, torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(a, b), "stream-K Wgrad is not deterministic"
+
+
+# More output tiles than fit in one wave of workgroups, with ragged edges in
+# both output dimensions: Fprop and Dgrad on 17 x 17 = 289 tiles; Wgrad on
+# 17 x 16 tiles = one data-parallel wave plus stream-K over a ragged tile
+# row.
+@pytest.mark.parametrize("shape,ops", [((4224, 4224, 1024), ("fprop",)), ((4224, 1024, 4224), ("dgrad",)),
+                                       ((2048, 4224, 4096), ("wgrad",))])
+def test_many_tiles_ragged(shape, ops):
+    M, N, K = shape
+    key = (67, M, N, K)
+    layer = Layer(varied((M, K), 1.0, key + (0,)), varied((N, K), 0.02, key + (1,)),
+                  varied((M, N), 1e-3, key + (2,)))
+    for op in ops:
+        n = layer.out_rows(op)
+        rows = np.unique(np.concatenate([_sample_rows(n, key + (OPS.index(op),), k=12),
+                                         np.arange(n - 140, n)]))   # the whole ragged last tile row
+        check_op(layer, op, "scaled", rows=rows, what="many tiles")
