@@ -45,7 +45,7 @@ def kernel_of(kind, algo):
     if kind in ("gemm_fprop", "gemm_dgrad"):
         return "gemm_mx_kernel<false>" if fast else "gemm_kernel<promote, weight-block scales>"
     if kind == "gemm_wgrad":
-        return ("gemm_mx_kernel<true> (+ splitk_reduce_kernel)" if fast
+        return ("gemm_mx_streamk_kernel<true> (+ sk_fixup_kernel)" if fast
                 else "gemm_kernel<promote, row scales> (+ splitk_reduce_kernel)")
     return kind + "_kernel"
 
@@ -77,7 +77,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=5,
+                    help="untimed steps before the timed ones (at least 1: the first also counts the launches)")
     ap.add_argument("--workload", choices=("layer", "linear", "stack28"), default="layer")
     ap.add_argument("--algo", choices=("default", "promote", "scaled"), default="default")
     ap.add_argument("--separate-quant", action="store_true",
@@ -88,22 +89,29 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (a known-size reference for HBM byte counters)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    args.warmup = max(1, args.warmup)
+    return args
 
 
 class Timer:
-    """Events around each launch, on the stream the library launches on."""
+    """Events around each launch, on the stream the library launches on.
+    The events are created up front (creating one costs far more host time
+    than recording it); a disabled Timer only counts launches."""
 
-    def __init__(self, torch, enabled):
+    def __init__(self, torch, enabled, n_launches=0):
         self.torch = torch
         self.enabled = enabled
+        self.count = 0
         self.recs = []
+        self.pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(n_launches)] if enabled else []
 
     def run(self, kind, flops, nbytes, fn):
+        self.count += 1
         if not self.enabled:
             return fn()
-        s = self.torch.cuda.Event(enable_timing=True)
-        e = self.torch.cuda.Event(enable_timing=True)
+        s, e = self.pool[len(self.recs)]
         s.record()
         out = fn()
         e.record()
@@ -358,11 +366,13 @@ def main():
         desc = "28 decoder layers' linears, forward chained then backward, 8192 tokens"
 
     null = Timer(torch, False)
-    for _ in range(args.warmup):
+    step(null)  # also counts the launches of one step
+    per_step = null.count
+    for _ in range(args.warmup - 1):
         step(null)
     torch.cuda.synchronize()
 
-    T = Timer(torch, True)
+    T = Timer(torch, True, per_step * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
