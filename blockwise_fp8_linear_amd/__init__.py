@@ -23,6 +23,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp8blk.h")
 FP8BLK_SCALE_POW2 = 0
 FP8BLK_OUT_BF16 = 0
 FP8BLK_OUT_FP32 = 1
+FP8BLK_OUT_FP32_ACCUM = 2
 FP8BLK_OP_FPROP = 0
 FP8BLK_OP_DGRAD = 1
 FP8BLK_OP_WGRAD = 2
@@ -183,8 +184,12 @@ def _out(shape, out_dtype, device, out):
     return torch.empty(shape, dtype=out_dtype, device=device)
 
 
-def _odt(out_dtype):
+def _odt(out_dtype, accumulate=False, out=None):
     import torch
+    if accumulate:
+        if out_dtype != torch.float32 or out is None:
+            raise ValueError("accumulate=True needs out_dtype=torch.float32 and an existing `out` to add to")
+        return FP8BLK_OUT_FP32_ACCUM
     if out_dtype == torch.bfloat16:
         return FP8BLK_OUT_BF16
     if out_dtype == torch.float32:
@@ -197,9 +202,10 @@ def fp8_block_gemm_workspace_size(op: int, M: int, N: int, K: int) -> int:
 
 
 def fp8_block_gemm(op, a, sa, b, sb, M, N, K, out_dtype=None, algo=FP8BLK_ALGO_DEFAULT, out=None,
-                   workspace=None, stream=None):
+                   workspace=None, stream=None, accumulate=False):
     """Any of the three contractions with an explicit algorithm (see
-    fp8_block_gemm in include/fp8blk.h for the operand roles)."""
+    fp8_block_gemm in include/fp8blk.h for the operand roles).  accumulate:
+    out += result in fp32 (out_dtype float32, `out` given)."""
     import torch
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     for t, n in ((a, "a"), (b, "b")):
@@ -214,11 +220,11 @@ def fp8_block_gemm(op, a, sa, b, sb, M, N, K, out_dtype=None, algo=FP8BLK_ALGO_D
     wptr = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load_library().fp8_block_gemm(op, M, N, K, a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(),
-                                         y.data_ptr(), _odt(out_dtype), algo, wptr, wbytes, _stream(stream)))
+                                         y.data_ptr(), _odt(out_dtype, accumulate, out), algo, wptr, wbytes, _stream(stream)))
     return y
 
 
-def fp8_block_gemm_fprop(qx, sx, qw, sw, out_dtype=None, out=None, stream=None):
+def fp8_block_gemm_fprop(qx, sx, qw, sw, out_dtype=None, out=None, stream=None, accumulate=False):
     """Y = X W^T.  qx [M,K], sx [M,K/128], qw [N,K], sw [N/128,K/128] -> Y [M,N]."""
     import torch
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
@@ -230,11 +236,11 @@ def fp8_block_gemm_fprop(qx, sx, qw, sw, out_dtype=None, out=None, stream=None):
         _dense(t, torch.float32, n)
     y = _out((M, N), out_dtype, qx.device, out)
     _check(load_library().fp8_block_gemm_fprop(M, N, K, qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(),
-                                               y.data_ptr(), _odt(out_dtype), _stream(stream)))
+                                               y.data_ptr(), _odt(out_dtype, accumulate, out), _stream(stream)))
     return y
 
 
-def fp8_block_gemm_dgrad(qdy, sdy, qwT, sw, out_dtype=None, out=None, stream=None):
+def fp8_block_gemm_dgrad(qdy, sdy, qwT, sw, out_dtype=None, out=None, stream=None, accumulate=False):
     """dX = dY W.  qdy [M,N], sdy [M,N/128], qwT [K,N], sw [N/128,K/128] -> dX [M,K]."""
     import torch
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
@@ -246,11 +252,12 @@ def fp8_block_gemm_dgrad(qdy, sdy, qwT, sw, out_dtype=None, out=None, stream=Non
         _dense(t, torch.float32, n)
     y = _out((M, K), out_dtype, qdy.device, out)
     _check(load_library().fp8_block_gemm_dgrad(M, N, K, qdy.data_ptr(), sdy.data_ptr(), qwT.data_ptr(),
-                                               sw.data_ptr(), y.data_ptr(), _odt(out_dtype), _stream(stream)))
+                                               sw.data_ptr(), y.data_ptr(), _odt(out_dtype, accumulate, out), _stream(stream)))
     return y
 
 
-def fp8_block_gemm_wgrad(qdyT, sdyT, qxT, sxT, out_dtype=None, out=None, workspace=None, stream=None):
+def fp8_block_gemm_wgrad(qdyT, sdyT, qxT, sxT, out_dtype=None, out=None, workspace=None, stream=None,
+                         accumulate=False):
     """dW = dY^T X.  qdyT [N,M], sdyT [N,M/128], qxT [K,M], sxT [K,M/128] -> dW [N,K]."""
     import torch
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
@@ -267,6 +274,6 @@ def fp8_block_gemm_wgrad(qdyT, sdyT, qxT, sxT, out_dtype=None, out=None, workspa
     wptr = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load_library().fp8_block_gemm_wgrad(M, N, K, qdyT.data_ptr(), sdyT.data_ptr(), qxT.data_ptr(),
-                                               sxT.data_ptr(), y.data_ptr(), _odt(out_dtype), wptr, wbytes,
+                                               sxT.data_ptr(), y.data_ptr(), _odt(out_dtype, accumulate, out), wptr, wbytes,
                                                _stream(stream)))
     return y

@@ -114,7 +114,8 @@ int fp8_quantize_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld
 
 static int check_gemm_common(int64_t M, int64_t N, int64_t K, const void* a, const float* sa, const void* b,
                              const float* sb, const void* out, int out_dtype) {
-  if (out_dtype != FP8BLK_OUT_BF16 && out_dtype != FP8BLK_OUT_FP32) return FP8BLK_ERR_ARG;
+  if (out_dtype != FP8BLK_OUT_BF16 && out_dtype != FP8BLK_OUT_FP32 && out_dtype != FP8BLK_OUT_FP32_ACCUM)
+    return FP8BLK_ERR_ARG;
   if (!a || !sa || !b || !sb || !out) return FP8BLK_ERR_NULL;
   if (!mult128(M) || !mult128(N) || !mult128(K)) return FP8BLK_ERR_DIM;
   if (M * N > kMaxElems || M * K > kMaxElems || N * K > kMaxElems || M / 128 >= (1 << 20) || N / 128 >= (1 << 20) ||
@@ -136,7 +137,7 @@ int fp8_block_gemm(int op, int64_t M, int64_t N, int64_t K, const uint8_t* a, co
   if (int rc = check_gemm_common(M, N, K, a, sa, b, sb, out, out_dtype)) return rc;
   fp8blk::GemmArgs g{};
   g.a = a; g.sa = sa; g.b = b; g.sb = sb;
-  g.out = out; g.out_f32 = out_dtype == FP8BLK_OUT_FP32;
+  g.out = out; g.out_f32 = out_dtype != FP8BLK_OUT_BF16; g.accumulate = out_dtype == FP8BLK_OUT_FP32_ACCUM;
   if (op == FP8BLK_OP_FPROP) {
     // Y[m][n] = sum_k X[m][k] W[n][k]; weight block (n/128, k/128)
     g.I = M; g.J = N; g.R = K;

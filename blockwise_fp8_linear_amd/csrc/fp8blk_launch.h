@@ -32,6 +32,7 @@ struct GemmArgs {
   BScale bmode;
   void* out;                // [I][J]
   bool out_f32;
+  bool accumulate;          // fp32 output only: out += result
   float* ws;                // split-K or stream-K workspace (may be null when none is needed)
   int splits;
 };

@@ -312,7 +312,13 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
         float* dst = g.ws + split * g.I * g.J + i * g.J + j;
         *reinterpret_cast<v4f*>(dst) = v;
       } else if (g.out_f32) {
-        *reinterpret_cast<v4f*>(static_cast<float*>(g.out) + i * g.J + j) = v;
+        v4f* const dst = reinterpret_cast<v4f*>(static_cast<float*>(g.out) + i * g.J + j);
+        if (g.accumulate) {
+          const v4f o = *dst;
+          *dst = v4f{o[0] + v[0], o[1] + v[1], o[2] + v[2], o[3] + v[3]};
+        } else {
+          *dst = v;
+        }
       } else {
         uint2 o;
         o.x = bf16x2_rne(v[0], v[1]);
@@ -323,9 +329,10 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
   }
 }
 
-// Deterministic split-K reduction: out[idx] = sum over s in order of ws[s][idx].
+// Deterministic split-K reduction: out[idx] = sum over s in order of ws[s][idx] (added to
+// out[idx] when accumulating).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int splits, int64_t n4,
-                                                            void* out, bool out_f32) {
+                                                            void* out, bool out_f32, bool accumulate) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < n4; v += stride) {
     v4f s = reinterpret_cast<const v4f*>(ws)[v];
@@ -334,6 +341,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
       s[0] += t[0]; s[1] += t[1]; s[2] += t[2]; s[3] += t[3];
     }
     if (out_f32) {
+      if (accumulate) {
+        const v4f o = reinterpret_cast<const v4f*>(out)[v];
+        s = v4f{o[0] + s[0], o[1] + s[1], o[2] + s[2], o[3] + s[3]};
+      }
       reinterpret_cast<v4f*>(out)[v] = s;
     } else {
       uint2 o;
@@ -397,7 +408,7 @@ static hipError_t launch_splitk_reduce(const GemmArgs& g, hipStream_t stream) {
   int64_t rblocks = (n4 + 255) / 256;
   if (rblocks > 4096) rblocks = 4096;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)rblocks), dim3(256), 0, stream, g.ws, g.splits, n4, g.out,
-                     g.out_f32);
+                     g.out_f32, g.accumulate);
   return hipGetLastError();
 }
 

@@ -350,6 +350,7 @@ struct Dst {
   void* out;
   int64_t ld, rows, cols;
   bool f32;
+  bool acc;  // fp32: out += tile
 };
 
 // Store a finished 256 x 256 tile at (i0, j0) of d.  src(a, b) yields the
@@ -431,7 +432,15 @@ __device__ __forceinline__ void store_tile_from(const Dst& d, uint8_t* lds, int6
           const uint32_t row = pass * 2 + (lane >> 5), k = lane & 31;
           const v4f v = *reinterpret_cast<const v4f*>(stage_area + row * 512 + ((k ^ (row & 31)) * 16));
           const int64_t i = i0 + wm0 + 64 * h + row;
-          if (i < d.rows && col0 < d.cols) *reinterpret_cast<v4f*>(outf + i * d.ld + col0 + 4 * k) = v;
+          if (i < d.rows && col0 < d.cols) {
+            v4f* const dst = reinterpret_cast<v4f*>(outf + i * d.ld + col0 + 4 * k);
+            if (d.acc) {
+              const v4f o = *dst;
+              *dst = v4f{o[0] + v[0], o[1] + v[1], o[2] + v[2], o[3] + v[3]};
+            } else {
+              *dst = v;
+            }
+          }
         }
       }
     }
@@ -460,7 +469,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
   tile_origin(tile, tiles_m, tiles_n, i0, j0);
   v16f acc[TM][TN];
   mma_segment<BROW>(g, lds, i0, j0, 0, g.R / 128, acc);
-  store_tile(Dst{g.out, g.J, g.I, g.J, g.out_f32}, lds, i0, j0, acc);
+  store_tile(Dst{g.out, g.J, g.I, g.J, g.out_f32, g.accumulate}, lds, i0, j0, acc);
 }
 
 // Wgrad (long reduction over tokens, few output tiles) on a persistent grid
@@ -498,7 +507,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_streamk_kernel(GemmArgs g, Sk
   const int64_t G = gridDim.x;
   const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t U = g.R / 512;  // units per tile
-  const Dst out{g.out, g.J, g.I, g.J, g.out_f32};
+  const Dst out{g.out, g.J, g.I, g.J, g.out_f32, g.accumulate};
   v16f acc[TM][TN];
   for (int64_t t = w; t < sg.dp_tiles; t += G) {
     int64_t i0, j0;
@@ -523,7 +532,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_streamk_kernel(GemmArgs g, Sk
       store_tile(out, lds, i0, j0, acc);
     } else {
       float* const slot = partials + (2 * r + (u == ubeg ? 0 : 1)) * (int64_t)(BM * BN);
-      store_tile(Dst{slot, BN, BM, BN, true}, lds, 0, 0, acc);
+      store_tile(Dst{slot, BN, BM, BN, true, false}, lds, 0, 0, acc);
     }
     u = ts * U + hi;
   }
@@ -566,7 +575,13 @@ __global__ __launch_bounds__(256) void sk_fixup_kernel(GemmArgs g, SkGeom sg, co
     const int64_t i = i0 + r0 + idx / (BN / 4), j = j0 + (idx % (BN / 4)) * 4;
     if (i >= g.I || j >= g.J) continue;
     if (g.out_f32) {
-      *reinterpret_cast<v4f*>(static_cast<float*>(g.out) + i * g.J + j) = sum[k];
+      v4f* const dst = reinterpret_cast<v4f*>(static_cast<float*>(g.out) + i * g.J + j);
+      if (g.accumulate) {
+        const v4f o = *dst;
+        *dst = v4f{o[0] + sum[k][0], o[1] + sum[k][1], o[2] + sum[k][2], o[3] + sum[k][3]};
+      } else {
+        *dst = sum[k];
+      }
     } else {
       uint2 o;
       o.x = bf16x2_rne(sum[k][0], sum[k][1]);

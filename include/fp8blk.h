@@ -63,8 +63,11 @@ extern "C" {
 /* Scale rule.  Only the power-of-two rule is implemented. */
 enum fp8blk_scale_mode { FP8BLK_SCALE_POW2 = 0 };
 
-/* GEMM output element type. */
-enum fp8blk_out_dtype { FP8BLK_OUT_BF16 = 0, FP8BLK_OUT_FP32 = 1 };
+/* GEMM output element type.  FP32_ACCUM: fp32 output that the result is
+ * added to (out = fl32(out + result)), for gradients accumulated in fp32 over
+ * micro-batches; the result is the one FP8BLK_OUT_FP32 would store, bit for
+ * bit, so the sum is deterministic too. */
+enum fp8blk_out_dtype { FP8BLK_OUT_BF16 = 0, FP8BLK_OUT_FP32 = 1, FP8BLK_OUT_FP32_ACCUM = 2 };
 
 /* Which contraction (for fp8_block_gemm and the workspace query). */
 enum fp8blk_op { FP8BLK_OP_FPROP = 0, FP8BLK_OP_DGRAD = 1, FP8BLK_OP_WGRAD = 2 };
@@ -153,7 +156,8 @@ int fp8_quantize_block(const uint16_t *w, int64_t rows, int64_t cols, int64_t ld
  * Fprop  Y = X W^T  (section 3.2, fourth paragraph).
  *   qx [M][K] codes + sx [M][K/128]   (from fp8_quantize_rowgroup of X)
  *   qw [N][K] codes + sw [N/128][K/128] (from fp8_quantize_block of W)
- *   y  [M][N], bf16 bits (out_dtype FP8BLK_OUT_BF16) or fp32 (FP8BLK_OUT_FP32)
+ *   y  [M][N], bf16 bits (out_dtype FP8BLK_OUT_BF16) or fp32 (FP8BLK_OUT_FP32;
+ *      FP8BLK_OUT_FP32_ACCUM adds to it)
  *   M, N, K positive multiples of 128; all operands dense.
  */
 int fp8_block_gemm_fprop(int64_t M, int64_t N, int64_t K,
@@ -166,7 +170,7 @@ int fp8_block_gemm_fprop(int64_t M, int64_t N, int64_t K,
  *   qdy [M][N] codes + sdy [M][N/128]  (from fp8_quantize_rowgroup of dY)
  *   qwT [K][N] codes (the transposed copy from fp8_quantize_block of W)
  *   sw  [N/128][K/128] the same block scales as Fprop
- *   dx  [M][K], bf16 bits or fp32
+ *   dx  [M][K], bf16 bits or fp32 (or fp32 accumulated, as for Fprop)
  */
 int fp8_block_gemm_dgrad(int64_t M, int64_t N, int64_t K,
                          const uint8_t *qdy, const float *sdy,
@@ -178,14 +182,14 @@ int fp8_block_gemm_dgrad(int64_t M, int64_t N, int64_t K,
  * over the M tokens, so both operands are column-group quantized.
  *   qdyT [N][M] codes + sdyT [N][M/128]  (fp8_quantize_colgroup of dY)
  *   qxT  [K][M] codes + sxT  [K][M/128]  (fp8_quantize_colgroup of X)
- *   dw   [N][K], bf16 bits or fp32
+ *   dw   [N][K], bf16 bits or fp32 (FP8BLK_OUT_FP32_ACCUM: dw += dY^T X in
+ *        fp32, the usual fp32 main-gradient accumulation)
  *   workspace: device memory of at least
  *     fp8_block_gemm_workspace_size(FP8BLK_OP_WGRAD, M, N, K) bytes, 16-byte
- *     aligned, contents on entry irrelevant (the library clears what it
- *     needs): fp32 partial tiles of output tiles whose reduction is shared
- *     by several workgroups, and their arrival counters.  Partials are
- *     summed in a fixed order, so results are deterministic.  May be NULL
- *     when that size is 0.  Two calls that run at the same time need
+ *     aligned, contents on entry irrelevant: fp32 partial tiles of output
+ *     tiles whose reduction is shared by several workgroups, which a second
+ *     kernel sums in a fixed order, so results are deterministic.  May be
+ *     NULL when that size is 0.  Two calls that run at the same time need
  *     separate workspaces.
  */
 int fp8_block_gemm_wgrad(int64_t M, int64_t N, int64_t K,

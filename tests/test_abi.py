@@ -98,6 +98,8 @@ def test_dual_errors(lib):
 def test_gemm_errors(lib):
     f = lib.fp8_block_gemm_fprop
     assert f(256, 256, 256, P, P3, P2, P3, P, 5, None) == EARG           # out dtype
+    assert f(256, 256, 256, P, P3, P2, P3, P, 3, None) == EARG
+    assert f(256, 256, 256, P, P3, P2, P3, P, 2, None) in (EHIP, EDEV)  # fp32 accumulate: valid
     assert f(256, 256, 256, None, P3, P2, P3, P, 0, None) == ENULL
     assert f(256, 256, 256, P, P3, P2, None, P, 0, None) == ENULL
     assert f(256, 200, 256, P, P3, P2, P3, P, 0, None) == EDIM

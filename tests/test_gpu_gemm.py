@@ -276,3 +276,32 @@ def test_many_tiles_ragged(shape, ops):
         rows = np.unique(np.concatenate([_sample_rows(n, key + (OPS.index(op),), k=12),
                                          np.arange(n - 140, n)]))   # the whole ragged last tile row
         check_op(layer, op, "scaled", rows=rows, what="many tiles")
+
+
+# fp32 accumulation into an existing output (FP8BLK_OUT_FP32_ACCUM, the fp32
+# main-gradient case): the result must be exactly fl32(old + r), r being what
+# FP8BLK_OUT_FP32 stores, for every op, both algorithms, and the Wgrad paths
+# that sum partial tiles (stream-K fix-up, split-K reduction).
+@pytest.mark.parametrize("shape", [(1024, 4096, 6144), (2048, 256, 256), (640, 384, 1024)])
+def test_fp32_accumulate(shape):
+    import torch
+    M, N, K = shape
+    key = (68, M, N, K)
+    layer = Layer(varied((M, K), 1.0, key + (0,)), varied((N, K), 0.02, key + (1,)),
+                  varied((M, N), 1e-3, key + (2,)))
+    g = layer.g
+    args = {"fprop": (fb.FP8BLK_OP_FPROP, g["qx"], g["sx"], g["qw"], g["sw"], (M, N)),
+            "dgrad": (fb.FP8BLK_OP_DGRAD, g["qdy"], g["sdy"], g["qwT"], g["sw"], (M, K)),
+            "wgrad": (fb.FP8BLK_OP_WGRAD, g["qdyT"], g["sdyT"], g["qxT"], g["sxT"], (N, K))}
+    gen = torch.Generator(device="cuda").manual_seed(68)
+    for op, (opc, a, sa, b, sb, oshape) in args.items():
+        for algo_name, algo in ALGOS.items():
+            old = torch.randn(oshape, device="cuda", dtype=torch.float32, generator=gen)
+            r = fb.fp8_block_gemm(opc, a, sa, b, sb, M, N, K, out_dtype=torch.float32, algo=algo)
+            acc = old.clone()
+            fb.fp8_block_gemm(opc, a, sa, b, sb, M, N, K, out_dtype=torch.float32, algo=algo, out=acc,
+                              accumulate=True)
+            torch.cuda.synchronize()
+            want = host_f32(old) + host_f32(r)          # float32 + float32 in numpy: one rounding
+            got = host_f32(acc)
+            assert np.array_equal(got, want), f"{op} {algo_name} {shape}: accumulation differs"
