@@ -44,6 +44,8 @@ def kernel_of(kind, algo):
     fast = algo in ("default", "scaled")
     if kind in ("gemm_fprop", "gemm_dgrad"):
         return "gemm_mx_kernel<false>" if fast else "gemm_kernel<promote, weight-block scales>"
+    if kind == "gemm_bwd":
+        return "gemm_mx_bwd_kernel (+ bwd_fixup_kernel)"
     if kind == "gemm_wgrad":
         return ("gemm_mx_streamk_kernel<true> (+ sk_fixup_kernel)" if fast
                 else "gemm_kernel<promote, row scales> (+ splitk_reduce_kernel)")
@@ -84,6 +86,8 @@ def parse():
     ap.add_argument("--separate-quant", action="store_true",
                     help="quantize X and dY with the separate row-group and column-group kernels "
                          "instead of the one-pass kernel")
+    ap.add_argument("--separate-bwd", action="store_true",
+                    help="run Dgrad and Wgrad as two calls instead of fp8_block_gemm_backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
@@ -153,7 +157,8 @@ def build_layer(torch, fb, synth, seed, linears=LINEARS, x_in=None):
         d["y"] = torch.empty((TOKENS, n), dtype=torch.bfloat16, device="cuda")
         d["dx"] = torch.empty((TOKENS, k), dtype=torch.bfloat16, device="cuda")
         d["dw"] = torch.empty((n, k), dtype=torch.bfloat16, device="cuda")
-        ws = fb.fp8_block_gemm_workspace_size(fb.FP8BLK_OP_WGRAD, TOKENS, n, k)
+        ws = max(fb.fp8_block_gemm_workspace_size(fb.FP8BLK_OP_WGRAD, TOKENS, n, k),
+                 fb.fp8_block_gemm_workspace_size(fb.FP8BLK_OP_BACKWARD, TOKENS, n, k))
         d["ws"] = torch.empty(max(ws, 16), dtype=u8, device="cuda")
         L.append(d)
     return L
@@ -170,6 +175,9 @@ def dual_bytes(rows, cols):
 # True: one pass writes both the row-group and the column-group copy of X and
 # of dY; False: two passes (the separate row-group and column-group kernels).
 DUAL = True
+# True: Dgrad and Wgrad of a linear in one call (fp8_block_gemm_backward);
+# False: the two separate calls.
+FUSED_BWD = True
 
 
 def quantize_both(fb, T, x, q, s, qT, sT):
@@ -196,6 +204,11 @@ def fwd_linear(fb, T, d, algo, x=None):
 def bwd_linear(fb, T, d, algo):
     n, k = d["N"], d["K"]
     quantize_both(fb, T, d["dy"], d["qdy"], d["sdy"], d["qdyT"], d["sdyT"])
+    if FUSED_BWD and algo == fb.FP8BLK_ALGO_DEFAULT:
+        T.run("gemm_bwd", 2 * 2.0 * TOKENS * n * k, 0,
+              lambda: fb.fp8_block_gemm_backward(d["qdy"], d["sdy"], d["qwT"], d["sw"], d["qdyT"], d["sdyT"],
+                                                 d["qxT"], d["sxT"], dx=d["dx"], dw=d["dw"], workspace=d["ws"]))
+        return
     T.run("gemm_dgrad", 2.0 * TOKENS * n * k, 0,
           lambda: fb.fp8_block_gemm(fb.FP8BLK_OP_DGRAD, d["qdy"], d["sdy"], d["qwT"], d["sw"], TOKENS, n, k,
                                     algo=algo, out=d["dx"]))
@@ -341,8 +354,9 @@ def main():
 
     fb.load_library()
     torch.cuda.set_device(0)
-    global DUAL
+    global DUAL, FUSED_BWD
     DUAL = not args.separate_quant
+    FUSED_BWD = not args.separate_bwd
     algo = {"default": fb.FP8BLK_ALGO_DEFAULT, "promote": fb.FP8BLK_ALGO_PROMOTE,
             "scaled": fb.FP8BLK_ALGO_SCALED_MFMA}[args.algo]
 
@@ -431,6 +445,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "name": args.workload, "tokens": TOKENS, "algo": args.algo,
                    "quantizer": "separate" if args.separate_quant else "one-pass",
+                   "backward": "separate" if args.separate_bwd else "fused",
                    "gemm_tflop_per_step": round(step_flops / 1e12, 4)},
         "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
         "gemm_only_TFLOP/s": round(gemm_flops_t / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,

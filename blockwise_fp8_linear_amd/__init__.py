@@ -27,6 +27,7 @@ FP8BLK_OUT_FP32_ACCUM = 2
 FP8BLK_OP_FPROP = 0
 FP8BLK_OP_DGRAD = 1
 FP8BLK_OP_WGRAD = 2
+FP8BLK_OP_BACKWARD = 3
 FP8BLK_ALGO_DEFAULT = 0
 FP8BLK_ALGO_PROMOTE = 1
 FP8BLK_ALGO_SCALED_MFMA = 2
@@ -53,6 +54,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fp8_block_gemm_dgrad": [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp],
         "fp8_block_gemm_wgrad": [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, sz, vp],
         "fp8_block_gemm": [i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp],
+        "fp8_block_gemm_backward": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, vp, sz, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -277,3 +279,33 @@ def fp8_block_gemm_wgrad(qdyT, sdyT, qxT, sxT, out_dtype=None, out=None, workspa
                                                sxT.data_ptr(), y.data_ptr(), _odt(out_dtype, accumulate, out), wptr, wbytes,
                                                _stream(stream)))
     return y
+
+
+def fp8_block_gemm_backward(qdy, sdy, qwT, sw, qdyT, sdyT, qxT, sxT, dx_dtype=None, dw_dtype=None, dx=None,
+                            dw=None, workspace=None, stream=None, accumulate_dw=False):
+    """Dgrad and Wgrad of one linear in one call.  Operands as for
+    fp8_block_gemm_dgrad and fp8_block_gemm_wgrad; returns (dx [M,K], dw [N,K]).
+    accumulate_dw: dw += dY^T X in fp32 (dw_dtype float32, `dw` given)."""
+    import torch
+    dx_dtype = torch.bfloat16 if dx_dtype is None else dx_dtype
+    dw_dtype = torch.bfloat16 if dw_dtype is None else dw_dtype
+    M, N = qdy.shape
+    K = qwT.shape[0]
+    for t, n in ((qdy, "qdy"), (qwT, "qwT"), (qdyT, "qdyT"), (qxT, "qxT")):
+        _dense(t, torch.uint8, n)
+    for t, n in ((sdy, "sdy"), (sw, "sw"), (sdyT, "sdyT"), (sxT, "sxT")):
+        _dense(t, torch.float32, n)
+    x = _out((M, K), dx_dtype, qdy.device, dx)
+    w = _out((N, K), dw_dtype, qdy.device, dw)
+    need = fp8_block_gemm_workspace_size(FP8BLK_OP_BACKWARD, M, N, K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=qdy.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().fp8_block_gemm_backward(M, N, K, qdy.data_ptr(), sdy.data_ptr(), qwT.data_ptr(),
+                                                  sw.data_ptr(), qdyT.data_ptr(), sdyT.data_ptr(), qxT.data_ptr(),
+                                                  sxT.data_ptr(), x.data_ptr(), _odt(dx_dtype),
+                                                  w.data_ptr(), _odt(dw_dtype, accumulate_dw, dw), wptr, wbytes,
+                                                  _stream(stream)))
+    return x, w
+

@@ -128,13 +128,9 @@ static int check_gemm_common(int64_t M, int64_t N, int64_t K, const void* a, con
 // The algorithm FP8BLK_ALGO_DEFAULT resolves to.
 constexpr fp8blk::GemmAlgo kDefaultAlgo = fp8blk::GemmAlgo::ScaledMfma;
 
-int fp8_block_gemm(int op, int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa, const uint8_t* b,
-                   const float* sb, void* out, int out_dtype, int algo, void* workspace, size_t ws_bytes,
-                   hipStream_t stream) {
-  if (op != FP8BLK_OP_FPROP && op != FP8BLK_OP_DGRAD && op != FP8BLK_OP_WGRAD) return FP8BLK_ERR_ARG;
-  if (algo != FP8BLK_ALGO_DEFAULT && algo != FP8BLK_ALGO_PROMOTE && algo != FP8BLK_ALGO_SCALED_MFMA)
-    return FP8BLK_ERR_ARG;
-  if (int rc = check_gemm_common(M, N, K, a, sa, b, sb, out, out_dtype)) return rc;
+// The kernel-side description of one contraction (arguments already checked).
+static fp8blk::GemmArgs make_args(int op, int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
+                                  const uint8_t* b, const float* sb, void* out, int out_dtype) {
   fp8blk::GemmArgs g{};
   g.a = a; g.sa = sa; g.b = b; g.sb = sb;
   g.out = out; g.out_f32 = out_dtype != FP8BLK_OUT_BF16; g.accumulate = out_dtype == FP8BLK_OUT_FP32_ACCUM;
@@ -152,16 +148,55 @@ int fp8_block_gemm(int op, int64_t M, int64_t N, int64_t K, const uint8_t* a, co
     g.I = N; g.J = K; g.R = M;
     g.sb_j = 0; g.sb_r = 0; g.bmode = fp8blk::BScale::Row;
   }
+  g.splits = fp8blk::gemm_splits(g.I, g.J, g.R, g.bmode);
+  return g;
+}
+
+int fp8_block_gemm(int op, int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa, const uint8_t* b,
+                   const float* sb, void* out, int out_dtype, int algo, void* workspace, size_t ws_bytes,
+                   hipStream_t stream) {
+  if (op != FP8BLK_OP_FPROP && op != FP8BLK_OP_DGRAD && op != FP8BLK_OP_WGRAD) return FP8BLK_ERR_ARG;
+  if (algo != FP8BLK_ALGO_DEFAULT && algo != FP8BLK_ALGO_PROMOTE && algo != FP8BLK_ALGO_SCALED_MFMA)
+    return FP8BLK_ERR_ARG;
+  if (int rc = check_gemm_common(M, N, K, a, sa, b, sb, out, out_dtype)) return rc;
+  fp8blk::GemmArgs g = make_args(op, M, N, K, a, sa, b, sb, out, out_dtype);
   const size_t need = fp8blk::gemm_workspace_bytes(g.I, g.J, g.R, g.bmode);
   if (need > 0 && (workspace == nullptr || ws_bytes < need)) return FP8BLK_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return FP8BLK_ERR_ALIGN;
   if (int rc = check_device()) return rc;
   g.ws = static_cast<float*>(workspace);
-  g.splits = fp8blk::gemm_splits(g.I, g.J, g.R, g.bmode);
   const fp8blk::GemmAlgo al = algo == FP8BLK_ALGO_PROMOTE      ? fp8blk::GemmAlgo::Promote
                               : algo == FP8BLK_ALGO_SCALED_MFMA ? fp8blk::GemmAlgo::ScaledMfma
                                                                 : kDefaultAlgo;
   return finish(fp8blk::launch_gemm(g, al, stream));
+}
+
+// Workspace of fp8_block_gemm_backward: its own launch, or the Wgrad of the
+// two-call fallback.
+static size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const size_t fused = fp8blk::gemm_mx_bwd_workspace_bytes(M, N, K);
+  const size_t wgrad = fp8blk::gemm_workspace_bytes(N, K, M, fp8blk::BScale::Row);
+  return fused > wgrad ? fused : wgrad;
+}
+
+int fp8_block_gemm_backward(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy,
+                            const uint8_t* qwT, const float* sw, const uint8_t* qdyT, const float* sdyT,
+                            const uint8_t* qxT, const float* sxT, void* dx, int dx_dtype, void* dw, int dw_dtype,
+                            void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (int rc = check_gemm_common(M, N, K, qdy, sdy, qwT, sw, dx, dx_dtype)) return rc;
+  if (int rc = check_gemm_common(M, N, K, qdyT, sdyT, qxT, sxT, dw, dw_dtype)) return rc;
+  if (dx == dw) return FP8BLK_ERR_ARG;
+  const size_t need = backward_workspace_bytes(M, N, K);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need)) return FP8BLK_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return FP8BLK_ERR_ALIGN;
+  if (int rc = check_device()) return rc;
+  fp8blk::GemmArgs gd = make_args(FP8BLK_OP_DGRAD, M, N, K, qdy, sdy, qwT, sw, dx, dx_dtype);
+  fp8blk::GemmArgs gw = make_args(FP8BLK_OP_WGRAD, M, N, K, qdyT, sdyT, qxT, sxT, dw, dw_dtype);
+  gw.ws = static_cast<float*>(workspace);
+  if (fp8blk::gemm_mx_bwd_eligible(gd, gw)) return finish(fp8blk::launch_gemm_mx_bwd(gd, gw, stream));
+  // shapes the fused launch does not take: the two contractions in turn
+  if (hipError_t e = fp8blk::launch_gemm(gd, kDefaultAlgo, stream)) return finish(e);
+  return finish(fp8blk::launch_gemm(gw, kDefaultAlgo, stream));
 }
 
 int fp8_block_gemm_fprop(int64_t M, int64_t N, int64_t K, const uint8_t* qx, const float* sx, const uint8_t* qw,
@@ -189,6 +224,7 @@ size_t fp8_block_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
     case FP8BLK_OP_FPROP: return fp8blk::gemm_workspace_bytes(M, N, K, fp8blk::BScale::Block);
     case FP8BLK_OP_DGRAD: return fp8blk::gemm_workspace_bytes(M, K, N, fp8blk::BScale::Block);
     case FP8BLK_OP_WGRAD: return fp8blk::gemm_workspace_bytes(N, K, M, fp8blk::BScale::Row);
+    case FP8BLK_OP_BACKWARD: return backward_workspace_bytes(M, N, K);
     default: return (size_t)-1;
   }
 }

@@ -55,4 +55,11 @@ bool gemm_mx_eligible(const GemmArgs& g);
 size_t gemm_mx_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode);
 hipError_t launch_gemm_mx(const GemmArgs& g, hipStream_t stream);
 
+// Dgrad (gd: I = M, J = K, R = N, weight-block scales) and Wgrad (gw: I = N,
+// J = K, R = M, row scales) of one linear in one launch; the workspace is
+// gw.ws.
+bool gemm_mx_bwd_eligible(const GemmArgs& gd, const GemmArgs& gw);
+size_t gemm_mx_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_mx_bwd(const GemmArgs& gd, const GemmArgs& gw, hipStream_t stream);
+
 }  // namespace fp8blk

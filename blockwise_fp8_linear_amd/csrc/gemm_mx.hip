@@ -482,13 +482,13 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
 // into p equal ranges (Gs divides W, the range length divides U), workgroup
 // w takes range (w mod T') p + w div T' of the T' stream-K tiles instead:
 // the workgroups of one XCD (consecutive w) then cover different tiles at
-// the same depth, sharing operand panels in L2, as a split-K launch would.  A stream-K range is a run of segments: whole tiles are stored
-// directly; a piece of a tile shared by several workgroups is stored, in
-// fp32, to a tile-sized slot of the workspace -- slot 2w for the first
-// segment of range r, 2r + 1 for its last one (the only segments that can
-// be partial) -- and a second kernel adds the pieces of every shared
-// tile in reduction order (deterministic) and stores it.  No workgroup ever
-// waits for another.
+// the same depth, sharing operand panels in L2, as a split-K launch would.
+// A stream-K range is a run of segments: whole tiles are stored directly; a
+// piece of a tile shared by several workgroups is stored, in fp32, to a
+// tile-sized slot of the workspace -- slot 2r for the first segment of
+// range r, 2r + 1 for its last one (the only segments that can be partial)
+// -- and a second kernel adds the pieces of every shared tile in reduction
+// order (deterministic) and stores it.  No workgroup ever waits for another.
 struct SkGeom {
   int64_t tiles_m, tiles_n;
   int64_t dp_tiles;  // tiles [0, dp_tiles) are data-parallel
@@ -591,6 +591,120 @@ __global__ __launch_bounds__(256) void sk_fixup_kernel(GemmArgs g, SkGeom sg, co
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dgrad and Wgrad of one linear in one persistent stream-K launch.  Problem
+// 0 is Dgrad (weight-block scales), problem 1 Wgrad (row scales); the two
+// have the same FLOP count.  The reductions of all their tiles are cut into
+// units of four 128-blocks, problem 0's tiles first, and range r of G takes
+// units [r W / G, (r + 1) W / G) of all W of them, so every workgroup does
+// the same work and the CUs stay busy across both GEMMs.  Segments, slots
+// and the fix-up of shared tiles work as in the Wgrad kernel above.
+struct BwdGeom {
+  int64_t tm0, tn0, u0, t0;  // problem 0: tile grid, units per tile, tiles
+  int64_t tm1, tn1, u1;      // problem 1
+  int64_t w0;                // units of problem 0
+  int64_t units;             // W, all units
+};
+
+__global__ __launch_bounds__(THREADS) void gemm_mx_bwd_kernel(GemmArgs gd, GemmArgs gw, BwdGeom bg,
+                                                              float* partials) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int64_t G = gridDim.x, W = bg.units;
+  const int64_t r = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t ubeg = sk_start(r, W, G), uend = sk_start(r + 1, W, G);
+  v16f acc[TM][TN];
+  for (int64_t u = ubeg; u < uend;) {
+    const bool p1 = u >= bg.w0;
+    const int64_t base = p1 ? bg.w0 : 0, U = p1 ? bg.u1 : bg.u0;
+    const int64_t ts = (u - base) / U;                     // tile of the problem
+    const int64_t lo = u - base - ts * U;                   // first unit of the segment, within the tile
+    const int64_t tend = base + (ts + 1) * U;
+    const int64_t hi = (uend < tend ? uend : tend) - base - ts * U;  // one past its last
+    int64_t i0, j0;
+    tile_origin(ts, p1 ? bg.tm1 : bg.tm0, p1 ? bg.tn1 : bg.tn0, i0, j0);
+    lds_barrier();  // the previous segment's epilogue is done with LDS
+    if (p1)
+      mma_segment<true>(gw, lds, i0, j0, lo * 4, (hi - lo) * 4, acc);
+    else
+      mma_segment<false>(gd, lds, i0, j0, lo * 4, (hi - lo) * 4, acc);
+    if (lo == 0 && hi == U) {
+      const Dst d{p1 ? gw.out : gd.out, p1 ? gw.J : gd.J, p1 ? gw.I : gd.I, p1 ? gw.J : gd.J,
+                  p1 ? gw.out_f32 : gd.out_f32, p1 ? gw.accumulate : gd.accumulate};
+      store_tile(d, lds, i0, j0, acc);
+    } else {
+      float* const slot = partials + (2 * r + (u == ubeg ? 0 : 1)) * (int64_t)(BM * BN);
+      store_tile(Dst{slot, BN, BM, BN, true, false}, lds, 0, 0, acc);
+    }
+    u = base + ts * U + hi;
+  }
+}
+
+// The shared tiles of a backward launch: block (t, r) sums rows
+// 16r..16r+15 of tile t (problem 0's tiles, then problem 1's) over its
+// pieces in reduction order and stores them; slots as in sk_fixup_kernel.
+__global__ __launch_bounds__(256) void bwd_fixup_kernel(GemmArgs gd, GemmArgs gw, BwdGeom bg, int64_t G,
+                                                        const float* __restrict__ partials) {
+  const int64_t t = blockIdx.x / (BM / FIX_ROWS);
+  const int64_t r0 = (blockIdx.x % (BM / FIX_ROWS)) * FIX_ROWS;
+  const bool p1 = t >= bg.t0;
+  const int64_t ts = p1 ? t - bg.t0 : t, U = p1 ? bg.u1 : bg.u0;
+  const int64_t first = (p1 ? bg.w0 : 0) + ts * U, W = bg.units;
+  const int64_t f = sk_owner(first, W, G);
+  const int pieces = (int)(sk_owner(first + U - 1, W, G) - f + 1);
+  if (pieces == 1) return;  // stored by the GEMM itself
+  const int64_t first_slot = 2 * f + (sk_start(f, W, G) < first ? 1 : 0);
+  int64_t i0, j0;
+  tile_origin(ts, p1 ? bg.tm1 : bg.tm0, p1 ? bg.tn1 : bg.tn0, i0, j0);
+  const int64_t I = p1 ? gw.I : gd.I, J = p1 ? gw.J : gd.J;
+  void* const out = p1 ? gw.out : gd.out;
+  const bool out_f32 = p1 ? gw.out_f32 : gd.out_f32, accumulate = p1 ? gw.accumulate : gd.accumulate;
+  constexpr int PER = FIX_ROWS * BN / 4 / 256;  // float4 per thread
+  v4f sum[PER];
+  for (int pc = 0; pc < pieces; ++pc) {
+    const int64_t slot = pc == 0 ? first_slot : 2 * (f + pc);
+    const v4f* src = reinterpret_cast<const v4f*>(partials + slot * (int64_t)(BM * BN) + r0 * BN);
+    v4f v[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) v[k] = __builtin_nontemporal_load(src + threadIdx.x + 256 * k);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      if (pc == 0) sum[k] = v[k];
+      else sum[k] = v4f{sum[k][0] + v[k][0], sum[k][1] + v[k][1], sum[k][2] + v[k][2], sum[k][3] + v[k][3]};
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    const int64_t i = i0 + r0 + idx / (BN / 4), j = j0 + (idx % (BN / 4)) * 4;
+    if (i >= I || j >= J) continue;
+    if (out_f32) {
+      v4f* const dst = reinterpret_cast<v4f*>(static_cast<float*>(out) + i * J + j);
+      if (accumulate) {
+        const v4f o = *dst;
+        *dst = v4f{o[0] + sum[k][0], o[1] + sum[k][1], o[2] + sum[k][2], o[3] + sum[k][3]};
+      } else {
+        *dst = sum[k];
+      }
+    } else {
+      uint2 o;
+      o.x = bf16x2_rne(sum[k][0], sum[k][1]);
+      o.y = bf16x2_rne(sum[k][2], sum[k][3]);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + i * J + j) = o;
+    }
+  }
+}
+
+struct BwdPlan {
+  BwdGeom geom;
+  int64_t grid;
+  bool partial;  // some tile is shared by several workgroups (workspace needed)
+  size_t bytes;
+};
+
+// Host mirrors of the range arithmetic above.
+inline int64_t h_start(int64_t w, int64_t W, int64_t G) { return w * W / G; }
+inline int64_t h_owner(int64_t u, int64_t W, int64_t G) { return ((u + 1) * G - 1) / W; }
+
 // Persistent grid: one workgroup per CU of an MI355X (fewer for tiny shapes).
 constexpr int64_t kSkGrid = 256;
 
@@ -616,6 +730,31 @@ SkPlan sk_plan(int64_t I, int64_t J, int64_t R) {
   // unit, or when Gs divides W and U divides W / Gs (whole tiles per workgroup)
   p.partial = !(W == 0 || U == 1 || (W % Gs == 0 && (W / Gs) % U == 0));
   p.geom.sk_tiles = (W > 0 && W % Gs == 0 && U % (W / Gs) == 0) ? T - p.geom.dp_tiles : 0;
+  p.bytes = p.partial ? (size_t)(2 * p.grid) * BM * BN * sizeof(float) : 0;
+  return p;
+}
+
+// Dgrad (I = M, J = K, R = N) and Wgrad (I = N, J = K, R = M) of one linear.
+BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K) {
+  BwdPlan p{};
+  BwdGeom& b = p.geom;
+  b.tm0 = (M + BM - 1) / BM;
+  b.tn0 = (K + BN - 1) / BN;
+  b.u0 = N / 512;
+  b.t0 = b.tm0 * b.tn0;
+  b.tm1 = (N + BM - 1) / BM;
+  b.tn1 = (K + BN - 1) / BN;
+  b.u1 = M / 512;
+  b.w0 = b.t0 * b.u0;
+  b.units = b.w0 + b.tm1 * b.tn1 * b.u1;
+  p.grid = b.units < kSkGrid ? b.units : kSkGrid;
+  // a tile is shared when its first and last units fall in different ranges
+  const int64_t T = b.t0 + b.tm1 * b.tn1;
+  for (int64_t t = 0; t < T && !p.partial; ++t) {
+    const bool p1 = t >= b.t0;
+    const int64_t U = p1 ? b.u1 : b.u0, first = (p1 ? b.w0 + (t - b.t0) * U : t * U);
+    p.partial = h_owner(first, b.units, p.grid) != h_owner(first + U - 1, b.units, p.grid);
+  }
   p.bytes = p.partial ? (size_t)(2 * p.grid) * BM * BN * sizeof(float) : 0;
   return p;
 }
@@ -656,6 +795,21 @@ hipError_t launch_mx_streamk(const GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_bwd(const GemmArgs& gd, const GemmArgs& gw, float* ws, hipStream_t stream) {
+  const BwdPlan p = bwd_plan(gd.I, gd.R, gd.J);
+  static bool attr_set = false;
+  if (hipError_t e = set_lds_attr(&gemm_mx_bwd_kernel, attr_set)) return e;
+  float* const partials = p.partial ? ws : nullptr;
+  hipLaunchKernelGGL(gemm_mx_bwd_kernel, dim3((uint32_t)p.grid), dim3(THREADS), LDS_BYTES, stream, gd, gw, p.geom,
+                     partials);
+  if (hipError_t e = hipGetLastError()) return e;
+  if (!p.partial) return hipSuccess;
+  const int64_t T = p.geom.t0 + p.geom.tm1 * p.geom.tn1;
+  hipLaunchKernelGGL(bwd_fixup_kernel, dim3((uint32_t)(T * (BM / FIX_ROWS))), dim3(256), 0, stream, gd, gw, p.geom,
+                     p.grid, partials);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool gemm_mx_eligible(const GemmArgs& g) {
@@ -678,6 +832,20 @@ size_t gemm_mx_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode) {
 hipError_t launch_gemm_mx(const GemmArgs& g, hipStream_t stream) {
   if (g.bmode == BScale::Row) return launch_mx_streamk<true>(g, stream);
   return launch_mx<false>(g, stream);
+}
+
+bool gemm_mx_bwd_eligible(const GemmArgs& gd, const GemmArgs& gw) {
+  return gd.bmode == BScale::Block && gw.bmode == BScale::Row && gemm_mx_eligible(gd) && gemm_mx_eligible(gw) &&
+         gd.I == gw.R && gd.R == gw.I && gd.J == gw.J;
+}
+
+size_t gemm_mx_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if ((N / 128) % 4 != 0 || (M / 128) % 4 != 0) return 0;
+  return bwd_plan(M, N, K).bytes;
+}
+
+hipError_t launch_gemm_mx_bwd(const GemmArgs& gd, const GemmArgs& gw, hipStream_t stream) {
+  return launch_bwd(gd, gw, gw.ws, stream);
 }
 
 }  // namespace fp8blk

@@ -69,8 +69,10 @@ enum fp8blk_scale_mode { FP8BLK_SCALE_POW2 = 0 };
  * bit, so the sum is deterministic too. */
 enum fp8blk_out_dtype { FP8BLK_OUT_BF16 = 0, FP8BLK_OUT_FP32 = 1, FP8BLK_OUT_FP32_ACCUM = 2 };
 
-/* Which contraction (for fp8_block_gemm and the workspace query). */
-enum fp8blk_op { FP8BLK_OP_FPROP = 0, FP8BLK_OP_DGRAD = 1, FP8BLK_OP_WGRAD = 2 };
+/* Which contraction (for fp8_block_gemm and the workspace query;
+ * FP8BLK_OP_BACKWARD, Dgrad and Wgrad together, for the workspace query and
+ * fp8_block_gemm_backward only). */
+enum fp8blk_op { FP8BLK_OP_FPROP = 0, FP8BLK_OP_DGRAD = 1, FP8BLK_OP_WGRAD = 2, FP8BLK_OP_BACKWARD = 3 };
 
 /* How the per-block scale product reaches the fp32 accumulators.
  *   PROMOTE:     one MFMA per 128-deep reduction block starting from zero,
@@ -197,6 +199,30 @@ int fp8_block_gemm_wgrad(int64_t M, int64_t N, int64_t K,
                          const uint8_t *qxT, const float *sxT,
                          void *dw, int out_dtype,
                          void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Dgrad and Wgrad of one linear in one call (section 3.2, fourth paragraph:
+ * both backward GEMMs of the layer).  Operands and outputs are exactly those
+ * of fp8_block_gemm_dgrad and fp8_block_gemm_wgrad, each output with its own
+ * out_dtype (FP8BLK_OUT_FP32_ACCUM allowed for both).  The two contractions
+ * have the same FLOP count and run as one launch whose workgroups share out
+ * the reduction work of both evenly; results equal those of the separate
+ * calls up to the order in which fp32 partial sums are added
+ * (deterministic).  Shapes the fused launch does not take (the 128-block
+ * count of M or N not a multiple of 4, N > 16384) run as the two separate
+ * contractions.
+ *   workspace: at least fp8_block_gemm_workspace_size(FP8BLK_OP_BACKWARD,
+ *     M, N, K) bytes, 16-byte aligned, contents on entry irrelevant; NULL
+ *     when that size is 0.
+ *   dx and dw must not be the same buffer (FP8BLK_ERR_ARG).
+ */
+int fp8_block_gemm_backward(int64_t M, int64_t N, int64_t K,
+                            const uint8_t *qdy, const float *sdy,
+                            const uint8_t *qwT, const float *sw,
+                            const uint8_t *qdyT, const float *sdyT,
+                            const uint8_t *qxT, const float *sxT,
+                            void *dx, int dx_dtype, void *dw, int dw_dtype,
+                            void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * All three contractions through one entry point, with an explicit algorithm.

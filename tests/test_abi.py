@@ -24,7 +24,7 @@ def test_exports_every_declared_function(lib):
     names = fb.header_functions()
     assert set(names) == {
         "fp8_quantize_rowgroup", "fp8_quantize_colgroup", "fp8_quantize_block", "fp8_quantize_dual",
-        "fp8_block_gemm_fprop", "fp8_block_gemm_dgrad", "fp8_block_gemm_wgrad",
+        "fp8_block_gemm_fprop", "fp8_block_gemm_dgrad", "fp8_block_gemm_wgrad", "fp8_block_gemm_backward",
         "fp8_block_gemm", "fp8_block_gemm_workspace_size", "fp8_status_string",
     }
     for n in names:
@@ -116,6 +116,32 @@ def test_gemm_errors(lib):
     assert w(8192, 256, 256, P, P3, P2, P3, P, 0, None, 0, None) == EWS
     assert w(8192, 256, 256, P, P3, P2, P3, P, 0, P, need - 1, None) == EWS
     assert w(8192, 256, 256, P, P3, P2, P3, P, 0, MIS, need, None) == EALIGN
+
+
+def test_backward_errors(lib):
+    f = lib.fp8_block_gemm_backward
+    P4, P5, P6, P7 = 0x400000, 0x500000, 0x600000, 0x700000
+    need = lib.fp8_block_gemm_workspace_size(3, 8192, 2048, 2048)
+    assert need > 0 and need != ctypes.c_size_t(-1).value
+    names = ("M", "N", "K", "qdy", "sdy", "qwT", "sw", "qdyT", "sdyT", "qxT", "sxT", "dx", "dxt", "dw", "dwt",
+             "ws", "wsb", "stream")
+    ok = (8192, 2048, 2048, P, P3, P2, P3, P4, P5, P6, P7, 0x800000, 0, 0x900000, 1, 0xA00000, need, None)
+
+    def call(**kw):
+        a = dict(zip(names, ok))
+        a.update(kw)
+        return f(*[a[n] for n in names])
+    assert call() in (EHIP, EDEV)                                  # valid arguments, no GPU here
+    assert call(dxt=2) in (EHIP, EDEV)                             # fp32 accumulate allowed
+    assert call(dwt=7) == EARG
+    assert call(dx=0x900000) == EARG                               # dx and dw alias
+    for n in ("qdy", "sdy", "qwT", "sw", "qdyT", "sdyT", "qxT", "sxT", "dx", "dw"):
+        assert call(**{n: None}) == ENULL, n
+    assert call(N=200) == EDIM
+    assert call(ws=None) == EWS
+    assert call(wsb=need - 1) == EWS
+    assert call(ws=MIS) == EALIGN
+    assert call(qxT=MIS) == EALIGN
 
 
 def test_workspace_query(lib):

@@ -305,3 +305,53 @@ def test_fp32_accumulate(shape):
             want = host_f32(old) + host_f32(r)          # float32 + float32 in numpy: one rounding
             got = host_f32(acc)
             assert np.array_equal(got, want), f"{op} {algo_name} {shape}: accumulation differs"
+
+
+def check_backward(layer, rows_dx, rows_dw, what):
+    """fp8_block_gemm_backward (Dgrad and Wgrad in one call) against the
+    oracle, fp32 and bf16 outputs, on the given output rows."""
+    import torch
+    g = layer.g
+    args = (g["qdy"], g["sdy"], g["qwT"], g["sw"], g["qdyT"], g["sdyT"], g["qxT"], g["sxT"])
+    dxf, dwf = fb.fp8_block_gemm_backward(*args, dx_dtype=torch.float32, dw_dtype=torch.float32)
+    dxb, dwb = fb.fp8_block_gemm_backward(*args)
+    torch.cuda.synchronize()
+    for op, rows, yf, yb in (("dgrad", rows_dx, dxf, dxb), ("wgrad", rows_dw, dwf, dwb)):
+        y32, _, bound = layer.ref(op, rows)
+        tag = f"{what} backward/{op} M={layer.M} N={layer.N} K={layer.K}"
+        st = check_f32(host_f32(yf)[rows], y32, bound, tag)
+        check_bf16(host(yb)[rows], host_f32(yf)[rows], y32, bound, tag)
+        note(f"{tag}: err/bound {st['err/bound']:.2e} normwise {st['normwise']:.2e}")
+    return dxf, dwf
+
+
+# (M, N, K): fused launches (M and N multiples of 512) with one, several or
+# shared tiles and a ragged K edge; (384, 640, 512) takes the two-call path.
+@pytest.mark.parametrize("shape", [(1024, 512, 384), (512, 1024, 640), (2048, 1536, 1152), (384, 640, 512)])
+def test_backward_small(shape):
+    import torch
+    M, N, K = shape
+    key = (69, M, N, K)
+    layer = Layer(varied((M, K), 1.0, key + (0,)), varied((N, K), 0.02, key + (1,)),
+                  varied((M, N), 1e-3, key + (2,)))
+    dxf, dwf = check_backward(layer, np.arange(M), np.arange(N), "small")
+    # deterministic, and fp32 accumulation into dW
+    g = layer.g
+    args = (g["qdy"], g["sdy"], g["qwT"], g["sw"], g["qdyT"], g["sdyT"], g["qxT"], g["sxT"])
+    dx2, dw2 = fb.fp8_block_gemm_backward(*args, dx_dtype=torch.float32, dw_dtype=torch.float32)
+    old = torch.randn((N, K), device="cuda", dtype=torch.float32, generator=torch.Generator(device="cuda").manual_seed(69))
+    acc = old.clone()
+    fb.fp8_block_gemm_backward(*args, dx_dtype=torch.float32, dw_dtype=torch.float32, dw=acc, accumulate_dw=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dxf, dx2) and torch.equal(dwf, dw2), "backward is not deterministic"
+    assert np.array_equal(host_f32(acc), host_f32(old) + host_f32(dwf)), "dW accumulation differs"
+
+
+@pytest.mark.parametrize("li", range(4))
+def test_backward_decoder_layer_full_size(li):
+    """The fused backward of each decoder-layer linear at 8192 tokens (the
+    benchmark's launch), sampled output rows of dX and dW."""
+    lin = synth.decoder_layer(linears=(synth.LAYER_LINEARS[li],))[0]
+    layer = Layer(lin["x"], lin["w"], lin["dy"])
+    check_backward(layer, _sample_rows(layer.M, (71, li, 0), k=8), _sample_rows(layer.N, (71, li, 1), k=8),
+                   f"layer {lin['name']}")
