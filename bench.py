@@ -88,6 +88,8 @@ def parse():
                          "instead of the one-pass kernel")
     ap.add_argument("--separate-bwd", action="store_true",
                     help="run Dgrad and Wgrad as two calls instead of fp8_block_gemm_backward")
+    ap.add_argument("--separate-wquant", action="store_true",
+                    help="quantize each weight in its own launch instead of one batched launch per layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
@@ -178,6 +180,8 @@ DUAL = True
 # True: Dgrad and Wgrad of a linear in one call (fp8_block_gemm_backward);
 # False: the two separate calls.
 FUSED_BWD = True
+# True: a layer's four weights quantized in one launch; False: one launch each.
+BATCH_W = True
 
 
 def quantize_both(fb, T, x, q, s, qT, sT):
@@ -189,12 +193,24 @@ def quantize_both(fb, T, x, q, s, qT, sT):
         T.run("quant_colgroup", 0, qbytes(rows, cols), lambda: fb.fp8_quantize_colgroup(x, qT=qT, sT=sT))
 
 
+def quantize_weights(fb, T, L):
+    """All the weights of a layer (with their transposed copies), known when
+    the step starts: one batched launch, or one launch per weight."""
+    if BATCH_W:
+        nbytes = sum(d["N"] * d["K"] * 4 + (d["N"] // 128) * (d["K"] // 128) * 4 for d in L)
+        T.run("quant_block_batch", 0, nbytes,
+              lambda: fb.fp8_quantize_block_batch([d["w"] for d in L], outs=[(d["qw"], d["qwT"], d["sw"]) for d in L]))
+    else:
+        for d in L:
+            n, k = d["N"], d["K"]
+            T.run("quant_block", 0, n * k * 4 + (n // 128) * (k // 128) * 4,
+                  lambda d=d: fb.fp8_quantize_block(d["w"], q=d["qw"], qT=d["qwT"], s=d["sw"]))
+
+
 def fwd_linear(fb, T, d, algo, x=None):
     n, k = d["N"], d["K"]
     x = d["x"] if x is None else x
     quantize_both(fb, T, x, d["qx"], d["sx"], d["qxT"], d["sxT"])
-    T.run("quant_block", 0, n * k * 4 + (n // 128) * (k // 128) * 4,
-          lambda: fb.fp8_quantize_block(d["w"], q=d["qw"], qT=d["qwT"], s=d["sw"]))
     T.run("gemm_fprop", 2.0 * TOKENS * n * k, 0,
           lambda: fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, d["qx"], d["sx"], d["qw"], d["sw"], TOKENS, n, k,
                                     algo=algo, out=d["y"]))
@@ -218,6 +234,7 @@ def bwd_linear(fb, T, d, algo):
 
 
 def layer_step(fb, T, L, algo):
+    quantize_weights(fb, T, L)
     for d in L:
         fwd_linear(fb, T, d, algo)
     for d in reversed(L):
@@ -241,6 +258,7 @@ def stack_step(fb, T, layers, algo):
     column-group copy of its input kept from the forward pass."""
     x = layers[0][0]["x"]
     for L in layers:
+        quantize_weights(fb, T, L)
         qkv, o, gu, dn = L
         y = fwd_linear(fb, T, qkv, algo, x)
         y = fwd_linear(fb, T, o, algo, y[:, :2048])
@@ -354,9 +372,10 @@ def main():
 
     fb.load_library()
     torch.cuda.set_device(0)
-    global DUAL, FUSED_BWD
+    global DUAL, FUSED_BWD, BATCH_W
     DUAL = not args.separate_quant
     FUSED_BWD = not args.separate_bwd
+    BATCH_W = not args.separate_wquant
     algo = {"default": fb.FP8BLK_ALGO_DEFAULT, "promote": fb.FP8BLK_ALGO_PROMOTE,
             "scaled": fb.FP8BLK_ALGO_SCALED_MFMA}[args.algo]
 
@@ -446,6 +465,7 @@ def main():
         "config": {"workload": desc, "name": args.workload, "tokens": TOKENS, "algo": args.algo,
                    "quantizer": "separate" if args.separate_quant else "one-pass",
                    "backward": "separate" if args.separate_bwd else "fused",
+                   "weight_quant": "per weight" if args.separate_wquant else "batched per layer",
                    "gemm_tflop_per_step": round(step_flops / 1e12, 4)},
         "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
         "gemm_only_TFLOP/s": round(gemm_flops_t / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,

@@ -35,6 +35,12 @@ FP8BLK_ALGO_SCALED_MFMA = 2
 _lib = None
 
 
+class _BlockJob(ctypes.Structure):
+    # struct fp8blk_block_job of include/fp8blk.h
+    _fields_ = [("w", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("ld_w", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("qT", ctypes.c_void_p), ("s", ctypes.c_void_p)]
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load libfp8blk.so (once).  Raises if it has not been built."""
     global _lib
@@ -60,6 +66,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = ctypes.c_int
+    lib.fp8_quantize_block_batch.argtypes = [ctypes.POINTER(_BlockJob), i32, i32, vp]
+    lib.fp8_quantize_block_batch.restype = ctypes.c_int
     lib.fp8_block_gemm_workspace_size.argtypes = [i32, i64, i64, i64]
     lib.fp8_block_gemm_workspace_size.restype = ctypes.c_size_t
     lib.fp8_status_string.argtypes = [i32]
@@ -155,6 +163,34 @@ def fp8_quantize_dual(x, q=None, s=None, qT=None, sT=None, stream=None):
                                             s.data_ptr(), qT.data_ptr(), qT.stride(0), sT.data_ptr(),
                                             FP8BLK_SCALE_POW2, _stream(stream)))
     return q, s, qT, sT
+
+
+def fp8_quantize_block_batch(weights, transpose=True, outs=None, stream=None):
+    """Several weights (bf16 [rows, cols] tensors, at most 8) quantized in one
+    launch, each as by fp8_quantize_block.  Returns a list of (q, qT or None,
+    s); `outs`, if given, is such a list of preallocated outputs."""
+    import torch
+    n = len(weights)
+    jobs = (_BlockJob * n)()
+    res = []
+    for k, w in enumerate(weights):
+        _dev(w, torch.bfloat16, f"weights[{k}]")
+        rows, cols = w.shape
+        if outs is not None:
+            q, qT, s = outs[k]
+            _dense(q, torch.uint8, "q")
+            _dense(s, torch.float32, "s")
+            if qT is not None:
+                _dense(qT, torch.uint8, "qT")
+        else:
+            q = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
+            qT = torch.empty((cols, rows), dtype=torch.uint8, device=w.device) if transpose else None
+            s = torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=w.device)
+        jobs[k] = _BlockJob(w.data_ptr(), rows, cols, w.stride(0), q.data_ptr(),
+                            qT.data_ptr() if qT is not None else None, s.data_ptr())
+        res.append((q, qT, s))
+    _check(load_library().fp8_quantize_block_batch(jobs, n, FP8BLK_SCALE_POW2, _stream(stream)))
+    return res
 
 
 def fp8_quantize_block(w, transpose=True, q=None, qT=None, s=None, stream=None):

@@ -99,8 +99,8 @@ int fp8_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_
   return finish(fp8blk::launch_quant_dual(x, rows, cols, ld_x, q, ld_q, s, qT, ld_qT, sT, stream));
 }
 
-int fp8_quantize_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld_w, uint8_t* q, uint8_t* qT,
-                       float* s, int scale_mode, hipStream_t stream) {
+static int check_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld_w, const uint8_t* q,
+                       const uint8_t* qT, const float* s, int scale_mode) {
   if (scale_mode != FP8BLK_SCALE_POW2) return FP8BLK_ERR_ARG;
   if (!w || !q || !s) return FP8BLK_ERR_NULL;
   if (!mult128(rows) || !mult128(cols)) return FP8BLK_ERR_DIM;
@@ -108,8 +108,30 @@ int fp8_quantize_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld
   if ((rows / 128) * (cols / 128) >= (int64_t(1) << 31) || rows * ld_w > kMaxElems || rows * cols > kMaxElems)
     return FP8BLK_ERR_ARG;
   if (!aligned16(w) || !aligned16(q) || (qT && !aligned16(qT)) || !aligned4(s) || ld_w % 8) return FP8BLK_ERR_ALIGN;
+  return FP8BLK_OK;
+}
+
+int fp8_quantize_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld_w, uint8_t* q, uint8_t* qT,
+                       float* s, int scale_mode, hipStream_t stream) {
+  if (int rc = check_block(w, rows, cols, ld_w, q, qT, s, scale_mode)) return rc;
   if (int rc = check_device()) return rc;
   return finish(fp8blk::launch_quant_block(w, rows, cols, ld_w, q, qT, s, stream));
+}
+
+int fp8_quantize_block_batch(const fp8blk_block_job* jobs, int n_jobs, int scale_mode, hipStream_t stream) {
+  if (!jobs) return FP8BLK_ERR_NULL;
+  if (n_jobs < 1 || n_jobs > fp8blk::kMaxBlockJobs) return FP8BLK_ERR_ARG;
+  fp8blk::BlockJob job[fp8blk::kMaxBlockJobs];
+  int64_t blocks = 0;
+  for (int k = 0; k < n_jobs; ++k) {
+    const fp8blk_block_job& j = jobs[k];
+    if (int rc = check_block(j.w, j.rows, j.cols, j.ld_w, j.q, j.qT, j.s, scale_mode)) return rc;
+    blocks += (j.rows / 128) * (j.cols / 128);
+    job[k] = fp8blk::BlockJob{j.w, j.rows, j.cols, j.ld_w, j.q, j.qT, j.s};
+  }
+  if (blocks >= (int64_t(1) << 31)) return FP8BLK_ERR_ARG;
+  if (int rc = check_device()) return rc;
+  return finish(fp8blk::launch_quant_block_batch(job, n_jobs, stream));
 }
 
 static int check_gemm_common(int64_t M, int64_t N, int64_t K, const void* a, const float* sa, const void* b,

@@ -14,6 +14,16 @@ hipError_t launch_quant_colgroup(const uint16_t* x, int64_t rows, int64_t cols, 
                                  int64_t ld_qT, float* sT, hipStream_t stream);
 hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
                              float* s, uint8_t* qT, int64_t ld_qT, float* sT, hipStream_t stream);
+// One weight of a batched block quantization.
+struct BlockJob {
+  const uint16_t* w;
+  int64_t rows, cols, ld_w;
+  uint8_t* q;
+  uint8_t* qT;  // may be null
+  float* s;
+};
+constexpr int kMaxBlockJobs = 8;
+hipError_t launch_quant_block_batch(const BlockJob* job, int n, hipStream_t stream);
 hipError_t launch_quant_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld_w, uint8_t* q, uint8_t* qT,
                               float* s, hipStream_t stream);
 

@@ -154,12 +154,13 @@ __global__ __launch_bounds__(kColThreads) void quant_colgroup_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kBlkThreads = 256;
 
-__global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
-    const uint16_t* __restrict__ w, int64_t ld_w, uint8_t* __restrict__ q, uint8_t* __restrict__ qT,
-    float* __restrict__ s, int64_t rows, int64_t cols, uint32_t row_blocks, uint32_t col_blocks) {
+// Block `logical` (row-major over the row_blocks x col_blocks blocks) of one
+// weight.
+__device__ __forceinline__ void quant_block_one(const uint16_t* __restrict__ w, int64_t ld_w, uint8_t* __restrict__ q,
+                                                uint8_t* __restrict__ qT, float* __restrict__ s, int64_t rows,
+                                                int64_t cols, uint32_t col_blocks, uint32_t logical) {
   __shared__ uint32_t red[kBlkThreads / 64];
   const uint32_t t = threadIdx.x;
-  const uint32_t logical = xcd_remap(blockIdx.x, row_blocks * col_blocks);
   const uint32_t bi = logical / col_blocks;
   const uint32_t bj = logical - bi * col_blocks;
   const uint32_t cg = t & 15;
@@ -207,6 +208,27 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
   if (t == 0) s[(int64_t)bi * col_blocks + bj] = pow2f(e);
 }
 
+__global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
+    const uint16_t* __restrict__ w, int64_t ld_w, uint8_t* __restrict__ q, uint8_t* __restrict__ qT,
+    float* __restrict__ s, int64_t rows, int64_t cols, uint32_t row_blocks, uint32_t col_blocks) {
+  quant_block_one(w, ld_w, q, qT, s, rows, cols, col_blocks, xcd_remap(blockIdx.x, row_blocks * col_blocks));
+}
+
+// Several weights in one launch: workgroup b quantizes block b - first[j] of
+// job j, the last job with first[j] <= b.
+struct BlockJobs {
+  BlockJob job[kMaxBlockJobs];
+  uint32_t first[kMaxBlockJobs];
+  int n;
+};
+
+__global__ __launch_bounds__(kBlkThreads) void quant_block_batch_kernel(BlockJobs jobs) {
+  int j = 0;
+  for (int k = 1; k < jobs.n; ++k)
+    if (blockIdx.x >= jobs.first[k]) j = k;
+  const BlockJob& b = jobs.job[j];
+  quant_block_one(b.w, b.ld_w, b.q, b.qT, b.s, b.rows, b.cols, (uint32_t)(b.cols / 128), blockIdx.x - jobs.first[j]);
+}
 
 // ---------------------------------------------------------------------------
 // Row groups and column groups of the same tensor in one pass.  The pages
@@ -236,9 +258,11 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     uint8_t* __restrict__ qT, int64_t ld_qT, float* __restrict__ sT, uint32_t row_tiles, uint32_t col_tiles) {
   __shared__ uint32_t red[kDualThreads / 64][16][4];
   const uint32_t t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const uint32_t logical = xcd_remap(blockIdx.x, row_tiles * col_tiles);
-  const uint32_t ct = logical / row_tiles;  // consecutive logical ids walk down the rows
-  const uint32_t rt = logical - ct * row_tiles;
+  // consecutive workgroups walk along the rows, so that the ones in flight
+  // together read whole rows of x (measured: a few per cent faster than
+  // walking down the columns, with or without the XCD remap)
+  const uint32_t rt = blockIdx.x / col_tiles;
+  const uint32_t ct = blockIdx.x - rt * col_tiles;
   const int64_t m0 = (int64_t)rt * 128, c0 = (int64_t)ct * 128;
   const uint32_t rb = t >> 4, cb = t & 15;
   const int64_t r0 = m0 + rb * 8;
@@ -336,6 +360,19 @@ hipError_t launch_quant_colgroup(const uint16_t* x, int64_t rows, int64_t cols, 
   const uint32_t ct = (uint32_t)(cols / kColTileCols);
   hipLaunchKernelGGL(quant_colgroup_kernel, dim3(rt * ct), dim3(kColThreads), 0, stream, x, ld_x, qT, ld_qT, sT, rt,
                      ct);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_block_batch(const BlockJob* job, int n, hipStream_t stream) {
+  BlockJobs jobs{};
+  uint32_t total = 0;
+  for (int k = 0; k < n; ++k) {
+    jobs.job[k] = job[k];
+    jobs.first[k] = total;
+    total += (uint32_t)((job[k].rows / 128) * (job[k].cols / 128));
+  }
+  jobs.n = n;
+  hipLaunchKernelGGL(quant_block_batch_kernel, dim3(total), dim3(kBlkThreads), 0, stream, jobs);
   return hipGetLastError();
 }
 

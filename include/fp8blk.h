@@ -155,6 +155,27 @@ int fp8_quantize_block(const uint16_t *w, int64_t rows, int64_t cols, int64_t ld
                        hipStream_t stream);
 
 /*
+ * Several weights quantized in one launch, each exactly as by
+ * fp8_quantize_block (the same arguments, the same results): for instance
+ * all the weights of a layer, which are known when a step starts.  Saves
+ * the fixed cost of a launch per weight, which dominates for small ones.
+ *   jobs    host array of n_jobs descriptors (1 <= n_jobs <= 8), read before
+ *           the call returns; each must pass fp8_quantize_block's checks,
+ *           and the first failing one decides the status (nothing is
+ *           launched then).
+ */
+typedef struct fp8blk_block_job {
+    const uint16_t *w;      /* [rows][cols] bf16, row stride ld_w */
+    int64_t rows, cols, ld_w;
+    uint8_t *q;             /* [rows][cols] codes, dense */
+    uint8_t *qT;            /* NULL, or [cols][rows] codes, dense */
+    float *s;               /* [rows/128][cols/128] scales */
+} fp8blk_block_job;
+
+int fp8_quantize_block_batch(const fp8blk_block_job *jobs, int n_jobs, int scale_mode,
+                             hipStream_t stream);
+
+/*
  * Fprop  Y = X W^T  (section 3.2, fourth paragraph).
  *   qx [M][K] codes + sx [M][K/128]   (from fp8_quantize_rowgroup of X)
  *   qw [N][K] codes + sw [N/128][K/128] (from fp8_quantize_block of W)

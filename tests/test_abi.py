@@ -24,6 +24,7 @@ def test_exports_every_declared_function(lib):
     names = fb.header_functions()
     assert set(names) == {
         "fp8_quantize_rowgroup", "fp8_quantize_colgroup", "fp8_quantize_block", "fp8_quantize_dual",
+        "fp8_quantize_block_batch",
         "fp8_block_gemm_fprop", "fp8_block_gemm_dgrad", "fp8_block_gemm_wgrad", "fp8_block_gemm_backward",
         "fp8_block_gemm", "fp8_block_gemm_workspace_size", "fp8_status_string",
     }
@@ -93,6 +94,23 @@ def test_dual_errors(lib):
     assert call(sT=P5 + 2) == EALIGN
     assert call(ld_x=388) == EALIGN                               # not a multiple of 8
     assert call(ld_qT=264) == EALIGN                              # not a multiple of 16
+
+
+def test_block_batch_errors(lib):
+    J = fb._BlockJob
+    good = [J(P, 256, 384, 384, P2, None, P3), J(P, 512, 128, 128, P2, P2 + 0x10000, P3)]
+    arr = lambda jobs: (J * len(jobs))(*jobs)
+    assert lib.fp8_quantize_block_batch(arr(good), 2, 0, None) in (EHIP, EDEV)   # valid, no GPU here
+    assert lib.fp8_quantize_block_batch(None, 1, 0, None) == ENULL
+    assert lib.fp8_quantize_block_batch(arr(good), 0, 0, None) == EARG
+    assert lib.fp8_quantize_block_batch(arr(good * 5), 9, 0, None) == EARG        # at most 8 jobs
+    assert lib.fp8_quantize_block_batch(arr(good), 2, 1, None) == EARG            # scale mode
+    bad = [good[0], J(P, 256, 300, 384, P2, None, P3)]
+    assert lib.fp8_quantize_block_batch(arr(bad), 2, 0, None) == EDIM             # second job's shape
+    bad = [good[0], J(P, 256, 384, 384, None, None, P3)]
+    assert lib.fp8_quantize_block_batch(arr(bad), 2, 0, None) == ENULL
+    bad = [J(MIS, 256, 384, 384, P2, None, P3)]
+    assert lib.fp8_quantize_block_batch(arr(bad), 1, 0, None) == EALIGN
 
 
 def test_gemm_errors(lib):

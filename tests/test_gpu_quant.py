@@ -258,6 +258,29 @@ def test_dual_outlier_stress():
     _assert_dual(x, "outlier X")
 
 
+def test_block_batch_equals_single():
+    """The batched block quantizer on the decoder layer's four weights (plus
+    an edge-case weight without the transposed copy): each result bit-equal
+    to the oracle."""
+    import torch
+    import blockwise_fp8_linear_amd as fb
+    ws = [lin["w"] for lin in synth.decoder_layer()]
+    e = synth.normal_bf16((384, 256), 0.02, 45, 0)
+    e[128:256, 128:256] = 0
+    e[:128, :128] = np.arange(128 * 128, dtype=np.uint16).reshape(128, 128) % 128
+    ws.append(e)
+    note(f"block batch {[w.shape for w in ws]}")
+    dev = [dev_bf16(w) for w in ws]
+    res = fb.fp8_quantize_block_batch(dev[:4]) + fb.fp8_quantize_block_batch(dev[4:], transpose=False)
+    torch.cuda.synchronize()
+    for k, (w, (q, qT, s)) in enumerate(zip(ws, res)):
+        q0, qT0, s0 = oracle.quantize_block(w, transpose=qT is not None)
+        assert np.array_equal(host(s), s0), f"job {k}: scales differ"
+        assert np.array_equal(host(q), q0), f"job {k}: codes differ"
+        if qT is not None:
+            assert np.array_equal(host(qT), qT0), f"job {k}: transposed codes differ"
+
+
 def test_quantizers_repeatable():
     import torch
     import blockwise_fp8_linear_amd as fb
