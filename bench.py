@@ -63,7 +63,9 @@ def sources_digest():
 
 def measured_traffic(kernel, workload, algo):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None when there is none or the kernels changed since."""
+    summary, or None when there is none or the kernels changed since.  A
+    label "a (+ b)" is a call that launches a and sometimes b: b's bytes are
+    counted in the proportion of its dispatches to a's."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.loads(f.read().split("BEGIN-JSON", 1)[1].split("END-JSON", 1)[0])
@@ -71,8 +73,12 @@ def measured_traffic(kernel, workload, algo):
         return None
     if rec.get("sources_digest") != sources_digest() or rec.get("workload") != workload or rec.get("algo") != algo:
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    names = [n.strip() for n in kernel.replace("(+", "+").replace(")", "").split("+")]
+    ks = rec.get("kernels", {})
+    if any(n not in ks for n in names):
+        return None
+    main = ks[names[0]]
+    return round(sum(ks[n]["hbm_bytes_per_launch"] * ks[n]["dispatches"] / main["dispatches"] for n in names))
 
 
 def parse():
