@@ -604,6 +604,12 @@ struct BwdGeom {
   int64_t tm1, tn1, u1;      // problem 1
   int64_t w0;                // units of problem 0
   int64_t units;             // W, all units
+  // k0, k1: when a problem's tiles fall whole into ranges, k of them per
+  // range (else 0); the ranges' tiles are then dealt out round-robin -- the
+  // j-th tile of the problem's i-th range is tile j R + i (R ranges) -- so
+  // that the ranges running side by side work on neighbouring tiles and
+  // share operand panels in L2.  Whole tiles never reach the fix-up.
+  int64_t k0, k1;
 };
 
 __global__ __launch_bounds__(THREADS) void gemm_mx_bwd_kernel(GemmArgs gd, GemmArgs gw, BwdGeom bg,
@@ -616,12 +622,15 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_bwd_kernel(GemmArgs gd, GemmA
   for (int64_t u = ubeg; u < uend;) {
     const bool p1 = u >= bg.w0;
     const int64_t base = p1 ? bg.w0 : 0, U = p1 ? bg.u1 : bg.u0;
-    const int64_t ts = (u - base) / U;                     // tile of the problem
+    const int64_t ts = (u - base) / U;                     // tile of the problem, in range order
     const int64_t lo = u - base - ts * U;                   // first unit of the segment, within the tile
     const int64_t tend = base + (ts + 1) * U;
     const int64_t hi = (uend < tend ? uend : tend) - base - ts * U;  // one past its last
+    const int64_t k = p1 ? bg.k1 : bg.k0;
+    const int64_t tiles = p1 ? bg.tm1 * bg.tn1 : bg.t0;
+    const int64_t tt = k > 0 ? (ts % k) * (tiles / k) + ts / k : ts;  // the tile itself
     int64_t i0, j0;
-    tile_origin(ts, p1 ? bg.tm1 : bg.tm0, p1 ? bg.tn1 : bg.tn0, i0, j0);
+    tile_origin(tt, p1 ? bg.tm1 : bg.tm0, p1 ? bg.tn1 : bg.tn0, i0, j0);
     lds_barrier();  // the previous segment's epilogue is done with LDS
     if (p1)
       mma_segment<true>(gw, lds, i0, j0, lo * 4, (hi - lo) * 4, acc);
@@ -748,6 +757,14 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K) {
   b.w0 = b.t0 * b.u0;
   b.units = b.w0 + b.tm1 * b.tn1 * b.u1;
   p.grid = b.units < kSkGrid ? b.units : kSkGrid;
+  // round-robin tiles for a problem whose ranges all hold whole tiles: every
+  // range of the grid holds the same number q of units (G divides W), the
+  // problem starts and ends on range boundaries, and U divides q
+  if (b.units % p.grid == 0) {
+    const int64_t q = b.units / p.grid;
+    if (b.w0 % q == 0 && q % b.u0 == 0) b.k0 = q / b.u0;
+    if ((b.units - b.w0) % q == 0 && q % b.u1 == 0) b.k1 = q / b.u1;
+  }
   // a tile is shared when its first and last units fall in different ranges
   const int64_t T = b.t0 + b.tm1 * b.tn1;
   for (int64_t t = 0; t < T && !p.partial; ++t) {
