@@ -107,13 +107,16 @@ def parse():
 
 
 class Timer:
-    """Events around each launch, on the stream the library launches on.
-    The events are created up front (creating one costs far more host time
-    than recording it); a disabled Timer only counts launches."""
+    """Events around launches, on the stream the library launches on.  The
+    events are created up front (creating one costs far more host time than
+    recording it).  Recording one costs GPU time too, so a Timer can be
+    limited to some kinds of launch (`only`); a disabled Timer only counts
+    launches."""
 
-    def __init__(self, torch, enabled, n_launches=0):
+    def __init__(self, torch, enabled, n_launches=0, only=None):
         self.torch = torch
         self.enabled = enabled
+        self.only = only
         self.count = 0
         self.recs = []
         self.pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -121,7 +124,7 @@ class Timer:
 
     def run(self, kind, flops, nbytes, fn):
         self.count += 1
-        if not self.enabled:
+        if not self.enabled or (self.only is not None and kind not in self.only):
             return fn()
         s, e = self.pool[len(self.recs)]
         s.record()
@@ -411,22 +414,19 @@ def main():
         step(null)
     torch.cuda.synchronize()
 
-    T = Timer(torch, True, per_step * args.steps)
+    # Breakdown pass (untimed): events around every launch, for the per-kind
+    # figures and to find the dominant kernel.
+    nb = 3
+    B = Timer(torch, True, per_step * nb)
+    for _ in range(nb):
+        step(B)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(T)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = wall / args.steps * 1e3
-    value = step_flops / (ms * 1e-3) / 1e12
-
-    agg = T.summary()
+    agg = B.summary()
     breakdown = {}
     for kind, a in agg.items():
         avg_ms = a["ms"] / a["launches"]
-        e = {"launches_per_step": a["launches"] // args.steps, "avg_ms": round(avg_ms, 5),
-             "ms_per_step": round(a["ms"] / args.steps, 4)}
+        e = {"launches_per_step": a["launches"] // nb, "avg_ms": round(avg_ms, 5),
+             "ms_per_step": round(a["ms"] / nb, 4)}
         if a["flops"]:
             e["TFLOP/s"] = round(a["flops"] / (a["ms"] * 1e-3) / 1e12, 1)
         if a["bytes"]:
@@ -441,7 +441,24 @@ def main():
         for f in b:
             b[f] += a[f]
     dom = max(by_kernel, key=lambda k: by_kernel[k]["ms"])
-    a = by_kernel[dom]
+    dom_kinds = {k for k in agg if kernel_of(k, args.algo) == dom}
+
+    # Timed steps: events only around the dominant kernel's launches (the
+    # roofline's durations are measured here, live).
+    T = Timer(torch, True, per_step * args.steps, only=dom_kinds)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(T)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall / args.steps * 1e3
+    value = step_flops / (ms * 1e-3) / 1e12
+
+    a = {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0}
+    for kind, x in T.summary().items():
+        for f in a:
+            a[f] += x[f]
     avg_s = a["ms"] / a["launches"] * 1e-3
     traffic = measured_traffic(dom, args.workload, args.algo)
     if a["flops"]:
@@ -477,6 +494,8 @@ def main():
         "gemm_only_TFLOP/s": round(gemm_flops_t / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
         "roofline": roof,
         "breakdown": breakdown,
+        "breakdown_note": "per-kind event times from 3 untimed steps with events around every launch "
+                          "(the timed steps carry events around the dominant kernel's launches only)",
         "sources_digest": sources_digest(),
     }
     if linears is not None and not args.no_bf16_baseline:
