@@ -96,6 +96,8 @@ def parse():
                     help="run Dgrad and Wgrad as two calls instead of fp8_block_gemm_backward")
     ap.add_argument("--separate-wquant", action="store_true",
                     help="quantize each weight in its own launch instead of one batched launch per layer")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip measuring the on-box MFMA and copy ceilings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
@@ -308,6 +310,51 @@ def bf16_baseline(torch, linears, reps, steps=5):
     return dt, gemm_flops(linears) * reps / dt / 1e12
 
 
+def onbox_ceilings(torch):
+    """What this machine sustains, measured here: the GEMM kernels' MFMA work
+    alone (libfp8probe: the same block-scaled 32x32x64 FP8 instruction, one
+    wave per SIMD, 16 accumulators, random codes, no memory traffic) and a
+    plain 1 GiB device-to-device copy (read + write bytes)."""
+    import ctypes
+    from blockwise_fp8_linear_amd.build import PROBE_LIB
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.fp8probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fp8probe_mfma.restype = ctypes.c_int
+    lib.fp8probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.fp8probe_mfma_flops.restype = ctypes.c_double
+    wgs, iters = 256, 20000
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn, reps=5):
+        fn()
+        best = None
+        for _ in range(reps):
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            e.synchronize()
+            ms = s.elapsed_time(e)
+            best = ms if best is None else min(best, ms)
+        return best * 1e-3
+
+    def mfma():
+        if lib.fp8probe_mfma(wgs, iters, 12345, out.data_ptr(), stream) != 0:
+            raise RuntimeError("fp8probe_mfma failed")
+    t = timed(mfma)
+    mfma_tf = lib.fp8probe_mfma_flops(wgs, iters) / t / 1e12
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 256)
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src))
+    copy_gbs = 2 * n / t / 1e9
+    return {"mfma_fp8_TFLOP/s": round(mfma_tf, 1), "copy_GB/s": round(copy_gbs, 1),
+            "what": "best of 5: block-scaled FP8 MFMA loop (GEMM layout, random codes, no memory) "
+                    "and a 1 GiB device copy (read + write bytes)"}
+
+
 def cpu_baseline(budget_s):
     """The CPU oracle, as it stands, on a bounded sample of the layer
     workload, scaled to a whole-step rate: the oracle quantizes every
@@ -498,6 +545,12 @@ def main():
                           "(the timed steps carry events around the dominant kernel's launches only)",
         "sources_digest": sources_digest(),
     }
+    if not args.no_ceilings:
+        ceil = onbox_ceilings(torch)
+        out["onbox_ceilings"] = ceil
+        key = "mfma_fp8_TFLOP/s" if roof["unit"] == "TFLOP/s" else "copy_GB/s"
+        roof["onbox_ceiling"] = ceil[key]
+        roof["frac_of_onbox"] = round(roof["achieved"] / ceil[key], 4)
     if linears is not None and not args.no_bf16_baseline:
         dt, tf = bf16_baseline(torch, linears, reps if args.workload != "stack28" else 28)
         out["bf16_baseline"] = {"ms_per_step": round(dt * 1e3, 3), "TFLOP/s": round(tf, 1),

@@ -1,0 +1,73 @@
+// On-box ceiling for the GEMM kernels' matrix-core work: the same
+// v_mfma_scale_f32_32x32x64_f8f6f4 instruction, 16 independent 32x32
+// accumulators per wave and one wave per SIMD (the GEMM's layout), issued
+// back to back on register operands -- no loads, no LDS, no epilogue.  The
+// operands are pseudo-random finite E4M3 codes (the matrix core's power,
+// hence its clock, depends on the data), the scales 2^0.  Used by the
+// benchmark to state achieved throughput against what the chip sustains,
+// besides the published peak.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8probe.h"
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint32_t mix(uint32_t x) {  // an integer hash (xorshift-multiply)
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return x;
+}
+
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, uint32_t seed, float* out) {
+  const uint32_t gid = blockIdx.x * 256 + threadIdx.x;
+  v8i a[4], b[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      // clearing bit 3 of every byte keeps the codes finite (no S.1111.111)
+      a[t][r] = (int)(mix(seed ^ (gid * 64 + t * 8 + r)) & 0xF7F7F7F7u);
+      b[t][r] = (int)(mix(~seed ^ (gid * 64 + t * 8 + r)) & 0xF7F7F7F7u);
+    }
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+  constexpr int kOne = 127;  // E8M0 scale byte of 2^0
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0, 0, kOne, 0, kOne);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s += acc[i][j][e];
+  out[gid] = s;
+}
+
+}  // namespace
+
+extern "C" int fp8probe_mfma(int workgroups, int iters, uint32_t seed, float* out, hipStream_t stream) {
+  if (workgroups <= 0 || iters <= 0 || out == nullptr) return -1;
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3((uint32_t)workgroups), dim3(256), 0, stream, iters, seed, out);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+extern "C" double fp8probe_mfma_flops(int workgroups, int iters) {
+  // 4 waves x 16 instructions x 2*32*32*64 FLOP per iteration per workgroup
+  return (double)workgroups * iters * 4.0 * 16.0 * 2.0 * 32 * 32 * 64;
+}

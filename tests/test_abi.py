@@ -197,3 +197,17 @@ def test_binding_fails_loudly_when_library_missing(tmp_path):
             fb.load_library(str(tmp_path / "nope.so"))
         finally:
             fb._lib = None
+
+
+def test_probe_library():
+    """The measurement probe (include/fp8probe.h) loads, counts its FLOPs, and
+    rejects bad arguments before launching."""
+    from blockwise_fp8_linear_amd.build import PROBE_LIB
+    p = ctypes.CDLL(PROBE_LIB)
+    p.fp8probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    p.fp8probe_mfma_flops.restype = ctypes.c_double
+    assert p.fp8probe_mfma_flops(256, 10) == 256 * 10 * 4 * 16 * 2 * 32 * 32 * 64
+    p.fp8probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    assert p.fp8probe_mfma(0, 10, 1, P, None) == -1
+    assert p.fp8probe_mfma(256, 0, 1, P, None) == -1
+    assert p.fp8probe_mfma(256, 10, 1, None, None) == -1
