@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fp8blk {
 
 hipError_t launch_quant_rowgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
@@ -46,6 +48,11 @@ struct GemmArgs {
   float* ws;                // split-K or stream-K workspace (may be null when none is needed)
   int splits;
 };
+
+// Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once
+// per device (bit d of *done set after device d succeeded; concurrent first
+// calls only repeat the same idempotent call).
+hipError_t ensure_lds_limit(const void* kernel, int bytes, std::atomic<uint64_t>* done);
 
 // Number of split-K slices the GEMM launcher uses at this shape and the
 // workspace bytes that needs.

@@ -364,6 +364,16 @@ using ScaledRow = Cfg<256, 128, 2, 2, false, true>;
 
 constexpr int kCUs = 256;
 
+hipError_t ensure_lds_limit(const void* kernel, int bytes, std::atomic<uint64_t>* done) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
+  if (bit && (done->load(std::memory_order_acquire) & bit)) return hipSuccess;
+  if (hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)) return e;
+  if (bit) done->fetch_or(bit, std::memory_order_release);
+  return hipSuccess;
+}
+
 int gemm_splits(int64_t I, int64_t J, int64_t R, BScale bmode) {
   if (bmode == BScale::Block) return 1;
   const int64_t tiles = ((I + 255) / 256) * ((J + 255) / 256);
@@ -391,13 +401,8 @@ static hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
   const int splits = g.splits > 0 ? g.splits : 1;
   const int64_t kb_per_split = (nkb + splits - 1) / splits;
   const int64_t blocks = tiles_m * tiles_n * splits;
-  static bool attr_set = false;  // idempotent; a race only repeats the same call
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<C>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> attr_set{0};
+  if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(&gemm_kernel<C>), C::LDS, &attr_set)) return e;
   hipLaunchKernelGGL(gemm_kernel<C>, dim3((uint32_t)blocks), dim3(C::THREADS), C::LDS, stream, g, tiles_m, tiles_n,
                      kb_per_split);
   return hipGetLastError();

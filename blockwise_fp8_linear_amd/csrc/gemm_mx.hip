@@ -777,20 +777,16 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K) {
 }
 
 template <class K>
-hipError_t set_lds_attr(K* kernel, bool& done) {  // idempotent; a race only repeats the same call
-  if (done) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     LDS_BYTES);
-  if (e == hipSuccess) done = true;
-  return e;
+hipError_t set_lds_attr(K* kernel, std::atomic<uint64_t>* done) {
+  return ensure_lds_limit(reinterpret_cast<const void*>(kernel), LDS_BYTES, done);
 }
 
 template <bool BROW>
 hipError_t launch_mx(const GemmArgs& g, hipStream_t stream) {
   const int64_t tiles_m = (g.I + BM - 1) / BM;
   const int64_t tiles_n = (g.J + BN - 1) / BN;
-  static bool attr_set = false;
-  if (hipError_t e = set_lds_attr(&gemm_mx_kernel<BROW>, attr_set)) return e;
+  static std::atomic<uint64_t> attr_set{0};
+  if (hipError_t e = set_lds_attr(&gemm_mx_kernel<BROW>, &attr_set)) return e;
   hipLaunchKernelGGL(gemm_mx_kernel<BROW>, dim3((uint32_t)(tiles_m * tiles_n)), dim3(THREADS), LDS_BYTES, stream, g,
                      tiles_m, tiles_n);
   return hipGetLastError();
@@ -799,8 +795,8 @@ hipError_t launch_mx(const GemmArgs& g, hipStream_t stream) {
 template <bool BROW>
 hipError_t launch_mx_streamk(const GemmArgs& g, hipStream_t stream) {
   const SkPlan p = sk_plan(g.I, g.J, g.R);
-  static bool attr_set = false;
-  if (hipError_t e = set_lds_attr(&gemm_mx_streamk_kernel<BROW>, attr_set)) return e;
+  static std::atomic<uint64_t> attr_set{0};
+  if (hipError_t e = set_lds_attr(&gemm_mx_streamk_kernel<BROW>, &attr_set)) return e;
   float* const partials = p.partial ? g.ws : nullptr;
   hipLaunchKernelGGL(gemm_mx_streamk_kernel<BROW>, dim3((uint32_t)p.grid), dim3(THREADS), LDS_BYTES, stream, g, p.geom,
                      partials);
@@ -814,8 +810,8 @@ hipError_t launch_mx_streamk(const GemmArgs& g, hipStream_t stream) {
 
 hipError_t launch_bwd(const GemmArgs& gd, const GemmArgs& gw, float* ws, hipStream_t stream) {
   const BwdPlan p = bwd_plan(gd.I, gd.R, gd.J);
-  static bool attr_set = false;
-  if (hipError_t e = set_lds_attr(&gemm_mx_bwd_kernel, attr_set)) return e;
+  static std::atomic<uint64_t> attr_set{0};
+  if (hipError_t e = set_lds_attr(&gemm_mx_bwd_kernel, &attr_set)) return e;
   float* const partials = p.partial ? ws : nullptr;
   hipLaunchKernelGGL(gemm_mx_bwd_kernel, dim3((uint32_t)p.grid), dim3(THREADS), LDS_BYTES, stream, gd, gw, p.geom,
                      partials);
