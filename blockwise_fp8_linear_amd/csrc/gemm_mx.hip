@@ -47,8 +47,8 @@ constexpr int PK = 2 * BK;                         // bytes of a row in a pair s
 constexpr int A_SLOT = BM * PK, B_SLOT = BN * PK, SLOT = A_SLOT + B_SLOT;  // 64 KiB
 constexpr int SLOTS = 2;
 constexpr int SC_BYTES = 8192;            // one group of raw scales: A rows, then B rows
-constexpr int MAX_KB = 128;               // 128-blocks per split-K slice (weight-block scales in LDS)
-constexpr int BS_BYTES = 4 * MAX_KB * 4;  // per wave: this slice's weight-block scales, fp32
+constexpr int MAX_KB = 128;               // 128-blocks per segment with weight-block scales (held in LDS)
+constexpr int BS_BYTES = 4 * MAX_KB * 4;  // the 4 waves' weight-block scales of a segment, fp32
 constexpr int LDS_BYTES = SLOTS * SLOT + 2 * SC_BYTES + BS_BYTES;  // 146 KiB
 constexpr int LOADS_A = A_SLOT / 1024 / (THREADS / 64);  // 1 KiB per wave instruction
 constexpr int LOADS_B = B_SLOT / 1024 / (THREADS / 64);
