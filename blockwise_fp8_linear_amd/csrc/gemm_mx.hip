@@ -357,7 +357,7 @@ struct Dst {
 // wave's 32x32 accumulator tile (a, b) in the MFMA register layout; it is
 // called once per tile, in (a, b) order.  Starts with a barrier, so the LDS
 // ring and any earlier staging are free.
-template <class Src>
+template <int BATCH, class Src>
 __device__ __forceinline__ void store_tile_from(const Dst& d, uint8_t* lds, int64_t i0, int64_t j0, Src src) {
   // ---- epilogue, staged through LDS so that global stores are whole rows.
   // src(a, b) lane l, element e holds row i = wm0 + 32a + l%32 and column
@@ -378,6 +378,10 @@ __device__ __forceinline__ void store_tile_from(const Dst& d, uint8_t* lds, int6
     float* const outf = static_cast<float*>(d.out);
     uint16_t* const outh = static_cast<uint16_t*>(d.out);
     const int64_t col0 = j0 + wn0;
+    // the wave's 128 columns are all in or all out (N is a multiple of 128);
+    // full: no row of the wave's tile is past the edge either
+    const bool col_ok = col0 < d.cols;
+    const bool full = col_ok && i0 + wm0 + WM <= d.rows;
     if (!f32) {
       // bf16: unit = 8 bytes, row = 256 bytes, all 128 rows at once
 #pragma unroll
@@ -395,17 +399,27 @@ __device__ __forceinline__ void store_tile_from(const Dst& d, uint8_t* lds, int6
             *reinterpret_cast<uint2*>(stage_area + row * 256 + unit * 8) = o;
           }
         }
-      // read: 16 lanes per row (16 bytes = units 2k, 2k+1 each), 4 rows per pass
-#pragma unroll 4
-      for (int pass = 0; pass < 32; ++pass) {
-        const uint32_t row = pass * 4 + (lane >> 4), k = lane & 15;
-        const uint32_t x = row & 31;
-        const uint32_t pu = (2 * k) ^ x;  // physical unit of logical unit 2k
-        u32x4 v = *reinterpret_cast<const u32x4*>(stage_area + row * 256 + (pu & ~1u) * 8);
-        if (pu & 1) v = u32x4{v[2], v[3], v[0], v[1]};  // the pair is stored swapped
-        const int64_t i = i0 + wm0 + row;
-        if (i < d.rows && col0 < d.cols)
-          *reinterpret_cast<u32x4*>(outh + i * d.ld + col0 + 8 * k) = v;
+      // read: 16 lanes per row (16 bytes = units 2k, 2k+1 each), 4 rows per
+      // pass, in batches of passes whose LDS reads are all issued before
+      // the first store (a read waited for right before its own store
+      // exposes the LDS latency 32 times)
+#pragma unroll 1
+      for (int pb = 0; pb < 32; pb += BATCH) {
+        u32x4 v[BATCH];
+#pragma unroll
+        for (int s = 0; s < BATCH; ++s) {
+          const uint32_t row = (pb + s) * 4 + (lane >> 4), k = lane & 15;
+          const uint32_t pu = (2 * k) ^ (row & 31);  // physical unit of logical unit 2k
+          v[s] = *reinterpret_cast<const u32x4*>(stage_area + row * 256 + (pu & ~1u) * 8);
+        }
+#pragma unroll
+        for (int s = 0; s < BATCH; ++s) {
+          const uint32_t row = (pb + s) * 4 + (lane >> 4), k = lane & 15;
+          // the pair is stored swapped when its physical unit is odd (row odd)
+          const u32x4 o = (row & 1) ? u32x4{v[s][2], v[s][3], v[s][0], v[s][1]} : v[s];
+          const int64_t i = i0 + wm0 + row;
+          if (full || (i < d.rows && col_ok)) *reinterpret_cast<u32x4*>(outh + i * d.ld + col0 + 8 * k) = o;
+        }
       }
     } else {
       // fp32: unit = 16 bytes, row = 512 bytes, two halves of 64 rows
@@ -426,19 +440,38 @@ __device__ __forceinline__ void store_tile_from(const Dst& d, uint8_t* lds, int6
             }
           }
         }
-        // read: 32 lanes per row (one unit each), 2 rows per pass
-#pragma unroll 4
-        for (int pass = 0; pass < 32; ++pass) {
-          const uint32_t row = pass * 2 + (lane >> 5), k = lane & 31;
-          const v4f v = *reinterpret_cast<const v4f*>(stage_area + row * 512 + ((k ^ (row & 31)) * 16));
-          const int64_t i = i0 + wm0 + 64 * h + row;
-          if (i < d.rows && col0 < d.cols) {
-            v4f* const dst = reinterpret_cast<v4f*>(outf + i * d.ld + col0 + 4 * k);
-            if (d.acc) {
-              const v4f o = *dst;
-              *dst = v4f{o[0] + v[0], o[1] + v[1], o[2] + v[2], o[3] + v[3]};
-            } else {
-              *dst = v;
+        // read: 32 lanes per row (one unit each), 2 rows per pass, batched
+        // as above
+#pragma unroll 1
+        for (int pb = 0; pb < 32; pb += BATCH) {
+          v4f v[BATCH];
+#pragma unroll
+          for (int s = 0; s < BATCH; ++s) {
+            const uint32_t row = (pb + s) * 2 + (lane >> 5), k = lane & 31;
+            v[s] = *reinterpret_cast<const v4f*>(stage_area + row * 512 + ((k ^ (row & 31)) * 16));
+          }
+          if (d.acc) {
+            v4f o[BATCH];
+#pragma unroll
+            for (int s = 0; s < BATCH; ++s) {
+              const uint32_t row = (pb + s) * 2 + (lane >> 5), k = lane & 31;
+              const int64_t i = i0 + wm0 + 64 * h + row;
+              if (full || (i < d.rows && col_ok)) o[s] = *reinterpret_cast<const v4f*>(outf + i * d.ld + col0 + 4 * k);
+            }
+#pragma unroll
+            for (int s = 0; s < BATCH; ++s) {
+              const uint32_t row = (pb + s) * 2 + (lane >> 5), k = lane & 31;
+              const int64_t i = i0 + wm0 + 64 * h + row;
+              if (full || (i < d.rows && col_ok))
+                *reinterpret_cast<v4f*>(outf + i * d.ld + col0 + 4 * k) =
+                    v4f{o[s][0] + v[s][0], o[s][1] + v[s][1], o[s][2] + v[s][2], o[s][3] + v[s][3]};
+            }
+          } else {
+#pragma unroll
+            for (int s = 0; s < BATCH; ++s) {
+              const uint32_t row = (pb + s) * 2 + (lane >> 5), k = lane & 31;
+              const int64_t i = i0 + wm0 + 64 * h + row;
+              if (full || (i < d.rows && col_ok)) *reinterpret_cast<v4f*>(outf + i * d.ld + col0 + 4 * k) = v[s];
             }
           }
         }
@@ -450,6 +483,7 @@ __device__ __forceinline__ void store_tile_from(const Dst& d, uint8_t* lds, int6
 // Store a tile from registers.  (A local copy: reading the caller's array
 // through the reference while storing to LDS makes the compiler keep it in
 // memory -- hundreds of spilled registers.)
+template <int BATCH>
 __device__ __forceinline__ void store_tile(const Dst& d, uint8_t* lds, int64_t i0, int64_t j0,
                                            const v16f (&acc_in)[TM][TN]) {
   v16f acc[TM][TN];
@@ -457,7 +491,7 @@ __device__ __forceinline__ void store_tile(const Dst& d, uint8_t* lds, int64_t i
   for (int a = 0; a < TM; ++a)
 #pragma unroll
     for (int b = 0; b < TN; ++b) acc[a][b] = acc_in[a][b];
-  store_tile_from(d, lds, i0, j0, [&](int a, int b) { return acc[a][b]; });
+  store_tile_from<BATCH>(d, lds, i0, j0, [&](int a, int b) { return acc[a][b]; });
 }
 
 // One output tile per workgroup, the whole reduction (Fprop and Dgrad).
@@ -469,7 +503,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
   tile_origin(tile, tiles_m, tiles_n, i0, j0);
   v16f acc[TM][TN];
   mma_segment<BROW>(g, lds, i0, j0, 0, g.R / 128, acc);
-  store_tile(Dst{g.out, g.J, g.I, g.J, g.out_f32, g.accumulate}, lds, i0, j0, acc);
+  store_tile<8>(Dst{g.out, g.J, g.I, g.J, g.out_f32, g.accumulate}, lds, i0, j0, acc);
 }
 
 // Wgrad (long reduction over tokens, few output tiles) on a persistent grid
@@ -514,7 +548,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_streamk_kernel(GemmArgs g, Sk
     tile_origin(t, sg.tiles_m, sg.tiles_n, i0, j0);
     lds_barrier();  // the previous tile's epilogue is done with LDS
     mma_segment<BROW>(g, lds, i0, j0, 0, U * 4, acc);
-    store_tile(out, lds, i0, j0, acc);
+    store_tile<1>(out, lds, i0, j0, acc);
   }
   const int64_t W = sg.units, Gs = sg.sk_grid;
   // r: this workgroup's range (and slot pair) index
@@ -529,10 +563,10 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_streamk_kernel(GemmArgs g, Sk
     lds_barrier();
     mma_segment<BROW>(g, lds, i0, j0, lo * 4, (hi - lo) * 4, acc);
     if (lo == 0 && hi == U) {
-      store_tile(out, lds, i0, j0, acc);
+      store_tile<1>(out, lds, i0, j0, acc);
     } else {
       float* const slot = partials + (2 * r + (u == ubeg ? 0 : 1)) * (int64_t)(BM * BN);
-      store_tile(Dst{slot, BN, BM, BN, true, false}, lds, 0, 0, acc);
+      store_tile<1>(Dst{slot, BN, BM, BN, true, false}, lds, 0, 0, acc);
     }
     u = ts * U + hi;
   }
@@ -639,10 +673,10 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_bwd_kernel(GemmArgs gd, GemmA
     if (lo == 0 && hi == U) {
       const Dst d{p1 ? gw.out : gd.out, p1 ? gw.J : gd.J, p1 ? gw.I : gd.I, p1 ? gw.J : gd.J,
                   p1 ? gw.out_f32 : gd.out_f32, p1 ? gw.accumulate : gd.accumulate};
-      store_tile(d, lds, i0, j0, acc);
+      store_tile<1>(d, lds, i0, j0, acc);
     } else {
       float* const slot = partials + (2 * r + (u == ubeg ? 0 : 1)) * (int64_t)(BM * BN);
-      store_tile(Dst{slot, BN, BM, BN, true, false}, lds, 0, 0, acc);
+      store_tile<1>(Dst{slot, BN, BM, BN, true, false}, lds, 0, 0, acc);
     }
     u = base + ts * U + hi;
   }
