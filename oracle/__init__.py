@@ -57,11 +57,13 @@ def _load():
     lib.orc_bf16_rne.restype = ctypes.c_uint16
     lib.orc_bf16_rne.argtypes = [ctypes.c_float]
     lib.orc_quantize_rowgroup.restype = None
-    lib.orc_quantize_rowgroup.argtypes = [u16p, i64, i64, i64, u8p, i64, f32p]
+    lib.orc_quantize_rowgroup.argtypes = [u16p, i64, i64, i64, u8p, i64, f32p, ctypes.c_int]
     lib.orc_quantize_colgroup.restype = None
-    lib.orc_quantize_colgroup.argtypes = [u16p, i64, i64, i64, u8p, i64, f32p]
+    lib.orc_quantize_colgroup.argtypes = [u16p, i64, i64, i64, u8p, i64, f32p, ctypes.c_int]
     lib.orc_quantize_block.restype = None
-    lib.orc_quantize_block.argtypes = [u16p, i64, i64, i64, u8p, u8p, f32p]
+    lib.orc_quantize_block.argtypes = [u16p, i64, i64, i64, u8p, u8p, f32p, ctypes.c_int]
+    lib.orc_scale_fp32.restype = ctypes.c_float
+    lib.orc_scale_fp32.argtypes = [ctypes.c_float]
     for name in ("orc_gemm_fprop", "orc_gemm_dgrad", "orc_gemm_wgrad"):
         f = getattr(lib, name)
         f.restype = None
@@ -138,7 +140,15 @@ def rounding_mode_is_nearest() -> bool:
 
 # ------------------------------------------------------------ quantizers --
 
-def quantize_rowgroup(x: np.ndarray, cols: int | None = None):
+SCALE_POW2, SCALE_FP32 = 0, 1   # the scale rules (`mode` of the quantizers)
+
+
+def scale_fp32(amax: float) -> float:
+    """The amax / 448 rule's scale of a group with this (bf16-exact) amax."""
+    return float(_load().orc_scale_fp32(float(amax)))
+
+
+def quantize_rowgroup(x: np.ndarray, cols: int | None = None, mode: int = SCALE_POW2):
     """Row groups of 128 along the last axis.  x: uint16 [rows, ld_x] (bf16 bits);
     the first `cols` columns are quantized.  Returns (q [rows, cols] uint8,
     s [rows, cols/128] float32)."""
@@ -148,11 +158,11 @@ def quantize_rowgroup(x: np.ndarray, cols: int | None = None):
     q = np.empty((rows, cols), dtype=np.uint8)
     s = np.empty((rows, cols // 128), dtype=np.float32)
     _load().orc_quantize_rowgroup(_p(x, ctypes.c_uint16), rows, cols, ld,
-                                  _p(q, ctypes.c_uint8), cols, _p(s, ctypes.c_float))
+                                  _p(q, ctypes.c_uint8), cols, _p(s, ctypes.c_float), mode)
     return q, s
 
 
-def quantize_colgroup(x: np.ndarray, cols: int | None = None):
+def quantize_colgroup(x: np.ndarray, cols: int | None = None, mode: int = SCALE_POW2):
     """Groups of 128 consecutive rows per column, output transposed.
     Returns (qT [cols, rows] uint8, sT [cols, rows/128] float32)."""
     x = _c(x, np.uint16)
@@ -161,11 +171,11 @@ def quantize_colgroup(x: np.ndarray, cols: int | None = None):
     qT = np.empty((cols, rows), dtype=np.uint8)
     sT = np.empty((cols, rows // 128), dtype=np.float32)
     _load().orc_quantize_colgroup(_p(x, ctypes.c_uint16), rows, cols, ld,
-                                  _p(qT, ctypes.c_uint8), rows, _p(sT, ctypes.c_float))
+                                  _p(qT, ctypes.c_uint8), rows, _p(sT, ctypes.c_float), mode)
     return qT, sT
 
 
-def quantize_block(w: np.ndarray, transpose: bool = True):
+def quantize_block(w: np.ndarray, transpose: bool = True, mode: int = SCALE_POW2):
     """128x128 blocks.  Returns (q [rows, cols], qT [cols, rows] or None,
     s [rows/128, cols/128])."""
     w = _c(w, np.uint16)
@@ -175,7 +185,7 @@ def quantize_block(w: np.ndarray, transpose: bool = True):
     s = np.empty((rows // 128, cols // 128), dtype=np.float32)
     _load().orc_quantize_block(_p(w, ctypes.c_uint16), rows, cols, cols, _p(q, ctypes.c_uint8),
                                _p(qT, ctypes.c_uint8) if transpose else None,
-                               _p(s, ctypes.c_float))
+                               _p(s, ctypes.c_float), mode)
     return q, qT, s
 
 

@@ -29,6 +29,13 @@
  *     all-zero group has s = 1.  s is stored as an fp32 multiplier (x ~ q*s).
  *   - q = RNE-to-E4M3(x / s), saturating at +-448; the division by a power of
  *     two is exact, so there is a single rounding.
+ *   - mode 1, a numerics variant (FP8BLK_SCALE_FP32): [P1 s3.2 para 3] sets
+ *     the run's power-of-two scale against the DeepSeek-V3 recipe it follows
+ *     otherwise, without printing that recipe's formula.  READING: the scale
+ *     that puts the group's amax on 448 exactly, s = fl32(amax / 448) (IEEE
+ *     single division; amax is a bf16 value, exact in float), s = 1 for an
+ *     all-zero group, and q = RNE-to-E4M3(fl32(x / s)) saturating at +-448
+ *     (the rounded quotient of the amax itself can exceed 448 by an ulp).
  *   - GEMMs (Fprop, Dgrad, Wgrad all on the FP8 path [P1 s3.2 para 4; P3 s2.3]):
  *     out[i][j] = sum over 128-deep reduction blocks b of
  *                 sa(i,b) * sb(j,b) * sum_{r in b} dec(A[i][r]) * dec(B[j][r]).
@@ -38,7 +45,10 @@
  *               2^-18 below 2^18, 128 of them need < 44 bits);
  *       y32   : READING of "fp32 accumulation": each exact block term
  *               p*sa*sb is rounded once to fp32 and added to an fp32
- *               accumulator in increasing block order;
+ *               accumulator in increasing block order (with mode-1 scales,
+ *               which are not powers of two, the term is first formed in
+ *               double: one extra rounding of 2^-53, far inside every
+ *               tolerance that y32 serves);
  *       bound : sum over all terms of |sa*dec*sb*dec| (double), the scale that
  *               any summation-order error is proportional to.
  *   - bf16 output: round-to-nearest-even of the fp32 result [P1 s3.2 para 4:
@@ -168,13 +178,43 @@ int orc_scale_exponent(double amax)
     return e;
 }
 
+/* READING of the mode-1 scale (see the header): fl32(amax / 448), 1 for 0. */
+float orc_scale_fp32(float amax)
+{
+    if (amax == 0.0f)
+        return 1.0f;
+    return amax / 448.0f;
+}
+
+/* The scale of a group with this amax under `mode`; for mode 0 also its
+ * exponent e (s = 2^e). */
+static float group_scale(double amax, int mode, int *e)
+{
+    if (mode == 0) {
+        *e = orc_scale_exponent(amax);
+        return ldexpf(1.0f, *e);
+    }
+    *e = 0;
+    return orc_scale_fp32((float)amax);
+}
+
+/* The code of element x of a group: mode 0 encodes the exact x * 2^-e,
+ * mode 1 the single-precision quotient fl32(x / s). */
+static uint8_t quantize_one(double x, int mode, int e, float s)
+{
+    if (mode == 0)
+        return orc_e4m3_encode(ldexp(x, -e));
+    return orc_e4m3_encode((double)((float)x / s));
+}
+
 /* ----------------------------------------------------------- quantizers --- */
 
 /* Row groups [P1 s3.2 para 2]: x is rows x cols (row stride ld_x), groups are
  * 128 consecutive elements of a row.  q is rows x cols (row stride ld_q),
- * s is rows x (cols/128), dense. */
+ * s is rows x (cols/128), dense.  mode: the scale rule (0 power of two,
+ * 1 amax / 448), as for the other two quantizers. */
 void orc_quantize_rowgroup(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
-                           uint8_t *q, int64_t ld_q, float *s)
+                           uint8_t *q, int64_t ld_q, float *s, int mode)
 {
     int64_t G = cols / GROUP;
     int64_t r;
@@ -183,17 +223,18 @@ void orc_quantize_rowgroup(const uint16_t *x, int64_t rows, int64_t cols, int64_
         int64_t g;
         for (g = 0; g < G; ++g) {
             double amax = 0.0;
+            float sc;
             int i, e;
             for (i = 0; i < GROUP; ++i) {
                 double v = fabs(orc_bf16_to_double(x[r * ld_x + g * GROUP + i]));
                 if (v > amax)
                     amax = v;
             }
-            e = orc_scale_exponent(amax);
-            s[r * G + g] = ldexpf(1.0f, e);
+            sc = group_scale(amax, mode, &e);
+            s[r * G + g] = sc;
             for (i = 0; i < GROUP; ++i)
                 q[r * ld_q + g * GROUP + i] =
-                    orc_e4m3_encode(ldexp(orc_bf16_to_double(x[r * ld_x + g * GROUP + i]), -e));
+                    quantize_one(orc_bf16_to_double(x[r * ld_x + g * GROUP + i]), mode, e, sc);
         }
     }
 }
@@ -202,7 +243,7 @@ void orc_quantize_rowgroup(const uint16_t *x, int64_t rows, int64_t cols, int64_
  * column (the token dimension, which is Wgrad's reduction dimension), written
  * transposed: qT is cols x rows (row stride ld_qT), sT is cols x (rows/128). */
 void orc_quantize_colgroup(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
-                           uint8_t *qT, int64_t ld_qT, float *sT)
+                           uint8_t *qT, int64_t ld_qT, float *sT, int mode)
 {
     int64_t G = rows / GROUP;
     int64_t c;
@@ -211,17 +252,18 @@ void orc_quantize_colgroup(const uint16_t *x, int64_t rows, int64_t cols, int64_
         int64_t g;
         for (g = 0; g < G; ++g) {
             double amax = 0.0;
+            float sc;
             int i, e;
             for (i = 0; i < GROUP; ++i) {
                 double v = fabs(orc_bf16_to_double(x[(g * GROUP + i) * ld_x + c]));
                 if (v > amax)
                     amax = v;
             }
-            e = orc_scale_exponent(amax);
-            sT[c * G + g] = ldexpf(1.0f, e);
+            sc = group_scale(amax, mode, &e);
+            sT[c * G + g] = sc;
             for (i = 0; i < GROUP; ++i)
                 qT[c * ld_qT + g * GROUP + i] =
-                    orc_e4m3_encode(ldexp(orc_bf16_to_double(x[(g * GROUP + i) * ld_x + c]), -e));
+                    quantize_one(orc_bf16_to_double(x[(g * GROUP + i) * ld_x + c]), mode, e, sc);
         }
     }
 }
@@ -230,7 +272,7 @@ void orc_quantize_colgroup(const uint16_t *x, int64_t rows, int64_t cols, int64_
  * rows x cols dense; qT (optional, may be NULL) is cols x rows dense; s is
  * (rows/128) x (cols/128). */
 void orc_quantize_block(const uint16_t *w, int64_t rows, int64_t cols, int64_t ld_w,
-                        uint8_t *q, uint8_t *qT, float *s)
+                        uint8_t *q, uint8_t *qT, float *s, int mode)
 {
     int64_t RB = rows / GROUP, CB = cols / GROUP;
     int64_t blk;
@@ -238,6 +280,7 @@ void orc_quantize_block(const uint16_t *w, int64_t rows, int64_t cols, int64_t l
     for (blk = 0; blk < RB * CB; ++blk) {
         int64_t bi = blk / CB, bj = blk % CB, r, c;
         double amax = 0.0;
+        float sc;
         int e;
         for (r = bi * GROUP; r < (bi + 1) * GROUP; ++r)
             for (c = bj * GROUP; c < (bj + 1) * GROUP; ++c) {
@@ -245,11 +288,11 @@ void orc_quantize_block(const uint16_t *w, int64_t rows, int64_t cols, int64_t l
                 if (v > amax)
                     amax = v;
             }
-        e = orc_scale_exponent(amax);
-        s[bi * CB + bj] = ldexpf(1.0f, e);
+        sc = group_scale(amax, mode, &e);
+        s[bi * CB + bj] = sc;
         for (r = bi * GROUP; r < (bi + 1) * GROUP; ++r)
             for (c = bj * GROUP; c < (bj + 1) * GROUP; ++c) {
-                uint8_t code = orc_e4m3_encode(ldexp(orc_bf16_to_double(w[r * ld_w + c]), -e));
+                uint8_t code = quantize_one(orc_bf16_to_double(w[r * ld_w + c]), mode, e, sc);
                 q[r * cols + c] = code;
                 if (qT)
                     qT[c * rows + r] = code;
