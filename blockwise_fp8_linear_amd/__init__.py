@@ -21,6 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp8blk.h")
 
 # enum values of include/fp8blk.h
 FP8BLK_SCALE_POW2 = 0
+FP8BLK_SCALE_FP32 = 1
 FP8BLK_OUT_BF16 = 0
 FP8BLK_OUT_FP32 = 1
 FP8BLK_OUT_FP32_ACCUM = 2
@@ -121,20 +122,22 @@ def _dense(t, dtype, name):
 
 # -------------------------------------------------------------- quantizers --
 
-def fp8_quantize_rowgroup(x, q=None, s=None, stream=None):
+def fp8_quantize_rowgroup(x, q=None, s=None, stream=None, scale_mode=FP8BLK_SCALE_POW2):
     """Groups of 128 along the last dim.  x: bf16 [rows, cols] (row stride may
-    exceed cols).  Returns (q uint8 [rows, cols], s fp32 [rows, cols/128])."""
+    exceed cols).  Returns (q uint8 [rows, cols], s fp32 [rows, cols/128]).
+    scale_mode (every quantizer): FP8BLK_SCALE_POW2 (power-of-two scales) or
+    FP8BLK_SCALE_FP32 (amax / 448; GEMMs then need FP8BLK_ALGO_PROMOTE)."""
     import torch
     _dev(x, torch.bfloat16, "x")
     rows, cols = x.shape
     q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else _dev(q, torch.uint8, "q")
     s = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device) if s is None else _dense(s, torch.float32, "s")
     _check(load_library().fp8_quantize_rowgroup(x.data_ptr(), rows, cols, x.stride(0), q.data_ptr(), q.stride(0),
-                                                s.data_ptr(), FP8BLK_SCALE_POW2, _stream(stream)))
+                                                s.data_ptr(), scale_mode, _stream(stream)))
     return q, s
 
 
-def fp8_quantize_colgroup(x, qT=None, sT=None, stream=None):
+def fp8_quantize_colgroup(x, qT=None, sT=None, stream=None, scale_mode=FP8BLK_SCALE_POW2):
     """Groups of 128 consecutive rows per column, written transposed.
     Returns (qT uint8 [cols, rows], sT fp32 [cols, rows/128])."""
     import torch
@@ -144,11 +147,11 @@ def fp8_quantize_colgroup(x, qT=None, sT=None, stream=None):
     sT = (torch.empty((cols, rows // 128), dtype=torch.float32, device=x.device) if sT is None
           else _dense(sT, torch.float32, "sT"))
     _check(load_library().fp8_quantize_colgroup(x.data_ptr(), rows, cols, x.stride(0), qT.data_ptr(), qT.stride(0),
-                                                sT.data_ptr(), FP8BLK_SCALE_POW2, _stream(stream)))
+                                                sT.data_ptr(), scale_mode, _stream(stream)))
     return qT, sT
 
 
-def fp8_quantize_dual(x, q=None, s=None, qT=None, sT=None, stream=None):
+def fp8_quantize_dual(x, q=None, s=None, qT=None, sT=None, stream=None, scale_mode=FP8BLK_SCALE_POW2):
     """Row groups and column groups in one pass.  Returns (q, s, qT, sT) equal
     to fp8_quantize_rowgroup(x) + fp8_quantize_colgroup(x)."""
     import torch
@@ -161,11 +164,11 @@ def fp8_quantize_dual(x, q=None, s=None, qT=None, sT=None, stream=None):
           else _dense(sT, torch.float32, "sT"))
     _check(load_library().fp8_quantize_dual(x.data_ptr(), rows, cols, x.stride(0), q.data_ptr(), q.stride(0),
                                             s.data_ptr(), qT.data_ptr(), qT.stride(0), sT.data_ptr(),
-                                            FP8BLK_SCALE_POW2, _stream(stream)))
+                                            scale_mode, _stream(stream)))
     return q, s, qT, sT
 
 
-def fp8_quantize_block_batch(weights, transpose=True, outs=None, stream=None):
+def fp8_quantize_block_batch(weights, transpose=True, outs=None, stream=None, scale_mode=FP8BLK_SCALE_POW2):
     """Several weights (bf16 [rows, cols] tensors, at most 8) quantized in one
     launch, each as by fp8_quantize_block.  Returns a list of (q, qT or None,
     s); `outs`, if given, is such a list of preallocated outputs."""
@@ -189,11 +192,11 @@ def fp8_quantize_block_batch(weights, transpose=True, outs=None, stream=None):
         jobs[k] = _BlockJob(w.data_ptr(), rows, cols, w.stride(0), q.data_ptr(),
                             qT.data_ptr() if qT is not None else None, s.data_ptr())
         res.append((q, qT, s))
-    _check(load_library().fp8_quantize_block_batch(jobs, n, FP8BLK_SCALE_POW2, _stream(stream)))
+    _check(load_library().fp8_quantize_block_batch(jobs, n, scale_mode, _stream(stream)))
     return res
 
 
-def fp8_quantize_block(w, transpose=True, q=None, qT=None, s=None, stream=None):
+def fp8_quantize_block(w, transpose=True, q=None, qT=None, s=None, stream=None, scale_mode=FP8BLK_SCALE_POW2):
     """128x128 blocks.  Returns (q uint8 [rows, cols], qT uint8 [cols, rows] or
     None, s fp32 [rows/128, cols/128])."""
     import torch
@@ -209,7 +212,7 @@ def fp8_quantize_block(w, transpose=True, q=None, qT=None, s=None, stream=None):
          else _dense(s, torch.float32, "s"))
     _check(load_library().fp8_quantize_block(w.data_ptr(), rows, cols, w.stride(0), q.data_ptr(),
                                              qT.data_ptr() if qT is not None else None, s.data_ptr(),
-                                             FP8BLK_SCALE_POW2, _stream(stream)))
+                                             scale_mode, _stream(stream)))
     return q, qT, s
 
 

@@ -19,6 +19,7 @@ std::atomic<int> g_device_ok[kMaxDevices];
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool mult128(int64_t v) { return v > 0 && v % kGroup == 0; }
+bool valid_scale_mode(int m) { return m == FP8BLK_SCALE_POW2 || m == FP8BLK_SCALE_FP32; }
 
 int check_device() {
   int dev = 0;
@@ -59,7 +60,7 @@ const char* fp8_status_string(int status) {
 
 int fp8_quantize_rowgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
                           float* s, int scale_mode, hipStream_t stream) {
-  if (scale_mode != FP8BLK_SCALE_POW2) return FP8BLK_ERR_ARG;
+  if (!valid_scale_mode(scale_mode)) return FP8BLK_ERR_ARG;
   if (!x || !q || !s) return FP8BLK_ERR_NULL;
   if (rows <= 0 || !mult128(cols)) return FP8BLK_ERR_DIM;
   if (ld_x < cols || ld_q < cols) return FP8BLK_ERR_ARG;
@@ -67,12 +68,12 @@ int fp8_quantize_rowgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t
     return FP8BLK_ERR_ARG;
   if (!aligned16(x) || !aligned16(q) || !aligned4(s) || ld_x % 8 || ld_q % 16) return FP8BLK_ERR_ALIGN;
   if (int rc = check_device()) return rc;
-  return finish(fp8blk::launch_quant_rowgroup(x, rows, cols, ld_x, q, ld_q, s, stream));
+  return finish(fp8blk::launch_quant_rowgroup(x, rows, cols, ld_x, q, ld_q, s, scale_mode == FP8BLK_SCALE_FP32, stream));
 }
 
 int fp8_quantize_colgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qT, int64_t ld_qT,
                           float* sT, int scale_mode, hipStream_t stream) {
-  if (scale_mode != FP8BLK_SCALE_POW2) return FP8BLK_ERR_ARG;
+  if (!valid_scale_mode(scale_mode)) return FP8BLK_ERR_ARG;
   if (!x || !qT || !sT) return FP8BLK_ERR_NULL;
   if (!mult128(rows) || !mult128(cols)) return FP8BLK_ERR_DIM;
   if (ld_x < cols || ld_qT < rows) return FP8BLK_ERR_ARG;
@@ -80,12 +81,12 @@ int fp8_quantize_colgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t
     return FP8BLK_ERR_ARG;
   if (!aligned16(x) || !aligned16(qT) || !aligned4(sT) || ld_x % 8 || ld_qT % 16) return FP8BLK_ERR_ALIGN;
   if (int rc = check_device()) return rc;
-  return finish(fp8blk::launch_quant_colgroup(x, rows, cols, ld_x, qT, ld_qT, sT, stream));
+  return finish(fp8blk::launch_quant_colgroup(x, rows, cols, ld_x, qT, ld_qT, sT, scale_mode == FP8BLK_SCALE_FP32, stream));
 }
 
 int fp8_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q, float* s,
                       uint8_t* qT, int64_t ld_qT, float* sT, int scale_mode, hipStream_t stream) {
-  if (scale_mode != FP8BLK_SCALE_POW2) return FP8BLK_ERR_ARG;
+  if (!valid_scale_mode(scale_mode)) return FP8BLK_ERR_ARG;
   if (!x || !q || !s || !qT || !sT) return FP8BLK_ERR_NULL;
   if (!mult128(rows) || !mult128(cols)) return FP8BLK_ERR_DIM;
   if (ld_x < cols || ld_q < cols || ld_qT < rows) return FP8BLK_ERR_ARG;
@@ -96,12 +97,13 @@ int fp8_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_
       ld_qT % 16)
     return FP8BLK_ERR_ALIGN;
   if (int rc = check_device()) return rc;
-  return finish(fp8blk::launch_quant_dual(x, rows, cols, ld_x, q, ld_q, s, qT, ld_qT, sT, stream));
+  return finish(fp8blk::launch_quant_dual(x, rows, cols, ld_x, q, ld_q, s, qT, ld_qT, sT, scale_mode == FP8BLK_SCALE_FP32,
+                                              stream));
 }
 
 static int check_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld_w, const uint8_t* q,
                        const uint8_t* qT, const float* s, int scale_mode) {
-  if (scale_mode != FP8BLK_SCALE_POW2) return FP8BLK_ERR_ARG;
+  if (!valid_scale_mode(scale_mode)) return FP8BLK_ERR_ARG;
   if (!w || !q || !s) return FP8BLK_ERR_NULL;
   if (!mult128(rows) || !mult128(cols)) return FP8BLK_ERR_DIM;
   if (ld_w < cols) return FP8BLK_ERR_ARG;
@@ -115,7 +117,7 @@ int fp8_quantize_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld
                        float* s, int scale_mode, hipStream_t stream) {
   if (int rc = check_block(w, rows, cols, ld_w, q, qT, s, scale_mode)) return rc;
   if (int rc = check_device()) return rc;
-  return finish(fp8blk::launch_quant_block(w, rows, cols, ld_w, q, qT, s, stream));
+  return finish(fp8blk::launch_quant_block(w, rows, cols, ld_w, q, qT, s, scale_mode == FP8BLK_SCALE_FP32, stream));
 }
 
 int fp8_quantize_block_batch(const fp8blk_block_job* jobs, int n_jobs, int scale_mode, hipStream_t stream) {
@@ -131,7 +133,7 @@ int fp8_quantize_block_batch(const fp8blk_block_job* jobs, int n_jobs, int scale
   }
   if (blocks >= (int64_t(1) << 31)) return FP8BLK_ERR_ARG;
   if (int rc = check_device()) return rc;
-  return finish(fp8blk::launch_quant_block_batch(job, n_jobs, stream));
+  return finish(fp8blk::launch_quant_block_batch(job, n_jobs, scale_mode == FP8BLK_SCALE_FP32, stream));
 }
 
 static int check_gemm_common(int64_t M, int64_t N, int64_t K, const void* a, const float* sa, const void* b,

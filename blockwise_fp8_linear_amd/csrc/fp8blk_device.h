@@ -1,8 +1,9 @@
 // Device-side helpers shared by the gfx950 kernels of libfp8blk.
 //
 // Conventions follow include/fp8blk.h: bf16 values arrive as raw 16-bit
-// patterns, E4M3 codes are OCP "fn" bytes, scales are powers of two stored
-// as fp32 (so their exponent field is an E8M0 byte).
+// patterns, E4M3 codes are OCP "fn" bytes, scales are fp32 multipliers --
+// powers of two by default (so their exponent field is an E8M0 byte), or
+// amax / 448 under FP8BLK_SCALE_FP32.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -88,21 +89,53 @@ __device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Four bf16 (two words) times 2^-e, rounded to E4M3 (RNE) into one word,
-// byte i holding element i.  The multiply by a power of two is exact, so
-// the conversion is the only rounding; the scale rule keeps |x * 2^-e| <= 448,
-// inside the converter's finite range.
-__device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, float inv) {
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w0) * inv, bf16_hi(w0) * inv, 0, false);
-  r = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w1) * inv, bf16_hi(w1) * inv, r, true);
+// The two scale rules, each built from the bf16 pattern of a group's
+// non-negative amax: `s` is the scale stored, and sc(x) the value that the
+// element x is rounded from (the converter rounds to nearest even).
+//  * Pow2Scale (the pages' run: "Puro-2B ... part 3/7", section 3.2, third
+//    paragraph): s = 2^e by scale_exponent; x * 2^-e is exact and, by the
+//    rule, at most 448 in magnitude, so the conversion is the only rounding.
+//  * Fp32Scale (the DeepSeek-V3 representation that the same paragraph
+//    contrasts with the power-of-two one): s = fl32(amax / 448), 1 for an
+//    all-zero group, and the value fl32(x / s), clamped to +-448 (the cast
+//    saturates; the rounded quotient of the amax itself may exceed 448 by
+//    an ulp).  Both divisions are IEEE-correctly rounded.
+struct Pow2Scale {
+  float s, inv;
+  __device__ __forceinline__ explicit Pow2Scale(uint32_t amax_bits) {
+    const int e = scale_exponent(amax_bits);
+    s = pow2f(e);
+    inv = pow2f(-e);
+  }
+  __device__ __forceinline__ float operator()(float x) const { return x * inv; }
+};
+
+struct Fp32Scale {
+  float s;
+  __device__ __forceinline__ explicit Fp32Scale(uint32_t amax_bits) {
+    s = amax_bits == 0 ? 1.0f : __uint_as_float(amax_bits << 16) / 448.0f;
+  }
+  __device__ __forceinline__ float operator()(float x) const {
+    const float v = x / s;
+    return __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
+  }
+};
+
+// Four bf16 (two words) scaled by sc and rounded to E4M3 (RNE) into one
+// word, byte i holding element i.
+template <class S>
+__device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, const S& sc) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(sc(bf16_lo(w0)), sc(bf16_hi(w0)), 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(sc(bf16_lo(w1)), sc(bf16_hi(w1)), r, true);
   return (uint32_t)r;
 }
 
 // Same for four values given as lo/hi halves of four different words
 // (used where a word holds two columns).
-__device__ __forceinline__ uint32_t quant4_sel(float a, float b, float c, float d, float inv) {
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a * inv, b * inv, 0, false);
-  r = __builtin_amdgcn_cvt_pk_fp8_f32(c * inv, d * inv, r, true);
+template <class S>
+__device__ __forceinline__ uint32_t quant4_sel(float a, float b, float c, float d, const S& sc) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(sc(a), sc(b), 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(sc(c), sc(d), r, true);
   return (uint32_t)r;
 }
 

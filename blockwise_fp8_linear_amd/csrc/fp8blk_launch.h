@@ -10,12 +10,14 @@
 
 namespace fp8blk {
 
+// fp32_scale: the scale rule of FP8BLK_SCALE_FP32 (amax / 448) instead of the
+// power-of-two one.
 hipError_t launch_quant_rowgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
-                                 int64_t ld_q, float* s, hipStream_t stream);
+                                 int64_t ld_q, float* s, bool fp32_scale, hipStream_t stream);
 hipError_t launch_quant_colgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qT,
-                                 int64_t ld_qT, float* sT, hipStream_t stream);
+                                 int64_t ld_qT, float* sT, bool fp32_scale, hipStream_t stream);
 hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
-                             float* s, uint8_t* qT, int64_t ld_qT, float* sT, hipStream_t stream);
+                             float* s, uint8_t* qT, int64_t ld_qT, float* sT, bool fp32_scale, hipStream_t stream);
 // One weight of a batched block quantization.
 struct BlockJob {
   const uint16_t* w;
@@ -25,9 +27,9 @@ struct BlockJob {
   float* s;
 };
 constexpr int kMaxBlockJobs = 8;
-hipError_t launch_quant_block_batch(const BlockJob* job, int n, hipStream_t stream);
+hipError_t launch_quant_block_batch(const BlockJob* job, int n, bool fp32_scale, hipStream_t stream);
 hipError_t launch_quant_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld_w, uint8_t* q, uint8_t* qT,
-                              float* s, hipStream_t stream);
+                              float* s, bool fp32_scale, hipStream_t stream);
 
 // How the B operand's scales are indexed.  A's scales are always per row:
 // sa[i * (R/128) + rb].  B_BLOCK: sb[(j/128) * sb_j + rb * sb_r] (a 128x128

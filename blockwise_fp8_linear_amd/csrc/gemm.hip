@@ -19,8 +19,9 @@
 // conflicts.  One v_mfma_*_16x16x128_f8f6f4 consumes exactly one 128-deep
 // block for a 16x16 sub-tile, so the per-block scale product is applied
 // between blocks:
-//   PROMOTE = true : P = MFMA(A_b, B_b) from zero, then acc += P * (sa*sb)
-//                    on the VALU, in fp32;
+//   PROMOTE = true : P = MFMA(A_b, B_b) from zero, then
+//                    acc = fma(P, fl32(sa*sb), acc) on the VALU, in fp32 --
+//                    any fp32 scales, so it also serves the amax / 448 rule;
 //   PROMOTE = false: the gfx950 block-scaled MFMA, which multiplies each
 //                    operand row by its power-of-two scale (an E8M0 byte:
 //                    the fp32 scale's exponent field) inside the matrix core
@@ -29,8 +30,10 @@
 // that each lane ends up holding 4 consecutive output columns of one row,
 // which makes the scale a single value per lane (per row) for the weight
 // block case and the epilogue a row-contiguous 8- or 16-byte store.
-// Scales of a chunk of up to kChunk reduction blocks are staged in LDS as
-// E8M0 bytes.
+// Scales of a chunk of up to kChunk reduction blocks are staged in LDS, as
+// fp32 values (PROMOTE) or E8M0 bytes (the scaled MFMA).
+#include <type_traits>
+
 #include "fp8blk_device.h"
 #include "fp8blk_launch.h"
 
@@ -50,8 +53,10 @@ struct Cfg {
   static constexpr bool PROMOTE = PROMOTE_, BROW = BROW_;
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int SA_BYTES = kChunk * BM;
-  static constexpr int SB_BYTES = BROW ? kChunk * BN : kChunk * (BN / 128 > 0 ? BN / 128 : 1);
+  // one staged scale: fp32 for PROMOTE, its E8M0 byte for the scaled MFMA
+  using SType = typename std::conditional<PROMOTE_, float, uint8_t>::type;
+  static constexpr int SA_BYTES = kChunk * BM * (int)sizeof(SType);
+  static constexpr int SB_BYTES = (BROW ? kChunk * BN : kChunk * (BN / 128 > 0 ? BN / 128 : 1)) * (int)sizeof(SType);
   static constexpr int LDS = 2 * STAGE + SA_BYTES + ((SB_BYTES + 15) / 16) * 16;
   static constexpr int A_LOADS = A_BYTES / 16 / THREADS;  // 16-byte chunks per thread
   static constexpr int B_LOADS = B_BYTES / 16 / THREADS;
@@ -61,7 +66,13 @@ struct Cfg {
 };
 
 __device__ __forceinline__ uint32_t e8_of(float s) { return (__float_as_uint(s) >> 23) & 0xFFu; }
-__device__ __forceinline__ float f_of_e8(uint32_t e) { return __uint_as_float(e << 23); }
+
+// A scale as staged in LDS by configuration C.
+template <class C>
+__device__ __forceinline__ typename C::SType staged_scale(float s) {
+  if constexpr (C::PROMOTE) return s;
+  else return (uint8_t)e8_of(s);
+}
 
 // Read a 32-byte MFMA fragment: row `row` of a swizzled [rows][128 B] tile,
 // logical 16-byte chunks 2g and 2g+1.
@@ -80,8 +91,9 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
                                                           int64_t kb_per_split) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint8_t* const tiles = lds;
-  uint8_t* const sa_lds = lds + 2 * C::STAGE;
-  uint8_t* const sb_lds = sa_lds + C::SA_BYTES;
+  typedef typename C::SType ST;
+  ST* const sa_lds = reinterpret_cast<ST*>(lds + 2 * C::STAGE);
+  ST* const sb_lds = reinterpret_cast<ST*>(lds + 2 * C::STAGE + C::SA_BYTES);
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -142,7 +154,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
       *reinterpret_cast<u32x4*>(tb + row * 128 + (((c & 7) ^ (row & 7)) << 4)) = rb[u];
     }
   };
-  // ---- scales of reduction blocks [kb0, kb0 + n) -> LDS as E8M0 bytes.
+  // ---- scales of reduction blocks [kb0, kb0 + n) -> LDS (fp32 or E8M0).
   // sa_lds[kbl][i % 16][i / 16]; row-mode B: promote keeps [kbl][j], the
   // scaled MFMA wants [kbl][j % 16][j / 16]; block-mode B: [kbl][j / 128].
   auto load_scales = [&](int64_t kb0, int64_t n) {
@@ -152,7 +164,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
       if (kbl < n) {
         int64_t row = i0 + i;
         row = row < g.I ? row : g.I - 1;
-        sa_lds[kbl * C::BM + (i & 15) * (C::BM / 16) + (i >> 4)] = (uint8_t)e8_of(g.sa[row * nkb_all + kb0 + kbl]);
+        sa_lds[kbl * C::BM + (i & 15) * (C::BM / 16) + (i >> 4)] = staged_scale<C>(g.sa[row * nkb_all + kb0 + kbl]);
       }
     }
     if constexpr (C::BROW) {
@@ -162,7 +174,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
           int64_t row = j0 + j;
           row = row < g.J ? row : g.J - 1;
           const uint32_t pos = C::PROMOTE ? j : (j & 15) * (C::BN / 16) + (j >> 4);
-          sb_lds[kbl * C::BN + pos] = (uint8_t)e8_of(g.sb[row * nkb_all + kb0 + kbl]);
+          sb_lds[kbl * C::BN + pos] = staged_scale<C>(g.sb[row * nkb_all + kb0 + kbl]);
         }
       }
     } else {
@@ -172,7 +184,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
         if (kbl < n) {
           int64_t jblk = (j0 >> 7) + jb;
           jblk = jblk < (g.J >> 7) ? jblk : (g.J >> 7) - 1;
-          sb_lds[kbl * NB + jb] = (uint8_t)e8_of(g.sb[jblk * g.sb_j + (kb0 + kbl) * g.sb_r]);
+          sb_lds[kbl * NB + jb] = staged_scale<C>(g.sb[jblk * g.sb_j + (kb0 + kbl) * g.sb_r]);
         }
       }
     }
@@ -206,11 +218,9 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
 #pragma unroll
     for (int ns = 0; ns < C::TN; ++ns) bf[ns] = read_frag(tb, wn0 + ns * 16 + l16, g4);
 
-    // A-row scales for this lane's rows i = wm0 + ms*16 + l16, as bytes
-    uint32_t saw[(C::TM + 3) / 4];
-#pragma unroll
-    for (int w = 0; w < (C::TM + 3) / 4; ++w)
-      saw[w] = *reinterpret_cast<const uint32_t*>(sa_lds + kbl * C::BM + l16 * (C::BM / 16) + (wm0 >> 4) + 4 * w);
+    // A-row scales of this lane's rows i = wm0 + ms*16 + l16 sit at
+    // sa_lds[kbl][l16][wm0 / 16 + ms]
+    const ST* const sa_row = sa_lds + kbl * C::BM + l16 * (C::BM / 16) + (wm0 >> 4);
 
     if constexpr (C::PROMOTE) {
       // scale of the B side: one value (weight block) or 4 per sub-tile (rows)
@@ -218,17 +228,17 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
       if constexpr (C::BROW) {
 #pragma unroll
         for (int ns = 0; ns < C::TN; ++ns) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(sb_lds + kbl * C::BN + wn0 + ns * 16 + g4 * 4);
+          const v4f w = *reinterpret_cast<const v4f*>(sb_lds + kbl * C::BN + wn0 + ns * 16 + g4 * 4);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) sbv[ns][t] = f_of_e8((w >> (8 * t)) & 0xFF);
+          for (int t = 0; t < 4; ++t) sbv[ns][t] = w[t];
         }
       } else {
-        sbv[0][0] = f_of_e8(sb_lds[kbl * (C::BN / 128) + (wn0 >> 7)]);
+        sbv[0][0] = sb_lds[kbl * (C::BN / 128) + (wn0 >> 7)];
       }
 #pragma unroll
       for (int ms = 0; ms < C::TM; ++ms) {
         const v8i af = read_frag(ta, wm0 + ms * 16 + l16, g4);
-        const float sa = f_of_e8((saw[ms >> 2] >> (8 * (ms & 3))) & 0xFF);
+        const float sa = sa_row[ms];
 #pragma unroll
         for (int ns = 0; ns < C::TN; ++ns) {
           const v4f z = {0.f, 0.f, 0.f, 0.f};
@@ -245,6 +255,9 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
       }
     } else {
       // scaled MFMA: every lane passes the E8M0 byte of its own operand row
+      uint32_t saw[(C::TM + 3) / 4];
+#pragma unroll
+      for (int w = 0; w < (C::TM + 3) / 4; ++w) saw[w] = *reinterpret_cast<const uint32_t*>(sa_row + 4 * w);
       uint32_t sbw[(C::TN + 3) / 4];
       if constexpr (C::BROW) {
 #pragma unroll

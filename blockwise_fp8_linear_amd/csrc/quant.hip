@@ -1,10 +1,13 @@
-// Quantizer kernels for gfx950: bf16 -> E4M3 codes + power-of-two fp32 scales.
+// Quantizer kernels for gfx950: bf16 -> E4M3 codes + fp32 scales.
 //
 // What is computed ("Puro-2B ... part 3/7", section 3.2, second and third
 // paragraphs): one scale per 128 consecutive values along the GEMM reduction
 // dimension for activations and gradients, one per 128x128 block for weights;
-// each scale a power of two.  The scale rule and the cast are the readings
-// stated in include/fp8blk.h.
+// each scale a power of two (Pow2Scale), or, as a numerics variant, the
+// unconstrained fp32 amax / 448 of the DeepSeek-V3 recipe that the same
+// paragraph sets against it (Fp32Scale).  The scale rules and the cast are
+// the readings stated in include/fp8blk.h; every kernel is instantiated for
+// both rules.
 //
 // All three kernels are bound by HBM bandwidth (about 3 bytes moved per
 // element for 0.1 flop), so the design work is in the memory access pattern:
@@ -26,6 +29,7 @@ constexpr int kRowUnroll = 4;
 constexpr int kRowThreads = 256;
 constexpr int kGroupsPerWave = 4 * kRowUnroll;
 
+template <class S>
 __global__ __launch_bounds__(kRowThreads) void quant_rowgroup_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q,
     float* __restrict__ s, uint32_t groups_per_row, uint32_t total_groups) {
@@ -53,14 +57,13 @@ __global__ __launch_bounds__(kRowThreads) void quant_rowgroup_kernel(
     uint32_t m = pk_max_u16(pk_max_u16(abs2(v[u].x), abs2(v[u].y)), pk_max_u16(abs2(v[u].z), abs2(v[u].w)));
     m = max(m & 0xFFFFu, m >> 16);
     m = row16_max(m);
-    int e = scale_exponent(m);
-    float inv = pow2f(-e);
+    const S sc(m);
     uint2 out;
-    out.x = quant4(v[u].x, v[u].y, inv);
-    out.y = quant4(v[u].z, v[u].w, inv);
+    out.x = quant4(v[u].x, v[u].y, sc);
+    out.y = quant4(v[u].z, v[u].w, sc);
     if (g < total_groups) {
       *reinterpret_cast<uint2*>(q + (int64_t)row[u] * ld_q + col[u] * 128 + l16 * 8) = out;
-      if (l16 == 0) s[(int64_t)row[u] * groups_per_row + col[u]] = pow2f(e);
+      if (l16 == 0) s[(int64_t)row[u] * groups_per_row + col[u]] = sc.s;
     }
   }
 }
@@ -81,6 +84,7 @@ constexpr int kColThreads = 256;
 
 __device__ __forceinline__ uint32_t col_swz(uint32_t r) { return ((r >> 4) & 3) << 3; }
 
+template <class S>
 __global__ __launch_bounds__(kColThreads) void quant_colgroup_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ qT, int64_t ld_qT,
     float* __restrict__ sT, uint32_t row_tiles, uint32_t col_tiles) {
@@ -122,9 +126,7 @@ __global__ __launch_bounds__(kColThreads) void quant_colgroup_kernel(
     m = pk_max_u16(m, abs2(w[i]));
   }
   m = lane8_max_pk(m);
-  const int e0 = scale_exponent(m & 0xFFFFu);
-  const int e1 = scale_exponent(m >> 16);
-  const float inv0 = pow2f(-e0), inv1 = pow2f(-e1);
+  const S inv0(m & 0xFFFFu), inv1(m >> 16);
   u32x4 o0, o1;
   o0.x = quant4_sel(bf16_lo(w[0]), bf16_lo(w[1]), bf16_lo(w[2]), bf16_lo(w[3]), inv0);
   o0.y = quant4_sel(bf16_lo(w[4]), bf16_lo(w[5]), bf16_lo(w[6]), bf16_lo(w[7]), inv0);
@@ -139,8 +141,8 @@ __global__ __launch_bounds__(kColThreads) void quant_colgroup_kernel(
   *reinterpret_cast<u32x4*>(qT + (c + 1) * ld_qT + m0 + rp * 16) = o1;
   if (rp == 0) {
     const int64_t G = (int64_t)row_tiles;  // rows / 128 groups per column
-    sT[c * G + rt] = pow2f(e0);
-    sT[(c + 1) * G + rt] = pow2f(e1);
+    sT[c * G + rt] = inv0.s;
+    sT[(c + 1) * G + rt] = inv1.s;
   }
 }
 
@@ -156,6 +158,7 @@ constexpr int kBlkThreads = 256;
 
 // Block `logical` (row-major over the row_blocks x col_blocks blocks) of one
 // weight.
+template <class S>
 __device__ __forceinline__ void quant_block_one(const uint16_t* __restrict__ w, int64_t ld_w, uint8_t* __restrict__ q,
                                                 uint8_t* __restrict__ qT, float* __restrict__ s, int64_t rows,
                                                 int64_t cols, uint32_t col_blocks, uint32_t logical) {
@@ -181,8 +184,7 @@ __device__ __forceinline__ void quant_block_one(const uint16_t* __restrict__ w, 
   if ((t & 63) == 0) red[t >> 6] = m;
   __syncthreads();
   m = max(max(red[0], red[1]), max(red[2], red[3]));
-  const int e = scale_exponent(m);
-  const float inv = pow2f(-e);
+  const S inv(m);
 
   uint32_t lo[8], hi[8];  // codes of row i: columns 0..3 in lo[i], 4..7 in hi[i]
 #pragma unroll
@@ -205,13 +207,14 @@ __device__ __forceinline__ void quant_block_one(const uint16_t* __restrict__ w, 
     for (int c = 0; c < 4; ++c)
       *reinterpret_cast<uint2*>(qT + (cc0 + 4 + c) * rows + r0) = make_uint2(a[c], b[c]);
   }
-  if (t == 0) s[(int64_t)bi * col_blocks + bj] = pow2f(e);
+  if (t == 0) s[(int64_t)bi * col_blocks + bj] = inv.s;
 }
 
+template <class S>
 __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
     const uint16_t* __restrict__ w, int64_t ld_w, uint8_t* __restrict__ q, uint8_t* __restrict__ qT,
     float* __restrict__ s, int64_t rows, int64_t cols, uint32_t row_blocks, uint32_t col_blocks) {
-  quant_block_one(w, ld_w, q, qT, s, rows, cols, col_blocks, xcd_remap(blockIdx.x, row_blocks * col_blocks));
+  quant_block_one<S>(w, ld_w, q, qT, s, rows, cols, col_blocks, xcd_remap(blockIdx.x, row_blocks * col_blocks));
 }
 
 // Several weights in one launch: workgroup b quantizes block b - first[j] of
@@ -222,12 +225,13 @@ struct BlockJobs {
   int n;
 };
 
+template <class S>
 __global__ __launch_bounds__(kBlkThreads) void quant_block_batch_kernel(BlockJobs jobs) {
   int j = 0;
   for (int k = 1; k < jobs.n; ++k)
     if (blockIdx.x >= jobs.first[k]) j = k;
   const BlockJob& b = jobs.job[j];
-  quant_block_one(b.w, b.ld_w, b.q, b.qT, b.s, b.rows, b.cols, (uint32_t)(b.cols / 128), blockIdx.x - jobs.first[j]);
+  quant_block_one<S>(b.w, b.ld_w, b.q, b.qT, b.s, b.rows, b.cols, (uint32_t)(b.cols / 128), blockIdx.x - jobs.first[j]);
 }
 
 // ---------------------------------------------------------------------------
@@ -246,13 +250,15 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_batch_kernel(BlockJob
 // ---------------------------------------------------------------------------
 constexpr int kDualThreads = 256;
 
-// Four codes, each value with its own inverse scale (four columns).
-__device__ __forceinline__ uint32_t quant4_cols(uint32_t w0, uint32_t w1, const float* inv) {
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w0) * inv[0], bf16_hi(w0) * inv[1], 0, false);
-  r = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w1) * inv[2], bf16_hi(w1) * inv[3], r, true);
+// Four codes, each value with its own scale (four columns).
+template <class S>
+__device__ __forceinline__ uint32_t quant4_cols(uint32_t w0, uint32_t w1, const S* sc) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(sc[0](bf16_lo(w0)), sc[1](bf16_hi(w0)), 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(sc[2](bf16_lo(w1)), sc[3](bf16_hi(w1)), r, true);
   return (uint32_t)r;
 }
 
+template <class S>
 __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ s,
     uint8_t* __restrict__ qT, int64_t ld_qT, float* __restrict__ sT, uint32_t row_tiles, uint32_t col_tiles) {
@@ -279,13 +285,12 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     uint32_t m = pk_max_u16(pk_max_u16(abs2(v[i].x), abs2(v[i].y)), pk_max_u16(abs2(v[i].z), abs2(v[i].w)));
     m = max(m & 0xFFFFu, m >> 16);
     m = row16_max(m);
-    const int e = scale_exponent(m);
-    const float inv = pow2f(-e);
+    const S sc(m);
     uint2 o;
-    o.x = quant4(v[i].x, v[i].y, inv);
-    o.y = quant4(v[i].z, v[i].w, inv);
+    o.x = quant4(v[i].x, v[i].y, sc);
+    o.y = quant4(v[i].z, v[i].w, sc);
     *reinterpret_cast<uint2*>(q + (r0 + i) * ld_q + c0 + cb * 8) = o;
-    if (cb == 0) s[(r0 + i) * G + ct] = pow2f(e);
+    if (cb == 0) s[(r0 + i) * G + ct] = sc.s;
   }
 
   // ---- column groups: packed (two columns per word) max over the 128 rows
@@ -310,14 +315,9 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
 #pragma unroll
   for (int w = 0; w < 4; ++w)
     cm[w] = pk_max_u16(pk_max_u16(red[0][cb][w], red[1][cb][w]), pk_max_u16(red[2][cb][w], red[3][cb][w]));
-  float inv[8];
-  int ec[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t a = (j & 1) ? (cm[j >> 1] >> 16) : (cm[j >> 1] & 0xFFFFu);
-    ec[j] = scale_exponent(a);
-    inv[j] = pow2f(-ec[j]);
-  }
+  // column j's amax is half j % 2 of cm[j / 2]
+  const S inv[8] = {S(cm[0] & 0xFFFFu), S(cm[0] >> 16), S(cm[1] & 0xFFFFu), S(cm[1] >> 16),
+                    S(cm[2] & 0xFFFFu), S(cm[2] >> 16), S(cm[3] & 0xFFFFu), S(cm[3] >> 16)};
   // codes of row i, columns 0..3 in lo[i] and 4..7 in hi[i], each column with its own scale
   uint32_t lo[8], hi[8];
 #pragma unroll
@@ -337,33 +337,41 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
   for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2*>(qT + (cc + 4 + j) * ld_qT + r0) = make_uint2(ta[j], tb[j]);
   if (rb == 0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sT[(cc + j) * row_tiles + rt] = pow2f(ec[j]);
+    for (int j = 0; j < 8; ++j) sT[(cc + j) * row_tiles + rt] = inv[j].s;
   }
 }
 
 // ------------------------------------------------------------- launchers ---
 
 hipError_t launch_quant_rowgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
-                                 int64_t ld_q, float* s, hipStream_t stream) {
+                                 int64_t ld_q, float* s, bool fp32_scale, hipStream_t stream) {
   const uint32_t gpr = (uint32_t)(cols / 128);
   const uint32_t total = (uint32_t)(rows * gpr);
   const uint32_t waves = (total + kGroupsPerWave - 1) / kGroupsPerWave;
   const uint32_t blocks = (waves + (kRowThreads / 64) - 1) / (kRowThreads / 64);
-  hipLaunchKernelGGL(quant_rowgroup_kernel, dim3(blocks), dim3(kRowThreads), 0, stream, x, ld_x, q, ld_q, s, gpr,
-                     total);
+  if (fp32_scale)
+    hipLaunchKernelGGL(quant_rowgroup_kernel<Fp32Scale>, dim3(blocks), dim3(kRowThreads), 0, stream, x, ld_x, q, ld_q,
+                       s, gpr, total);
+  else
+    hipLaunchKernelGGL(quant_rowgroup_kernel<Pow2Scale>, dim3(blocks), dim3(kRowThreads), 0, stream, x, ld_x, q, ld_q,
+                       s, gpr, total);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_colgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qT,
-                                 int64_t ld_qT, float* sT, hipStream_t stream) {
+                                 int64_t ld_qT, float* sT, bool fp32_scale, hipStream_t stream) {
   const uint32_t rt = (uint32_t)(rows / kColTileRows);
   const uint32_t ct = (uint32_t)(cols / kColTileCols);
-  hipLaunchKernelGGL(quant_colgroup_kernel, dim3(rt * ct), dim3(kColThreads), 0, stream, x, ld_x, qT, ld_qT, sT, rt,
-                     ct);
+  if (fp32_scale)
+    hipLaunchKernelGGL(quant_colgroup_kernel<Fp32Scale>, dim3(rt * ct), dim3(kColThreads), 0, stream, x, ld_x, qT,
+                       ld_qT, sT, rt, ct);
+  else
+    hipLaunchKernelGGL(quant_colgroup_kernel<Pow2Scale>, dim3(rt * ct), dim3(kColThreads), 0, stream, x, ld_x, qT,
+                       ld_qT, sT, rt, ct);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_block_batch(const BlockJob* job, int n, hipStream_t stream) {
+hipError_t launch_quant_block_batch(const BlockJob* job, int n, bool fp32_scale, hipStream_t stream) {
   BlockJobs jobs{};
   uint32_t total = 0;
   for (int k = 0; k < n; ++k) {
@@ -372,25 +380,36 @@ hipError_t launch_quant_block_batch(const BlockJob* job, int n, hipStream_t stre
     total += (uint32_t)((job[k].rows / 128) * (job[k].cols / 128));
   }
   jobs.n = n;
-  hipLaunchKernelGGL(quant_block_batch_kernel, dim3(total), dim3(kBlkThreads), 0, stream, jobs);
+  if (fp32_scale)
+    hipLaunchKernelGGL(quant_block_batch_kernel<Fp32Scale>, dim3(total), dim3(kBlkThreads), 0, stream, jobs);
+  else
+    hipLaunchKernelGGL(quant_block_batch_kernel<Pow2Scale>, dim3(total), dim3(kBlkThreads), 0, stream, jobs);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld_w, uint8_t* q, uint8_t* qT,
-                              float* s, hipStream_t stream) {
+                              float* s, bool fp32_scale, hipStream_t stream) {
   const uint32_t rb = (uint32_t)(rows / 128);
   const uint32_t cb = (uint32_t)(cols / 128);
-  hipLaunchKernelGGL(quant_block_kernel, dim3(rb * cb), dim3(kBlkThreads), 0, stream, w, ld_w, q, qT, s, rows, cols,
-                     rb, cb);
+  if (fp32_scale)
+    hipLaunchKernelGGL(quant_block_kernel<Fp32Scale>, dim3(rb * cb), dim3(kBlkThreads), 0, stream, w, ld_w, q, qT, s,
+                       rows, cols, rb, cb);
+  else
+    hipLaunchKernelGGL(quant_block_kernel<Pow2Scale>, dim3(rb * cb), dim3(kBlkThreads), 0, stream, w, ld_w, q, qT, s,
+                       rows, cols, rb, cb);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
-                             float* s, uint8_t* qT, int64_t ld_qT, float* sT, hipStream_t stream) {
+                             float* s, uint8_t* qT, int64_t ld_qT, float* sT, bool fp32_scale, hipStream_t stream) {
   const uint32_t rt = (uint32_t)(rows / 128);
   const uint32_t ct = (uint32_t)(cols / 128);
-  hipLaunchKernelGGL(quant_dual_kernel, dim3(rt * ct), dim3(kDualThreads), 0, stream, x, ld_x, q, ld_q, s, qT, ld_qT,
-                     sT, rt, ct);
+  if (fp32_scale)
+    hipLaunchKernelGGL(quant_dual_kernel<Fp32Scale>, dim3(rt * ct), dim3(kDualThreads), 0, stream, x, ld_x, q, ld_q, s,
+                       qT, ld_qT, sT, rt, ct);
+  else
+    hipLaunchKernelGGL(quant_dual_kernel<Pow2Scale>, dim3(rt * ct), dim3(kDualThreads), 0, stream, x, ld_x, q, ld_q, s,
+                       qT, ld_qT, sT, rt, ct);
   return hipGetLastError();
 }
 

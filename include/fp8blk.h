@@ -27,6 +27,13 @@
  *     multiplier (x ~ decode(q) * s) and is stored as fp32.
  *   - q = round-to-nearest-even(x / s) to E4M3, saturating at +-448 (under
  *     the rule above |x / s| never exceeds 448); the sign of zero is kept.
+ *   - FP8BLK_SCALE_FP32, a numerics variant: the third paragraph of section
+ *     3.2 sets the power-of-two scale of the run against the DeepSeek-V3
+ *     recipe it otherwise follows, whose formula the pages do not print.  Its
+ *     plainest reading: s = fl32(amax / 448) (IEEE division, so the group's
+ *     largest magnitude lands on 448), s = 1 for an all-zero group, and
+ *     q = round-to-nearest-even(fl32(x / s)) to E4M3, saturating at +-448
+ *     (the rounded quotient of the amax itself can exceed 448 by an ulp).
  *   - out[i][j] = sum over 128-deep reduction blocks b of
  *       sa(i, b) * sb(j, b) * sum_{r in b} dec(A[i][r]) * dec(B[j][r]),
  *     accumulated in fp32, rounded to bf16 (RNE) or returned as fp32.
@@ -44,9 +51,12 @@
  *   - Return value: FP8BLK_OK (0), or a negative FP8BLK_ERR_* code.  All
  *     argument checks run on the host before any launch: on an error nothing
  *     is enqueued and no output is touched.  No C++ exception crosses the ABI.
- *   - Scales handed to the GEMMs must be exact powers of two in
- *     [2^-126, 2^127], as the quantizers produce; the GEMMs use only their
- *     exponent bits.
+ *   - Scales handed to the GEMMs with FP8BLK_ALGO_DEFAULT or
+ *     FP8BLK_ALGO_SCALED_MFMA (and to the named GEMM functions, which use
+ *     DEFAULT) must be exact powers of two in [2^-126, 2^127], as the
+ *     FP8BLK_SCALE_POW2 quantizers produce: those paths use only their
+ *     exponent bits.  FP8BLK_ALGO_PROMOTE takes any positive finite fp32
+ *     scales; FP8BLK_SCALE_FP32 operands need it.
  */
 #ifndef FP8BLK_H
 #define FP8BLK_H
@@ -60,8 +70,9 @@
 extern "C" {
 #endif
 
-/* Scale rule.  Only the power-of-two rule is implemented. */
-enum fp8blk_scale_mode { FP8BLK_SCALE_POW2 = 0 };
+/* Scale rule of the quantizers (the readings above): POW2, the pages' rule,
+ * or FP32, s = amax / 448 unconstrained (GEMMs with FP8BLK_ALGO_PROMOTE only). */
+enum fp8blk_scale_mode { FP8BLK_SCALE_POW2 = 0, FP8BLK_SCALE_FP32 = 1 };
 
 /* GEMM output element type.  FP32_ACCUM: fp32 output that the result is
  * added to (out = fl32(out + result)), for gradients accumulated in fp32 over
@@ -76,12 +87,14 @@ enum fp8blk_op { FP8BLK_OP_FPROP = 0, FP8BLK_OP_DGRAD = 1, FP8BLK_OP_WGRAD = 2, 
 
 /* How the per-block scale product reaches the fp32 accumulators.
  *   PROMOTE:     one MFMA per 128-deep reduction block starting from zero,
- *                then acc += P * (sa * sb) on the vector ALU;
+ *                then acc = fma(P, fl32(sa * sb), acc) on the vector ALU;
+ *                takes any fp32 scales;
  *   SCALED_MFMA: gfx950's block-scaled MFMA multiplies each operand row by
  *                its power-of-two scale (E8M0) inside the matrix core and
- *                accumulates in place.
- * Both compute the same sum of exactly scaled block products in fp32; they
- * differ only in rounding order.  DEFAULT picks the faster one. */
+ *                accumulates in place; power-of-two scales only.
+ * With power-of-two scales both compute the same sum of exactly scaled block
+ * products in fp32; they differ only in rounding order.  DEFAULT picks the
+ * faster one (SCALED_MFMA). */
 enum fp8blk_gemm_algo { FP8BLK_ALGO_DEFAULT = 0, FP8BLK_ALGO_PROMOTE = 1, FP8BLK_ALGO_SCALED_MFMA = 2 };
 
 /* Status codes. */
@@ -97,6 +110,9 @@ enum fp8blk_status {
 };
 
 /*
+ * Every quantizer takes scale_mode = FP8BLK_SCALE_POW2 or FP8BLK_SCALE_FP32
+ * (anything else: FP8BLK_ERR_ARG); the two differ only in the scale rule.
+ *
  * Row-group quantization (section 3.2, second paragraph: groups of 128 along
  * the reduction dimension).  Used for X before Fprop and for dY before Dgrad.
  *   x    [rows][cols] bf16, row stride ld_x (>= cols, multiple of 8)

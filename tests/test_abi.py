@@ -40,7 +40,9 @@ def test_status_strings(lib):
 
 def test_rowgroup_errors(lib):
     f = lib.fp8_quantize_rowgroup
-    assert f(P, 4, 256, 256, P2, 256, P3, 1, None) == EARG      # scale mode
+    assert f(P, 4, 256, 256, P2, 256, P3, 2, None) == EARG      # scale mode (0 and 1 are valid)
+    assert f(P, 4, 256, 256, P2, 256, P3, -1, None) == EARG
+    assert f(P, 4, 256, 256, P2, 256, P3, 1, None) in (EHIP, EDEV)   # amax / 448 scales: valid
     assert f(None, 4, 256, 256, P2, 256, P3, 0, None) == ENULL
     assert f(P, 4, 256, 256, None, 256, P3, 0, None) == ENULL
     assert f(P, 4, 256, 256, P2, 256, None, 0, None) == ENULL
@@ -80,7 +82,8 @@ def test_dual_errors(lib):
         a = dict(zip(names, ok))
         a.update(kw)
         return f(*[a[n] for n in names])
-    assert call(mode=1) == EARG
+    assert call(mode=2) == EARG
+    assert call(mode=1) in (EHIP, EDEV)
     for n in ("x", "q", "s", "qT", "sT"):
         assert call(**{n: None}) == ENULL, n
     assert call(rows=200) == EDIM                                 # both dims multiples of 128
@@ -104,7 +107,8 @@ def test_block_batch_errors(lib):
     assert lib.fp8_quantize_block_batch(None, 1, 0, None) == ENULL
     assert lib.fp8_quantize_block_batch(arr(good), 0, 0, None) == EARG
     assert lib.fp8_quantize_block_batch(arr(good * 5), 9, 0, None) == EARG        # at most 8 jobs
-    assert lib.fp8_quantize_block_batch(arr(good), 2, 1, None) == EARG            # scale mode
+    assert lib.fp8_quantize_block_batch(arr(good), 2, 2, None) == EARG            # scale mode
+    assert lib.fp8_quantize_block_batch(arr(good), 2, 1, None) in (EHIP, EDEV)
     bad = [good[0], J(P, 256, 300, 384, P2, None, P3)]
     assert lib.fp8_quantize_block_batch(arr(bad), 2, 0, None) == EDIM             # second job's shape
     bad = [good[0], J(P, 256, 384, 384, None, None, P3)]

@@ -49,26 +49,27 @@ def varied(shape, std, key):
 
 
 class Layer:
-    """One linear's operands, quantized on the GPU and by the oracle."""
+    """One linear's operands, quantized on the GPU and by the oracle, under
+    scale rule `mode` (0 power of two, 1 amax / 448)."""
 
-    def __init__(self, x, w, dy):
+    def __init__(self, x, w, dy, mode=0):
         import torch
         self.M, self.K = x.shape
         self.N = w.shape[0]
         xt, wt, dyt = dev_bf16(x), dev_bf16(w), dev_bf16(dy)
         self.g = {}
-        self.g["qx"], self.g["sx"] = fb.fp8_quantize_rowgroup(xt)
-        self.g["qxT"], self.g["sxT"] = fb.fp8_quantize_colgroup(xt)
-        self.g["qw"], self.g["qwT"], self.g["sw"] = fb.fp8_quantize_block(wt)
-        self.g["qdy"], self.g["sdy"] = fb.fp8_quantize_rowgroup(dyt)
-        self.g["qdyT"], self.g["sdyT"] = fb.fp8_quantize_colgroup(dyt)
+        self.g["qx"], self.g["sx"] = fb.fp8_quantize_rowgroup(xt, scale_mode=mode)
+        self.g["qxT"], self.g["sxT"] = fb.fp8_quantize_colgroup(xt, scale_mode=mode)
+        self.g["qw"], self.g["qwT"], self.g["sw"] = fb.fp8_quantize_block(wt, scale_mode=mode)
+        self.g["qdy"], self.g["sdy"] = fb.fp8_quantize_rowgroup(dyt, scale_mode=mode)
+        self.g["qdyT"], self.g["sdyT"] = fb.fp8_quantize_colgroup(dyt, scale_mode=mode)
         torch.cuda.synchronize()
         self.o = {}
-        self.o["qx"], self.o["sx"] = oracle.quantize_rowgroup(x)
-        self.o["qxT"], self.o["sxT"] = oracle.quantize_colgroup(x)
-        self.o["qw"], _, self.o["sw"] = oracle.quantize_block(w, transpose=False)
-        self.o["qdy"], self.o["sdy"] = oracle.quantize_rowgroup(dy)
-        self.o["qdyT"], self.o["sdyT"] = oracle.quantize_colgroup(dy)
+        self.o["qx"], self.o["sx"] = oracle.quantize_rowgroup(x, mode=mode)
+        self.o["qxT"], self.o["sxT"] = oracle.quantize_colgroup(x, mode=mode)
+        self.o["qw"], _, self.o["sw"] = oracle.quantize_block(w, transpose=False, mode=mode)
+        self.o["qdy"], self.o["sdy"] = oracle.quantize_rowgroup(dy, mode=mode)
+        self.o["qdyT"], self.o["sdyT"] = oracle.quantize_colgroup(dy, mode=mode)
 
     def gpu(self, op, algo, out_dtype):
         g = self.g
@@ -210,6 +211,32 @@ def test_decoder_layer_full_size(li):
         rows = _sample_rows(layer.out_rows(op), (64, li, OPS.index(op)), k=8)
         for algo in ALGOS:
             check_op(layer, op, algo, rows=rows, what=f"layer {lin['name']}")
+
+
+# ---- scales by the amax / 448 rule (FP8BLK_SCALE_FP32): not powers of two,
+# so only the promote algorithm takes them; the same tolerance bar.
+
+@pytest.mark.parametrize("shape", [(384, 640, 512), (640, 384, 1024), (1024, 512, 384), (256, 128, 640),
+                                   (640, 256, 1152)])
+def test_fp32_scales_promote_small_shapes(shape):
+    M, N, K = shape
+    key = (66, M, N, K)
+    layer = Layer(varied((M, K), 1.0, key + (0,)), varied((N, K), 0.02, key + (1,)),
+                  varied((M, N), 1e-3, key + (2,)), mode=1)
+    assert not np.all(np.frexp(oracle.quantize_rowgroup(varied((M, K), 1.0, key + (0,)), mode=1)[1])[0] == 0.5)
+    for op in OPS:
+        check_op(layer, op, "promote", what="fp32 scales")
+
+
+@pytest.mark.parametrize("li", [0, 3])
+def test_fp32_scales_promote_decoder_layer_full_size(li):
+    """QKV and down-projection linears at 8192 tokens with amax / 448 scales:
+    fprop, dgrad and wgrad (split-K) on sampled output rows."""
+    lin = synth.decoder_layer(linears=(synth.LAYER_LINEARS[li],))[0]
+    layer = Layer(lin["x"], lin["w"], lin["dy"], mode=1)
+    for op in OPS:
+        rows = _sample_rows(layer.out_rows(op), (67, li, OPS.index(op)), k=8)
+        check_op(layer, op, "promote", rows=rows, what=f"fp32 scales, layer {lin['name']}")
 
 
 def test_named_entry_points_and_determinism():

@@ -19,21 +19,21 @@ def _gpu():
     require_gpu()
 
 
-def _rowgroup(x_bits, cols=None):
+def _rowgroup(x_bits, cols=None, mode=0):
     import torch
     import blockwise_fp8_linear_amd as fb
     xt = dev_bf16(x_bits)
     if cols is not None:
         xt = xt[:, :cols]
-    q, s = fb.fp8_quantize_rowgroup(xt)
+    q, s = fb.fp8_quantize_rowgroup(xt, scale_mode=mode)
     torch.cuda.synchronize()
     return host(q), host(s)
 
 
-def _assert_rowgroup(x_bits, what, cols=None):
-    note(f"rowgroup {what} {x_bits.shape} cols={cols}")
-    q, s = _rowgroup(x_bits, cols)
-    q0, s0 = oracle.quantize_rowgroup(x_bits, cols=cols)
+def _assert_rowgroup(x_bits, what, cols=None, mode=0):
+    note(f"rowgroup {what} {x_bits.shape} cols={cols} mode={mode}")
+    q, s = _rowgroup(x_bits, cols, mode)
+    q0, s0 = oracle.quantize_rowgroup(x_bits, cols=cols, mode=mode)
     assert np.array_equal(s, s0), f"{what}: scales differ ({int((s != s0).sum())})"
     assert np.array_equal(q, q0), f"{what}: codes differ ({int((q != q0).sum())})"
 
@@ -108,18 +108,18 @@ def test_rowgroup_edge_groups():
     _assert_rowgroup(x, "edge groups")
 
 
-def _colgroup(x_bits):
+def _colgroup(x_bits, mode=0):
     import torch
     import blockwise_fp8_linear_amd as fb
-    qT, sT = fb.fp8_quantize_colgroup(dev_bf16(x_bits))
+    qT, sT = fb.fp8_quantize_colgroup(dev_bf16(x_bits), scale_mode=mode)
     torch.cuda.synchronize()
     return host(qT), host(sT)
 
 
-def _assert_colgroup(x_bits, what):
-    note(f"colgroup {what} {x_bits.shape}")
-    qT, sT = _colgroup(x_bits)
-    q0, s0 = oracle.quantize_colgroup(x_bits)
+def _assert_colgroup(x_bits, what, mode=0):
+    note(f"colgroup {what} {x_bits.shape} mode={mode}")
+    qT, sT = _colgroup(x_bits, mode)
+    q0, s0 = oracle.quantize_colgroup(x_bits, mode=mode)
     assert np.array_equal(sT, s0), f"{what}: scales differ ({int((sT != s0).sum())})"
     assert np.array_equal(qT, q0), f"{what}: codes differ ({int((qT != q0).sum())})"
 
@@ -148,13 +148,13 @@ def test_colgroup_strided_input():
     assert np.array_equal(host(qT), q0) and np.array_equal(host(sT), s0)
 
 
-def _assert_block(w_bits, what, transpose=True):
+def _assert_block(w_bits, what, transpose=True, mode=0):
     import torch
     import blockwise_fp8_linear_amd as fb
-    note(f"block {what} {w_bits.shape} transpose={transpose}")
-    q, qT, s = fb.fp8_quantize_block(dev_bf16(w_bits), transpose=transpose)
+    note(f"block {what} {w_bits.shape} transpose={transpose} mode={mode}")
+    q, qT, s = fb.fp8_quantize_block(dev_bf16(w_bits), transpose=transpose, scale_mode=mode)
     torch.cuda.synchronize()
-    q0, qT0, s0 = oracle.quantize_block(w_bits, transpose=transpose)
+    q0, qT0, s0 = oracle.quantize_block(w_bits, transpose=transpose, mode=mode)
     assert np.array_equal(host(s), s0), f"{what}: scales differ"
     assert np.array_equal(host(q), q0), f"{what}: codes differ"
     if transpose:
@@ -181,23 +181,23 @@ def test_block_decoder_layer():
         _assert_block(lin["w"], f"W {lin['name']}")
 
 
-def _assert_dual(x_bits, what, cols=None, pad_q=0, pad_qT=0):
+def _assert_dual(x_bits, what, cols=None, pad_q=0, pad_qT=0, mode=0):
     """The one-pass quantizer against the oracle's row-group and column-group
     quantizers, bit for bit; optional strided input and padded outputs (the
     padding must stay untouched)."""
     import torch
     import blockwise_fp8_linear_amd as fb
-    note(f"dual {what} {x_bits.shape} cols={cols} pad={pad_q},{pad_qT}")
+    note(f"dual {what} {x_bits.shape} cols={cols} pad={pad_q},{pad_qT} mode={mode}")
     xt = dev_bf16(x_bits)
     if cols is not None:
         xt = xt[:, :cols]
     rows, c = xt.shape
     qbuf = torch.full((rows, c + pad_q), 0xAB, dtype=torch.uint8, device="cuda")
     qTbuf = torch.full((c, rows + pad_qT), 0xCD, dtype=torch.uint8, device="cuda")
-    q, s, qT, sT = fb.fp8_quantize_dual(xt, q=qbuf[:, :c], qT=qTbuf[:, :rows])
+    q, s, qT, sT = fb.fp8_quantize_dual(xt, q=qbuf[:, :c], qT=qTbuf[:, :rows], scale_mode=mode)
     torch.cuda.synchronize()
-    q0, s0 = oracle.quantize_rowgroup(x_bits, cols=cols)
-    qT0, sT0 = oracle.quantize_colgroup(x_bits, cols=cols)
+    q0, s0 = oracle.quantize_rowgroup(x_bits, cols=cols, mode=mode)
+    qT0, sT0 = oracle.quantize_colgroup(x_bits, cols=cols, mode=mode)
     qh, qTh = host(qbuf), host(qTbuf)
     assert np.array_equal(host(s), s0), f"{what}: row scales differ ({int((host(s) != s0).sum())})"
     assert np.array_equal(qh[:, :c], q0), f"{what}: row codes differ ({int((qh[:, :c] != q0).sum())})"
@@ -258,10 +258,11 @@ def test_dual_outlier_stress():
     _assert_dual(x, "outlier X")
 
 
-def test_block_batch_equals_single():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_block_batch_equals_single(mode):
     """The batched block quantizer on the decoder layer's four weights (plus
     an edge-case weight without the transposed copy): each result bit-equal
-    to the oracle."""
+    to the oracle, under both scale rules."""
     import torch
     import blockwise_fp8_linear_amd as fb
     ws = [lin["w"] for lin in synth.decoder_layer()]
@@ -269,12 +270,13 @@ def test_block_batch_equals_single():
     e[128:256, 128:256] = 0
     e[:128, :128] = np.arange(128 * 128, dtype=np.uint16).reshape(128, 128) % 128
     ws.append(e)
-    note(f"block batch {[w.shape for w in ws]}")
+    note(f"block batch {[w.shape for w in ws]} mode={mode}")
     dev = [dev_bf16(w) for w in ws]
-    res = fb.fp8_quantize_block_batch(dev[:4]) + fb.fp8_quantize_block_batch(dev[4:], transpose=False)
+    res = (fb.fp8_quantize_block_batch(dev[:4], scale_mode=mode) +
+           fb.fp8_quantize_block_batch(dev[4:], transpose=False, scale_mode=mode))
     torch.cuda.synchronize()
     for k, (w, (q, qT, s)) in enumerate(zip(ws, res)):
-        q0, qT0, s0 = oracle.quantize_block(w, transpose=qT is not None)
+        q0, qT0, s0 = oracle.quantize_block(w, transpose=qT is not None, mode=mode)
         assert np.array_equal(host(s), s0), f"job {k}: scales differ"
         assert np.array_equal(host(q), q0), f"job {k}: codes differ"
         if qT is not None:
@@ -293,3 +295,84 @@ def test_quantizers_repeatable():
     for u, v in zip(a, b):
         for s, t in zip(u, v):
             assert torch.equal(s, t)
+
+
+# ---------------------------------------------------------------------------
+# The amax / 448 scale rule (FP8BLK_SCALE_FP32, oracle mode 1): the same
+# bit-exact bar.  Its scales are not powers of two, so every quotient x / s
+# is a rounded IEEE division on both sides.
+
+FP32 = 1
+
+
+def _division_sweep():
+    """Groups whose amax is a * 2^e for a few non-power-of-two mantissas a
+    (so s = a * 2^e / 448 is inexact), the other 127 elements sweeping every
+    bf16 magnitude up to a, and its negative, scaled alike; e across the
+    exponent range, down to bf16 subnormal groups."""
+    mags_all = (np.arange(0x8000, dtype=np.uint32) << 16).view(np.float32)
+    blocks = []
+    for a in (1.0, 1.375, 3.0, 300.0):
+        mags = mags_all[np.isfinite(mags_all) & (mags_all <= a)]
+        vals = np.concatenate([mags, -mags]).astype(np.float32)
+        per = 127
+        ng = (vals.size + per - 1) // per
+        vals = np.concatenate([vals, np.zeros(ng * per - vals.size, np.float32)]).reshape(ng, per)
+        for e in (-140, -128, -100, -37, -9, 0, 7, 50, 110):
+            blk = np.empty((ng, 128), np.float32)
+            blk[:, 0] = np.float32(a) * np.float32(2.0 ** e)
+            blk[:, 1:] = vals * np.float32(2.0 ** e)
+            blocks.append(blk)
+    x = np.concatenate(blocks)
+    x = np.concatenate([x, np.zeros(((-x.shape[0]) % 128, 128), np.float32)])
+    return synth.bf16_bits_from_f32(x)
+
+
+def test_fp32_scale_rowgroup_edges_and_ragged():
+    x = synth.normal_bf16((256, 1024), 1.0, 42, 0)
+    x[3, 128:256] = 0                                            # all +0
+    x[4, :128] = 0x8000                                          # all -0
+    x[5, 256:384] = np.arange(128, dtype=np.uint16)              # bf16 subnormals
+    x[6, 384:512] = (np.arange(128, dtype=np.uint16) | 0x8000)   # negative subnormals
+    x[7, :128] = synth.bf16_bits_from_f32(np.full(128, 3.0e38, np.float32))   # near bf16 max
+    x[8, :128] = synth.bf16_bits_from_f32(np.linspace(-1e-30, 1e-30, 128).astype(np.float32))
+    x[9, :128] = 1                                               # the smallest subnormal everywhere
+    _assert_rowgroup(x, "edge groups", mode=FP32)
+    for rows in (1, 3, 17, 257):
+        _assert_rowgroup(synth.normal_bf16((rows, 384), 1.0, 40, rows), f"ragged rows={rows}", mode=FP32)
+
+
+def test_fp32_scale_division_sweep_all_orientations():
+    x = _division_sweep()
+    _assert_rowgroup(x, "division sweep", mode=FP32)
+    _assert_dual(x, "division sweep, row side", mode=FP32)
+    xt = np.ascontiguousarray(x.T)
+    _assert_dual(xt, "division sweep, column side", mode=FP32)
+    _assert_colgroup(xt[:, :4096], "division sweep, colgroup", mode=FP32)
+
+
+def test_fp32_scale_decoder_layer_dual_and_colgroup():
+    for lin in synth.decoder_layer():
+        _assert_dual(lin["x"], f"X {lin['name']}", mode=FP32)
+        _assert_dual(lin["dy"], f"dY {lin['name']}", mode=FP32)
+    lin = synth.decoder_layer()[0]
+    _assert_colgroup(lin["x"], "X qkv", mode=FP32)
+
+
+def test_fp32_scale_outlier_stress_and_strided():
+    x, _, _ = synth.outlier_stress()
+    _assert_rowgroup(x, "outlier X", mode=FP32)
+    _assert_dual(x, "outlier X", mode=FP32)
+    wide = synth.normal_bf16((1024, 4096), 1.0, 48, 0)
+    _assert_dual(wide, "column slice, padded outputs", cols=2048, pad_q=256, pad_qT=128, mode=FP32)
+
+
+def test_fp32_scale_block():
+    w = synth.normal_bf16((384, 256), 0.02, 45, 0)
+    w[128:256, 128:256] = 0
+    w[:128, :128] = np.arange(128 * 128, dtype=np.uint16).reshape(128, 128) % 128   # subnormal block
+    _assert_block(w, "edges", mode=FP32)
+    _assert_block(w, "edges, no transpose", transpose=False, mode=FP32)
+    _, w = synth.single_linear()
+    _assert_block(w, "12288x2048 W", mode=FP32)
+
