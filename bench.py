@@ -89,6 +89,9 @@ def parse():
                     help="untimed steps before the timed ones (at least 1: the first also counts the launches)")
     ap.add_argument("--workload", choices=("layer", "linear", "stack28"), default="layer")
     ap.add_argument("--algo", choices=("default", "promote", "scaled"), default="default")
+    ap.add_argument("--scale", choices=("pow2", "fp32"), default="pow2",
+                    help="scale rule of every quantizer: power of two (the pages' run) or amax / 448 "
+                         "(FP8BLK_SCALE_FP32, which the GEMMs take only through the promote algorithm)")
     ap.add_argument("--separate-quant", action="store_true",
                     help="quantize X and dY with the separate row-group and column-group kernels "
                          "instead of the one-pass kernel")
@@ -193,15 +196,20 @@ DUAL = True
 FUSED_BWD = True
 # True: a layer's four weights quantized in one launch; False: one launch each.
 BATCH_W = True
+# Scale rule of every quantizer call (FP8BLK_SCALE_POW2 or FP8BLK_SCALE_FP32).
+SCALE_MODE = 0
 
 
 def quantize_both(fb, T, x, q, s, qT, sT):
     rows, cols = x.shape
     if DUAL:
-        T.run("quant_dual", 0, dual_bytes(rows, cols), lambda: fb.fp8_quantize_dual(x, q=q, s=s, qT=qT, sT=sT))
+        T.run("quant_dual", 0, dual_bytes(rows, cols),
+              lambda: fb.fp8_quantize_dual(x, q=q, s=s, qT=qT, sT=sT, scale_mode=SCALE_MODE))
     else:
-        T.run("quant_rowgroup", 0, qbytes(rows, cols), lambda: fb.fp8_quantize_rowgroup(x, q=q, s=s))
-        T.run("quant_colgroup", 0, qbytes(rows, cols), lambda: fb.fp8_quantize_colgroup(x, qT=qT, sT=sT))
+        T.run("quant_rowgroup", 0, qbytes(rows, cols),
+              lambda: fb.fp8_quantize_rowgroup(x, q=q, s=s, scale_mode=SCALE_MODE))
+        T.run("quant_colgroup", 0, qbytes(rows, cols),
+              lambda: fb.fp8_quantize_colgroup(x, qT=qT, sT=sT, scale_mode=SCALE_MODE))
 
 
 def quantize_weights(fb, T, L):
@@ -210,12 +218,13 @@ def quantize_weights(fb, T, L):
     if BATCH_W:
         nbytes = sum(d["N"] * d["K"] * 4 + (d["N"] // 128) * (d["K"] // 128) * 4 for d in L)
         T.run("quant_block_batch", 0, nbytes,
-              lambda: fb.fp8_quantize_block_batch([d["w"] for d in L], outs=[(d["qw"], d["qwT"], d["sw"]) for d in L]))
+              lambda: fb.fp8_quantize_block_batch([d["w"] for d in L], outs=[(d["qw"], d["qwT"], d["sw"]) for d in L],
+                                                  scale_mode=SCALE_MODE))
     else:
         for d in L:
             n, k = d["N"], d["K"]
             T.run("quant_block", 0, n * k * 4 + (n // 128) * (k // 128) * 4,
-                  lambda d=d: fb.fp8_quantize_block(d["w"], q=d["qw"], qT=d["qwT"], s=d["sw"]))
+                  lambda d=d: fb.fp8_quantize_block(d["w"], q=d["qw"], qT=d["qwT"], s=d["sw"], scale_mode=SCALE_MODE))
 
 
 def fwd_linear(fb, T, d, algo, x=None):
@@ -254,9 +263,10 @@ def layer_step(fb, T, L, algo):
 
 def linear_step(fb, T, d, algo):
     n, k = d["N"], d["K"]
-    T.run("quant_rowgroup", 0, qbytes(TOKENS, k), lambda: fb.fp8_quantize_rowgroup(d["x"], q=d["qx"], s=d["sx"]))
+    T.run("quant_rowgroup", 0, qbytes(TOKENS, k),
+          lambda: fb.fp8_quantize_rowgroup(d["x"], q=d["qx"], s=d["sx"], scale_mode=SCALE_MODE))
     T.run("quant_block", 0, n * k * 3 + (n // 128) * (k // 128) * 4,
-          lambda: fb.fp8_quantize_block(d["w"], transpose=False, q=d["qw"], s=d["sw"]))
+          lambda: fb.fp8_quantize_block(d["w"], transpose=False, q=d["qw"], s=d["sw"], scale_mode=SCALE_MODE))
     T.run("gemm_fprop", 2.0 * TOKENS * n * k, 0,
           lambda: fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, d["qx"], d["sx"], d["qw"], d["sw"], TOKENS, n, k,
                                     algo=algo, out=d["y"]))
@@ -355,7 +365,7 @@ def onbox_ceilings(torch):
                     "and a 1 GiB device copy (read + write bytes)"}
 
 
-def cpu_baseline(budget_s):
+def cpu_baseline(budget_s, mode=0):
     """The CPU oracle, as it stands, on a bounded sample of the layer
     workload, scaled to a whole-step rate: the oracle quantizes every
     operand of the four linears at full size (timed), then computes sampled
@@ -376,11 +386,11 @@ def cpu_baseline(budget_s):
         w = synth.normal_bf16((n, k), 0.02, 0, 3, 3 * li + 1)
         dy = synth.normal_bf16((TOKENS, n), 1e-3, 0, 3, 3 * li + 2)
         t0 = time.perf_counter()
-        qx, sx = oracle.quantize_rowgroup(x)
-        qxT, sxT = oracle.quantize_colgroup(x)
-        qw, _, sw = oracle.quantize_block(w, transpose=False)
-        qdy, sdy = oracle.quantize_rowgroup(dy)
-        qdyT, sdyT = oracle.quantize_colgroup(dy)
+        qx, sx = oracle.quantize_rowgroup(x, mode=mode)
+        qxT, sxT = oracle.quantize_colgroup(x, mode=mode)
+        qw, _, sw = oracle.quantize_block(w, transpose=False, mode=mode)
+        qdy, sdy = oracle.quantize_rowgroup(dy, mode=mode)
+        qdyT, sdyT = oracle.quantize_colgroup(dy, mode=mode)
         t_q += time.perf_counter() - t0
         ops.append({"rows": TOKENS, "t": 0.0, "done": 0, "flops": 2.0 * TOKENS * n * k,
                     "fn": lambda r, a=(qx, sx, qw, sw): oracle.gemm_fprop(*a, rows=r)})
@@ -428,10 +438,18 @@ def main():
 
     fb.load_library()
     torch.cuda.set_device(0)
-    global DUAL, FUSED_BWD, BATCH_W
+    global DUAL, FUSED_BWD, BATCH_W, SCALE_MODE
     DUAL = not args.separate_quant
     FUSED_BWD = not args.separate_bwd
     BATCH_W = not args.separate_wquant
+    if args.scale == "fp32":
+        # amax / 448 scales are not powers of two: only the promote GEMM takes them
+        if args.algo == "scaled":
+            print("bench.py: --scale fp32 needs the promote algorithm (the block-scaled MFMA applies "
+                  "power-of-two scales only)", file=sys.stderr)
+            sys.exit(2)
+        args.algo = "promote"
+        SCALE_MODE = fb.FP8BLK_SCALE_FP32
     algo = {"default": fb.FP8BLK_ALGO_DEFAULT, "promote": fb.FP8BLK_ALGO_PROMOTE,
             "scaled": fb.FP8BLK_ALGO_SCALED_MFMA}[args.algo]
 
@@ -533,6 +551,7 @@ def main():
         "dtype": "fp8e4m3",
         "data": "synthetic",
         "config": {"workload": desc, "name": args.workload, "tokens": TOKENS, "algo": args.algo,
+                   "scale": "power of two" if args.scale == "pow2" else "fp32 amax/448",
                    "quantizer": "separate" if args.separate_quant else "one-pass",
                    "backward": "separate" if args.separate_bwd else "fused",
                    "weight_quant": "per weight" if args.separate_wquant else "batched per layer",
@@ -564,7 +583,7 @@ def main():
         torch.cuda.synchronize()
         out["copy_calibration"] = {"bytes_read": src.numel() * 2, "bytes_written": dst.numel() * 2, "launches": 3}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_budget_s)
+        out["cpu_baseline"] = cpu_baseline(args.cpu_budget_s, mode=SCALE_MODE)
     print(json.dumps(out), flush=True)
 
 
