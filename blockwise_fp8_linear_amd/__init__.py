@@ -29,6 +29,7 @@ FP8BLK_OP_FPROP = 0
 FP8BLK_OP_DGRAD = 1
 FP8BLK_OP_WGRAD = 2
 FP8BLK_OP_BACKWARD = 3
+FP8BLK_OP_DGRAD_W = 4
 FP8BLK_ALGO_DEFAULT = 0
 FP8BLK_ALGO_PROMOTE = 1
 FP8BLK_ALGO_SCALED_MFMA = 2
@@ -62,6 +63,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fp8_block_gemm_wgrad": [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, sz, vp],
         "fp8_block_gemm": [i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp],
         "fp8_block_gemm_backward": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, vp, sz, vp],
+        "fp8_block_gemm_dgrad_w": [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp],
+        "fp8_block_gemm_backward_w": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, vp, sz, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -253,7 +256,7 @@ def fp8_block_gemm(op, a, sa, b, sb, M, N, K, out_dtype=None, algo=FP8BLK_ALGO_D
         _dense(t, torch.uint8, n)
     for t, n in ((sa, "sa"), (sb, "sb")):
         _dense(t, torch.float32, n)
-    shape = {FP8BLK_OP_FPROP: (M, N), FP8BLK_OP_DGRAD: (M, K), FP8BLK_OP_WGRAD: (N, K)}[op]
+    shape = {FP8BLK_OP_FPROP: (M, N), FP8BLK_OP_DGRAD: (M, K), FP8BLK_OP_WGRAD: (N, K), FP8BLK_OP_DGRAD_W: (M, K)}[op]
     y = _out(shape, out_dtype, a.device, out)
     need = fp8_block_gemm_workspace_size(op, M, N, K)
     if need and workspace is None:
@@ -297,6 +300,24 @@ def fp8_block_gemm_dgrad(qdy, sdy, qwT, sw, out_dtype=None, out=None, stream=Non
     return y
 
 
+def fp8_block_gemm_dgrad_w(qdy, sdy, qw, sw, out_dtype=None, out=None, stream=None, accumulate=False):
+    """dX = dY W from the weight codes as quantized.  qdy [M,N], sdy [M,N/128],
+    qw [N,K], sw [N/128,K/128] -> dX [M,K]."""
+    import torch
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    M, N = qdy.shape
+    K = qw.shape[1]
+    for t, n in ((qdy, "qdy"), (qw, "qw")):
+        _dense(t, torch.uint8, n)
+    for t, n in ((sdy, "sdy"), (sw, "sw")):
+        _dense(t, torch.float32, n)
+    y = _out((M, K), out_dtype, qdy.device, out)
+    _check(load_library().fp8_block_gemm_dgrad_w(M, N, K, qdy.data_ptr(), sdy.data_ptr(), qw.data_ptr(),
+                                                 sw.data_ptr(), y.data_ptr(), _odt(out_dtype, accumulate, out),
+                                                 _stream(stream)))
+    return y
+
+
 def fp8_block_gemm_wgrad(qdyT, sdyT, qxT, sxT, out_dtype=None, out=None, workspace=None, stream=None,
                          accumulate=False):
     """dW = dY^T X.  qdyT [N,M], sdyT [N,M/128], qxT [K,M], sxT [K,M/128] -> dW [N,K]."""
@@ -325,12 +346,25 @@ def fp8_block_gemm_backward(qdy, sdy, qwT, sw, qdyT, sdyT, qxT, sxT, dx_dtype=No
     """Dgrad and Wgrad of one linear in one call.  Operands as for
     fp8_block_gemm_dgrad and fp8_block_gemm_wgrad; returns (dx [M,K], dw [N,K]).
     accumulate_dw: dw += dY^T X in fp32 (dw_dtype float32, `dw` given)."""
+    return _backward("fp8_block_gemm_backward", qdy, sdy, qwT, qwT.shape[0], sw, qdyT, sdyT, qxT, sxT, dx_dtype,
+                     dw_dtype, dx, dw, workspace, stream, accumulate_dw)
+
+
+def fp8_block_gemm_backward_w(qdy, sdy, qw, sw, qdyT, sdyT, qxT, sxT, dx_dtype=None, dw_dtype=None, dx=None,
+                              dw=None, workspace=None, stream=None, accumulate_dw=False):
+    """fp8_block_gemm_backward with Dgrad reading the weight codes qw [N,K] as
+    quantized (no transposed copy)."""
+    return _backward("fp8_block_gemm_backward_w", qdy, sdy, qw, qw.shape[1], sw, qdyT, sdyT, qxT, sxT, dx_dtype,
+                     dw_dtype, dx, dw, workspace, stream, accumulate_dw)
+
+
+def _backward(fn, qdy, sdy, qwT, K, sw, qdyT, sdyT, qxT, sxT, dx_dtype, dw_dtype, dx, dw, workspace, stream,
+              accumulate_dw):
     import torch
     dx_dtype = torch.bfloat16 if dx_dtype is None else dx_dtype
     dw_dtype = torch.bfloat16 if dw_dtype is None else dw_dtype
     M, N = qdy.shape
-    K = qwT.shape[0]
-    for t, n in ((qdy, "qdy"), (qwT, "qwT"), (qdyT, "qdyT"), (qxT, "qxT")):
+    for t, n in ((qdy, "qdy"), (qwT, "weight codes"), (qdyT, "qdyT"), (qxT, "qxT")):
         _dense(t, torch.uint8, n)
     for t, n in ((sdy, "sdy"), (sw, "sw"), (sdyT, "sdyT"), (sxT, "sxT")):
         _dense(t, torch.float32, n)
@@ -341,10 +375,10 @@ def fp8_block_gemm_backward(qdy, sdy, qwT, sw, qdyT, sdyT, qxT, sxT, dx_dtype=No
         workspace = torch.empty(need, dtype=torch.uint8, device=qdy.device)
     wptr = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(load_library().fp8_block_gemm_backward(M, N, K, qdy.data_ptr(), sdy.data_ptr(), qwT.data_ptr(),
-                                                  sw.data_ptr(), qdyT.data_ptr(), sdyT.data_ptr(), qxT.data_ptr(),
-                                                  sxT.data_ptr(), x.data_ptr(), _odt(dx_dtype),
-                                                  w.data_ptr(), _odt(dw_dtype, accumulate_dw, dw), wptr, wbytes,
-                                                  _stream(stream)))
+    _check(getattr(load_library(), fn)(M, N, K, qdy.data_ptr(), sdy.data_ptr(), qwT.data_ptr(),
+                                       sw.data_ptr(), qdyT.data_ptr(), sdyT.data_ptr(), qxT.data_ptr(),
+                                       sxT.data_ptr(), x.data_ptr(), _odt(dx_dtype),
+                                       w.data_ptr(), _odt(dw_dtype, accumulate_dw, dw), wptr, wbytes,
+                                       _stream(stream)))
     return x, w
 

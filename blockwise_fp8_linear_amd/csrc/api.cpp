@@ -162,11 +162,13 @@ static fp8blk::GemmArgs make_args(int op, int64_t M, int64_t N, int64_t K, const
     // Y[m][n] = sum_k X[m][k] W[n][k]; weight block (n/128, k/128)
     g.I = M; g.J = N; g.R = K;
     g.sb_j = K / kGroup; g.sb_r = 1; g.bmode = fp8blk::BScale::Block;
-  } else if (op == FP8BLK_OP_DGRAD) {
-    // dX[m][k] = sum_n dY[m][n] W[n][k]: B = qwT [K][N]; the weight block
-    // holding (n, k) has scale sw[(n/128) * (K/128) + k/128]
+  } else if (op == FP8BLK_OP_DGRAD || op == FP8BLK_OP_DGRAD_W) {
+    // dX[m][k] = sum_n dY[m][n] W[n][k]: B = qwT [K][N] (DGRAD) or qw [N][K]
+    // read as quantized (DGRAD_W); the weight block holding (n, k) has
+    // scale sw[(n/128) * (K/128) + k/128]
     g.I = M; g.J = K; g.R = N;
     g.sb_j = 1; g.sb_r = K / kGroup; g.bmode = fp8blk::BScale::Block;
+    g.bt = op == FP8BLK_OP_DGRAD_W;
   } else {
     // dW[n][k] = sum_m dY[m][n] X[m][k]: A = qdyT [N][M], B = qxT [K][M]
     g.I = N; g.J = K; g.R = M;
@@ -179,7 +181,8 @@ static fp8blk::GemmArgs make_args(int op, int64_t M, int64_t N, int64_t K, const
 int fp8_block_gemm(int op, int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa, const uint8_t* b,
                    const float* sb, void* out, int out_dtype, int algo, void* workspace, size_t ws_bytes,
                    hipStream_t stream) {
-  if (op != FP8BLK_OP_FPROP && op != FP8BLK_OP_DGRAD && op != FP8BLK_OP_WGRAD) return FP8BLK_ERR_ARG;
+  if (op != FP8BLK_OP_FPROP && op != FP8BLK_OP_DGRAD && op != FP8BLK_OP_WGRAD && op != FP8BLK_OP_DGRAD_W)
+    return FP8BLK_ERR_ARG;
   if (algo != FP8BLK_ALGO_DEFAULT && algo != FP8BLK_ALGO_PROMOTE && algo != FP8BLK_ALGO_SCALED_MFMA)
     return FP8BLK_ERR_ARG;
   if (int rc = check_gemm_common(M, N, K, a, sa, b, sb, out, out_dtype)) return rc;
@@ -203,24 +206,42 @@ static size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return fused > wgrad ? fused : wgrad;
 }
 
-int fp8_block_gemm_backward(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy,
-                            const uint8_t* qwT, const float* sw, const uint8_t* qdyT, const float* sdyT,
-                            const uint8_t* qxT, const float* sxT, void* dx, int dx_dtype, void* dw, int dw_dtype,
-                            void* workspace, size_t ws_bytes, hipStream_t stream) {
-  if (int rc = check_gemm_common(M, N, K, qdy, sdy, qwT, sw, dx, dx_dtype)) return rc;
+// Both backward entry points: dgrad_op is FP8BLK_OP_DGRAD (w = qwT [K][N])
+// or FP8BLK_OP_DGRAD_W (w = qw [N][K]).
+static int backward(int dgrad_op, int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy,
+                    const uint8_t* w, const float* sw, const uint8_t* qdyT, const float* sdyT, const uint8_t* qxT,
+                    const float* sxT, void* dx, int dx_dtype, void* dw, int dw_dtype, void* workspace,
+                    size_t ws_bytes, hipStream_t stream) {
+  if (int rc = check_gemm_common(M, N, K, qdy, sdy, w, sw, dx, dx_dtype)) return rc;
   if (int rc = check_gemm_common(M, N, K, qdyT, sdyT, qxT, sxT, dw, dw_dtype)) return rc;
   if (dx == dw) return FP8BLK_ERR_ARG;
   const size_t need = backward_workspace_bytes(M, N, K);
   if (need > 0 && (workspace == nullptr || ws_bytes < need)) return FP8BLK_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return FP8BLK_ERR_ALIGN;
   if (int rc = check_device()) return rc;
-  fp8blk::GemmArgs gd = make_args(FP8BLK_OP_DGRAD, M, N, K, qdy, sdy, qwT, sw, dx, dx_dtype);
+  fp8blk::GemmArgs gd = make_args(dgrad_op, M, N, K, qdy, sdy, w, sw, dx, dx_dtype);
   fp8blk::GemmArgs gw = make_args(FP8BLK_OP_WGRAD, M, N, K, qdyT, sdyT, qxT, sxT, dw, dw_dtype);
   gw.ws = static_cast<float*>(workspace);
   if (fp8blk::gemm_mx_bwd_eligible(gd, gw)) return finish(fp8blk::launch_gemm_mx_bwd(gd, gw, stream));
   // shapes the fused launch does not take: the two contractions in turn
   if (hipError_t e = fp8blk::launch_gemm(gd, kDefaultAlgo, stream)) return finish(e);
   return finish(fp8blk::launch_gemm(gw, kDefaultAlgo, stream));
+}
+
+int fp8_block_gemm_backward(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy,
+                            const uint8_t* qwT, const float* sw, const uint8_t* qdyT, const float* sdyT,
+                            const uint8_t* qxT, const float* sxT, void* dx, int dx_dtype, void* dw, int dw_dtype,
+                            void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return backward(FP8BLK_OP_DGRAD, M, N, K, qdy, sdy, qwT, sw, qdyT, sdyT, qxT, sxT, dx, dx_dtype, dw, dw_dtype,
+                  workspace, ws_bytes, stream);
+}
+
+int fp8_block_gemm_backward_w(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy,
+                              const uint8_t* qw, const float* sw, const uint8_t* qdyT, const float* sdyT,
+                              const uint8_t* qxT, const float* sxT, void* dx, int dx_dtype, void* dw, int dw_dtype,
+                              void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return backward(FP8BLK_OP_DGRAD_W, M, N, K, qdy, sdy, qw, sw, qdyT, sdyT, qxT, sxT, dx, dx_dtype, dw, dw_dtype,
+                  workspace, ws_bytes, stream);
 }
 
 int fp8_block_gemm_fprop(int64_t M, int64_t N, int64_t K, const uint8_t* qx, const float* sx, const uint8_t* qw,
@@ -235,6 +256,12 @@ int fp8_block_gemm_dgrad(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, co
                         stream);
 }
 
+int fp8_block_gemm_dgrad_w(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy, const uint8_t* qw,
+                           const float* sw, void* dx, int out_dtype, hipStream_t stream) {
+  return fp8_block_gemm(FP8BLK_OP_DGRAD_W, M, N, K, qdy, sdy, qw, sw, dx, out_dtype, FP8BLK_ALGO_DEFAULT, nullptr, 0,
+                        stream);
+}
+
 int fp8_block_gemm_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* qdyT, const float* sdyT,
                          const uint8_t* qxT, const float* sxT, void* dw, int out_dtype, void* workspace,
                          size_t ws_bytes, hipStream_t stream) {
@@ -246,7 +273,8 @@ size_t fp8_block_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
   if (!mult128(M) || !mult128(N) || !mult128(K)) return (size_t)-1;
   switch (op) {
     case FP8BLK_OP_FPROP: return fp8blk::gemm_workspace_bytes(M, N, K, fp8blk::BScale::Block);
-    case FP8BLK_OP_DGRAD: return fp8blk::gemm_workspace_bytes(M, K, N, fp8blk::BScale::Block);
+    case FP8BLK_OP_DGRAD:
+    case FP8BLK_OP_DGRAD_W: return fp8blk::gemm_workspace_bytes(M, K, N, fp8blk::BScale::Block);
     case FP8BLK_OP_WGRAD: return fp8blk::gemm_workspace_bytes(N, K, M, fp8blk::BScale::Row);
     case FP8BLK_OP_BACKWARD: return backward_workspace_bytes(M, N, K);
     default: return (size_t)-1;

@@ -151,6 +151,18 @@ __device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[
   out[3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
 }
 
+// ds_read_b64_tr_b8 (gfx950), as probed on the GPU: within each group of 16
+// lanes, lane i receives, as byte b, byte i % 8 of the 8 bytes addressed by
+// lane 2 b + i / 8 of the group.  With lanes 2b and 2b+1 addressing row b of
+// a [reduction][column] tile in LDS at columns c..c+7 and c+8..c+15, lane i
+// gets column c + i and the 8 consecutive reduction values of rows 0..7 --
+// an MFMA operand fragment of a tile stored along the reduction's rows.
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v2i_t lds_read_tr8(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) v2i_t lds_v2i;
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)((const __attribute__((address_space(3))) uint8_t*)p));
+}
+
 // Two fp32 values rounded to bf16 (nearest even), packed: lo in bits 15:0.
 // One v_cvt_pk_bf16_f32 on gfx950.
 typedef float v2f_t __attribute__((ext_vector_type(2)));

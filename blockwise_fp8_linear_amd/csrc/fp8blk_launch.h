@@ -49,6 +49,8 @@ struct GemmArgs {
   bool accumulate;          // fp32 output only: out += result
   float* ws;                // split-K or stream-K workspace (may be null when none is needed)
   int splits;
+  bool bt;                  // B stored [R][J] instead of [J][R] (Dgrad from the weight codes
+                            // as quantized); weight-block scales only
 };
 
 // Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once

@@ -8,6 +8,7 @@
 // reduction dimension, so
 //   Fprop  Y  = X W^T : A = qx   [M][K], B = qw  [N][K], B scales per block
 //   Dgrad  dX = dY W  : A = qdy  [M][N], B = qwT [K][N], B scales per block
+//                       (or B = qw [N][K] as quantized: the BT configurations)
 //   Wgrad  dW = dY^T X: A = qdyT [N][M], B = qxT [K][M], B scales per row
 // (one scale per 128 along the reduction dimension for activations and
 // gradients, per 128x128 block for weights: section 3.2, second paragraph).
@@ -43,9 +44,14 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kChunk = 32;  // reduction blocks whose scales sit in LDS at once
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, bool PROMOTE_, bool BROW_>
+// BT_: B stored [R][J] (Dgrad from the weight codes as quantized): the B
+// tile is staged as 128 reduction rows of BN bytes and its fragments come
+// from LDS transpose reads.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, bool PROMOTE_, bool BROW_, bool BT_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
+  static constexpr bool BT = BT_;
+  static_assert(!BT_ || (!BROW_ && BN_ == 128), "transposed B: Dgrad's weight-block layout, 128-byte rows");
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 16, TN = WN / 16;
@@ -72,6 +78,25 @@ template <class C>
 __device__ __forceinline__ typename C::SType staged_scale(float s) {
   if constexpr (C::PROMOTE) return s;
   else return (uint8_t)e8_of(s);
+}
+
+// Read a 32-byte MFMA fragment of a transposed-B tile ([128 reduction
+// rows][128 B of columns], 16-byte chunks swizzled by row & 7): the lane's
+// column is 16 * col16 + lane % 16 and its reduction values are
+// 32 (lane / 16) .. +31, the order of read_frag's; four transpose reads of 8
+// rows each (see lds_read_tr8).  Row n = 32 q + 8 r + s / 2 of lane group
+// q, position s, so n & 7 = s / 2.
+__device__ __forceinline__ v8i read_frag_bt(const uint8_t* tile, uint32_t col16, uint32_t lane) {
+  const uint32_t q = lane >> 4, s = lane & 15;
+  const uint8_t* p = tile + (32 * q + (s >> 1)) * 128 + ((col16 ^ (s >> 1)) << 4) + 8 * (s & 1);
+  v8i f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const v2i_t v = lds_read_tr8(p + r * 8 * 128);
+    f[2 * r] = v[0];
+    f[2 * r + 1] = v[1];
+  }
+  return f;
 }
 
 // Read a 32-byte MFMA fragment: row `row` of a swizzled [rows][128 B] tile,
@@ -133,9 +158,17 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
 #pragma unroll
     for (int u = 0; u < C::B_LOADS; ++u) {
       const uint32_t c = tid + u * C::THREADS;
-      int64_t row = j0 + (c >> 3);
-      row = row < g.J ? row : g.J - 1;
-      rb[u] = *reinterpret_cast<const u32x4*>(g.b + row * R + kb * 128 + (c & 7) * 16);
+      if constexpr (C::BT) {
+        // reduction row kb * 128 + c / 8, columns j0 + 16 (c % 8) .. (a chunk
+        // past a ragged column edge reads the last valid one, never stored)
+        int64_t col = j0 + (c & 7) * 16;
+        col = col < g.J - 16 ? col : g.J - 16;
+        rb[u] = *reinterpret_cast<const u32x4*>(g.b + (kb * 128 + (c >> 3)) * g.J + col);
+      } else {
+        int64_t row = j0 + (c >> 3);
+        row = row < g.J ? row : g.J - 1;
+        rb[u] = *reinterpret_cast<const u32x4*>(g.b + row * R + kb * 128 + (c & 7) * 16);
+      }
     }
   };
   auto lstore = [&](int buf) {
@@ -216,7 +249,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
     // B fragments (the instruction's A operand) for the wave's TN sub-tiles
     v8i bf[C::TN];
 #pragma unroll
-    for (int ns = 0; ns < C::TN; ++ns) bf[ns] = read_frag(tb, wn0 + ns * 16 + l16, g4);
+    for (int ns = 0; ns < C::TN; ++ns)
+      bf[ns] = C::BT ? read_frag_bt(tb, (wn0 >> 4) + ns, lane) : read_frag(tb, wn0 + ns * 16 + l16, g4);
 
     // A-row scales of this lane's rows i = wm0 + ms*16 + l16 sit at
     // sa_lds[kbl][l16][wm0 / 16 + ms]
@@ -374,6 +408,8 @@ using PromoteBlock = Cfg<256, 128, 2, 2, true, false>;
 using PromoteRow = Cfg<256, 128, 2, 2, true, true>;
 using ScaledBlock = Cfg<256, 128, 2, 2, false, false>;
 using ScaledRow = Cfg<256, 128, 2, 2, false, true>;
+using PromoteBlockBT = Cfg<256, 128, 2, 2, true, false, true>;
+using ScaledBlockBT = Cfg<256, 128, 2, 2, false, false, true>;
 
 constexpr int kCUs = 256;
 
@@ -434,7 +470,9 @@ hipError_t launch_gemm(const GemmArgs& g, GemmAlgo algo, hipStream_t stream) {
   // the 256x256 kernel needs no split-K reduction (Wgrad runs stream-K)
   if (algo == GemmAlgo::ScaledMfma && gemm_mx_eligible(g)) return launch_gemm_mx(g, stream);
   hipError_t e;
-  if (algo == GemmAlgo::Promote)
+  if (g.bt)
+    e = algo == GemmAlgo::Promote ? launch_cfg<PromoteBlockBT>(g, stream) : launch_cfg<ScaledBlockBT>(g, stream);
+  else if (algo == GemmAlgo::Promote)
     e = g.bmode == BScale::Row ? launch_cfg<PromoteRow>(g, stream) : launch_cfg<PromoteBlock>(g, stream);
   else
     e = g.bmode == BScale::Row ? launch_cfg<ScaledRow>(g, stream) : launch_cfg<ScaledBlock>(g, stream);

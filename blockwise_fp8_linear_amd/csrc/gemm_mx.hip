@@ -20,6 +20,10 @@
 //     register per operand row and picked by the instruction's op_sel; the
 //     weight-block scales of a tile are staged in LDS once;
 //   * the epilogue stages each wave's tile through LDS and stores whole rows;
+//   * Dgrad can read the weight codes W[n][k] as quantized (reduction along
+//     the rows, no transposed copy): that B tile is staged as 128 weight rows
+//     of 256 bytes and its fragments come from LDS transpose reads
+//     (ds_read_b64_tr_b8);
 //   * Wgrad (long reduction over tokens, few output tiles) runs stream-K:
 //     a persistent grid in which every workgroup does the same number of
 //     512-deep reduction units, tiles shared by several workgroups being
@@ -101,6 +105,14 @@ struct IntC {
 // depends on row & 31 only, so it is the same for every 32-row MFMA tile.
 __device__ __forceinline__ uint32_t swz(uint32_t row) { return ((row & 31) ^ ((row & 31) >> 3)) & 7; }
 
+// The transposed-B tile (128 reduction rows x 256 bytes = 16 chunks): physical
+// chunk = logical ^ swz_bt(row).  A transpose read of one 16-lane group
+// touches 8 consecutive rows (aligned to 8) at one or two adjacent logical
+// chunks; 2 * (row & 7) sends those 16 (row, chunk) pairs to 16 distinct
+// chunk positions, i.e. distinct banks.
+__device__ __forceinline__ uint32_t swz_bt(uint32_t row) { return 2 * (row & 7); }
+
+
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt low 4 bits and
 // bits 15:14, expcnt 6:4, lgkmcnt 11:8).
 template <int N>
@@ -133,9 +145,12 @@ __device__ __forceinline__ void tile_origin(int64_t tile, int64_t tiles_m, int64
 // [kb_begin, kb_begin + nkb_seg) (nkb_seg a multiple of 4) into acc, which it
 // zeroes first.  On return every direct load has landed; the LDS ring may
 // still be read by other waves until the next barrier.
-template <bool BROW>
+// BT: B is stored [R][J] (the weight codes W[n][k] read as quantized, for
+// Dgrad) instead of [J][R]; weight-block scales only.
+template <bool BROW, bool BT = false>
 __device__ __forceinline__ void mma_segment(const GemmArgs& g, uint8_t* lds, int64_t i0, int64_t j0, int64_t kb_begin,
                                             int64_t nkb_seg, v16f (&acc)[TM][TN]) {
+  static_assert(!(BT && BROW), "the transposed-B layout is Dgrad's, with weight-block scales");
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t wm = wave >> 1, wn = wave & 1;
@@ -151,7 +166,9 @@ __device__ __forceinline__ void mma_segment(const GemmArgs& g, uint8_t* lds, int
   // past a ragged edge read the last row (valid memory, results never stored).
   const int npair = (int)nkb_seg;
   const uint8_t* baseA = g.a + i0 * R + kb_begin * 128;
-  const uint8_t* baseB = g.b + j0 * R + kb_begin * 128;
+  // BT: pair p is reduction rows 128 (kb_begin + p) .. +127 of B[R][J]
+  const uint8_t* baseB = BT ? g.b + kb_begin * 128 * g.J + j0 : g.b + j0 * R + kb_begin * 128;
+  const int64_t pairB = BT ? 128 * g.J : PK;  // bytes from one pair of B to the next
   uint32_t offLA[LOADS_A], offLB[LOADS_B];
 #pragma unroll
   for (int u = 0; u < LOADS_A; ++u) {
@@ -162,10 +179,21 @@ __device__ __forceinline__ void mma_segment(const GemmArgs& g, uint8_t* lds, int
   }
 #pragma unroll
   for (int u = 0; u < LOADS_B; ++u) {
-    const uint32_t row = (wave * LOADS_B + u) * 8 + (lane >> 3);
-    int64_t gr = j0 + row;
-    gr = gr < g.J ? gr : g.J - 1;
-    offLB[u] = (uint32_t)((gr - j0) * R) + (((lane & 7) ^ swz(row)) << 4);
+    if constexpr (BT) {
+      // wave instruction u fills 4 reduction rows x 256 B: lane p writes
+      // row p/16, physical chunk p%16, which holds logical chunk
+      // (p%16) ^ swz_bt(row), i.e. columns j0 + 16 * logical ..; chunks
+      // past a ragged column edge read the last valid one (never stored)
+      const uint32_t row = (wave * LOADS_B + u) * 4 + (lane >> 4);
+      int64_t col = 16 * (int64_t)((lane & 15) ^ swz_bt(row));
+      col = j0 + col < g.J - 16 ? col : g.J - 16 - j0;
+      offLB[u] = (uint32_t)(row * g.J + col);
+    } else {
+      const uint32_t row = (wave * LOADS_B + u) * 8 + (lane >> 3);
+      int64_t gr = j0 + row;
+      gr = gr < g.J ? gr : g.J - 1;
+      offLB[u] = (uint32_t)((gr - j0) * R) + (((lane & 7) ^ swz(row)) << 4);
+    }
   }
   // pair p -> slot p % SLOTS; a pair past the end reloads the last one into a
   // slot that is never read again (keeps the waits uniform).
@@ -176,7 +204,7 @@ __device__ __forceinline__ void mma_segment(const GemmArgs& g, uint8_t* lds, int
     if (u < LOADS_A)
       dma16(baseA + (int64_t)pc * PK, offLA[u], slot + (wave * LOADS_A + u) * 1024);
     else
-      dma16(baseB + (int64_t)pc * PK, offLB[u - LOADS_A], slot + A_SLOT + (wave * LOADS_B + u - LOADS_A) * 1024);
+      dma16(baseB + (int64_t)pc * pairB, offLB[u - LOADS_A], slot + A_SLOT + (wave * LOADS_B + u - LOADS_A) * 1024);
   };
   auto issue_pair = [&](int pr) {
 #pragma unroll
@@ -224,11 +252,35 @@ __device__ __forceinline__ void mma_segment(const GemmArgs& g, uint8_t* lds, int
     const u32x4 hi = *reinterpret_cast<const u32x4*>(p + hiOff);
     return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
+  // BT: the fragment of the wave's t-th 32-column tile in four transpose
+  // reads.  Lane l needs column wn0 + 32t + l%32 and, of stage st, reduction
+  // values 32 (l/32) .. +31 (the same order as A's fragment); read r covers
+  // 8r .. 8r+7 of them.  In the lane's 16-lane group q = l/16 and position
+  // s = l%16 it addresses row 64 (st%2) + 32 (q/2) + 8r + s/2 of the pair at
+  // columns wn0 + 32t + 16 (q%2) + 8 (s%2) .. +7; swz_bt(row) = 2 (s/2).
+  const uint32_t bt_q = lane >> 4, bt_s = lane & 15;
+  const uint32_t bt_row = (32 * (bt_q >> 1) + (bt_s >> 1)) * 256 + 8 * (bt_s & 1);
+  auto read_frag_bt = [&](int st, int t) {
+    const uint8_t* p = lds + ((st >> 1) % SLOTS) * SLOT + A_SLOT + bt_row + (st & 1) * 64 * 256 +
+                       (((((wn0 >> 4) + 2 * t + (bt_q & 1)) ^ (2 * (bt_s >> 1))) << 4));
+    v8i f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const v2i_t v = lds_read_tr8(p + r * 8 * 256);
+      f[2 * r] = v[0];
+      f[2 * r + 1] = v[1];
+    }
+    return f;
+  };
+  auto read_frag_b = [&](int st, int t) {
+    if constexpr (BT) return read_frag_bt(st, t);
+    else return read_frag(st, rowB + t * 32 * PK);
+  };
   auto read_frags = [&](int st, v8i* fa, v8i* fb) {
 #pragma unroll
     for (int t = 0; t < TM; ++t) fa[t] = read_frag(st, rowA + t * 32 * PK);
 #pragma unroll
-    for (int t = 0; t < TN; ++t) fb[t] = read_frag(st, rowB + t * 32 * PK);
+    for (int t = 0; t < TN; ++t) fb[t] = read_frag_b(st, t);
   };
   // packed E8M0 scale bytes of group q for this lane's operand rows
   // (row wm0 + 32t + l%32 of A, of B in row mode); weight-block scales are
@@ -314,7 +366,7 @@ __device__ __forceinline__ void mma_segment(const GemmArgs& g, uint8_t* lds, int
           fb[BUF][b0 + 1], fa[BUF][a], acc[a][b0 + 1], 0, 0, OPSEL, (int)sb_cur[b0 + 1], OPSEL, (int)sa_cur[a]);
       // next stage's fragments in the order its MFMAs consume them
       if (p == 0) fa[NXT][0] = read_frag(st + 1, rowA);
-      else if (p <= 4) fb[NXT][p - 1] = read_frag(st + 1, rowB + (p - 1) * 32 * PK);
+      else if (p <= 4) fb[NXT][p - 1] = read_frag_b(st + 1, p - 1);
       else fa[NXT][p - 4] = read_frag(st + 1, rowA + (p - 4) * 32 * PK);
       if constexpr (BUF == 1) {
         issue_one((st + 3) >> 1, 2 * p);
@@ -494,15 +546,16 @@ __device__ __forceinline__ void store_tile(const Dst& d, uint8_t* lds, int64_t i
   store_tile_from<BATCH>(d, lds, i0, j0, [&](int a, int b) { return acc[a][b]; });
 }
 
-// One output tile per workgroup, the whole reduction (Fprop and Dgrad).
-template <bool BROW>
+// One output tile per workgroup, the whole reduction (Fprop and Dgrad; BT:
+// Dgrad from the weight codes as quantized).
+template <bool BROW, bool BT = false>
 __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t tiles_m, int64_t tiles_n) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
   int64_t i0, j0;
   tile_origin(tile, tiles_m, tiles_n, i0, j0);
   v16f acc[TM][TN];
-  mma_segment<BROW>(g, lds, i0, j0, 0, g.R / 128, acc);
+  mma_segment<BROW, BT>(g, lds, i0, j0, 0, g.R / 128, acc);
   store_tile<8>(Dst{g.out, g.J, g.I, g.J, g.out_f32, g.accumulate}, lds, i0, j0, acc);
 }
 
@@ -646,6 +699,8 @@ struct BwdGeom {
   int64_t k0, k1;
 };
 
+// BT: Dgrad reads the weight codes as quantized (gd.b is W[N][K]).
+template <bool BT>
 __global__ __launch_bounds__(THREADS) void gemm_mx_bwd_kernel(GemmArgs gd, GemmArgs gw, BwdGeom bg,
                                                               float* partials) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -669,7 +724,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_bwd_kernel(GemmArgs gd, GemmA
     if (p1)
       mma_segment<true>(gw, lds, i0, j0, lo * 4, (hi - lo) * 4, acc);
     else
-      mma_segment<false>(gd, lds, i0, j0, lo * 4, (hi - lo) * 4, acc);
+      mma_segment<false, BT>(gd, lds, i0, j0, lo * 4, (hi - lo) * 4, acc);
     if (lo == 0 && hi == U) {
       const Dst d{p1 ? gw.out : gd.out, p1 ? gw.J : gd.J, p1 ? gw.I : gd.I, p1 ? gw.J : gd.J,
                   p1 ? gw.out_f32 : gd.out_f32, p1 ? gw.accumulate : gd.accumulate};
@@ -815,14 +870,14 @@ hipError_t set_lds_attr(K* kernel, std::atomic<uint64_t>* done) {
   return ensure_lds_limit(reinterpret_cast<const void*>(kernel), LDS_BYTES, done);
 }
 
-template <bool BROW>
+template <bool BROW, bool BT>
 hipError_t launch_mx(const GemmArgs& g, hipStream_t stream) {
   const int64_t tiles_m = (g.I + BM - 1) / BM;
   const int64_t tiles_n = (g.J + BN - 1) / BN;
   static std::atomic<uint64_t> attr_set{0};
-  if (hipError_t e = set_lds_attr(&gemm_mx_kernel<BROW>, &attr_set)) return e;
-  hipLaunchKernelGGL(gemm_mx_kernel<BROW>, dim3((uint32_t)(tiles_m * tiles_n)), dim3(THREADS), LDS_BYTES, stream, g,
-                     tiles_m, tiles_n);
+  if (hipError_t e = set_lds_attr(&gemm_mx_kernel<BROW, BT>, &attr_set)) return e;
+  hipLaunchKernelGGL((gemm_mx_kernel<BROW, BT>), dim3((uint32_t)(tiles_m * tiles_n)), dim3(THREADS), LDS_BYTES, stream,
+                     g, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -842,12 +897,13 @@ hipError_t launch_mx_streamk(const GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <bool BT>
 hipError_t launch_bwd(const GemmArgs& gd, const GemmArgs& gw, float* ws, hipStream_t stream) {
   const BwdPlan p = bwd_plan(gd.I, gd.R, gd.J);
   static std::atomic<uint64_t> attr_set{0};
-  if (hipError_t e = set_lds_attr(&gemm_mx_bwd_kernel, &attr_set)) return e;
+  if (hipError_t e = set_lds_attr(&gemm_mx_bwd_kernel<BT>, &attr_set)) return e;
   float* const partials = p.partial ? ws : nullptr;
-  hipLaunchKernelGGL(gemm_mx_bwd_kernel, dim3((uint32_t)p.grid), dim3(THREADS), LDS_BYTES, stream, gd, gw, p.geom,
+  hipLaunchKernelGGL(gemm_mx_bwd_kernel<BT>, dim3((uint32_t)p.grid), dim3(THREADS), LDS_BYTES, stream, gd, gw, p.geom,
                      partials);
   if (hipError_t e = hipGetLastError()) return e;
   if (!p.partial) return hipSuccess;
@@ -865,7 +921,9 @@ bool gemm_mx_eligible(const GemmArgs& g) {
   // weight-block mode keeps the tile's whole column of block scales in LDS
   if (g.bmode == BScale::Block && nkb > MAX_KB) return false;
   // per-lane 32-bit offsets: 256 rows x R bytes of codes, 256 rows of scales
+  // (the transposed-B layout: 128 rows x J bytes)
   if (g.R > (int64_t(1) << 22)) return false;
+  if (g.bt && (g.bmode != BScale::Block || g.J > (int64_t(1) << 22))) return false;
   if ((reinterpret_cast<uintptr_t>(g.sa) & 15) != 0) return false;
   if (g.bmode == BScale::Row && (reinterpret_cast<uintptr_t>(g.sb) & 15) != 0) return false;
   return true;
@@ -878,7 +936,7 @@ size_t gemm_mx_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode) {
 
 hipError_t launch_gemm_mx(const GemmArgs& g, hipStream_t stream) {
   if (g.bmode == BScale::Row) return launch_mx_streamk<true>(g, stream);
-  return launch_mx<false>(g, stream);
+  return g.bt ? launch_mx<false, true>(g, stream) : launch_mx<false, false>(g, stream);
 }
 
 bool gemm_mx_bwd_eligible(const GemmArgs& gd, const GemmArgs& gw) {
@@ -892,7 +950,7 @@ size_t gemm_mx_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm_mx_bwd(const GemmArgs& gd, const GemmArgs& gw, hipStream_t stream) {
-  return launch_bwd(gd, gw, gw.ws, stream);
+  return gd.bt ? launch_bwd<true>(gd, gw, gw.ws, stream) : launch_bwd<false>(gd, gw, gw.ws, stream);
 }
 
 }  // namespace fp8blk

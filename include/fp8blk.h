@@ -82,8 +82,10 @@ enum fp8blk_out_dtype { FP8BLK_OUT_BF16 = 0, FP8BLK_OUT_FP32 = 1, FP8BLK_OUT_FP3
 
 /* Which contraction (for fp8_block_gemm and the workspace query;
  * FP8BLK_OP_BACKWARD, Dgrad and Wgrad together, for the workspace query and
- * fp8_block_gemm_backward only). */
-enum fp8blk_op { FP8BLK_OP_FPROP = 0, FP8BLK_OP_DGRAD = 1, FP8BLK_OP_WGRAD = 2, FP8BLK_OP_BACKWARD = 3 };
+ * the two backward functions only).  FP8BLK_OP_DGRAD_W is Dgrad reading the
+ * weight codes qw [N][K] as quantized instead of the transposed copy. */
+enum fp8blk_op { FP8BLK_OP_FPROP = 0, FP8BLK_OP_DGRAD = 1, FP8BLK_OP_WGRAD = 2, FP8BLK_OP_BACKWARD = 3,
+                 FP8BLK_OP_DGRAD_W = 4 };
 
 /* How the per-block scale product reaches the fp32 accumulators.
  *   PROMOTE:     one MFMA per 128-deep reduction block starting from zero,
@@ -217,6 +219,21 @@ int fp8_block_gemm_dgrad(int64_t M, int64_t N, int64_t K,
                          void *dx, int out_dtype, hipStream_t stream);
 
 /*
+ * Dgrad from the weight codes as quantized: the same contraction and result
+ * as fp8_block_gemm_dgrad, but B is qw [N][K], the row-major codes of
+ * fp8_quantize_block (section 3.2, fourth paragraph: the weights are
+ * quantized right before the GEMMs), so the block quantizer can skip the
+ * transposed copy (qT = NULL).  The kernel stages [n][k] tiles and forms its
+ * operand fragments with LDS transpose reads.
+ *   qdy [M][N] codes + sdy [M][N/128]; qw [N][K] codes; sw [N/128][K/128]
+ *   dx  [M][K], bf16 bits or fp32 (or fp32 accumulated)
+ */
+int fp8_block_gemm_dgrad_w(int64_t M, int64_t N, int64_t K,
+                           const uint8_t *qdy, const float *sdy,
+                           const uint8_t *qw, const float *sw,
+                           void *dx, int out_dtype, hipStream_t stream);
+
+/*
  * Wgrad  dW = dY^T X  (section 3.2, fourth paragraph); the reduction runs
  * over the M tokens, so both operands are column-group quantized.
  *   qdyT [N][M] codes + sdyT [N][M/128]  (fp8_quantize_colgroup of dY)
@@ -262,10 +279,24 @@ int fp8_block_gemm_backward(int64_t M, int64_t N, int64_t K,
                             void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * fp8_block_gemm_backward with Dgrad reading the weight codes qw [N][K] as
+ * quantized (as fp8_block_gemm_dgrad_w does); everything else identical,
+ * including the workspace (FP8BLK_OP_BACKWARD's size).
+ */
+int fp8_block_gemm_backward_w(int64_t M, int64_t N, int64_t K,
+                              const uint8_t *qdy, const float *sdy,
+                              const uint8_t *qw, const float *sw,
+                              const uint8_t *qdyT, const float *sdyT,
+                              const uint8_t *qxT, const float *sxT,
+                              void *dx, int dx_dtype, void *dw, int dw_dtype,
+                              void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * All three contractions through one entry point, with an explicit algorithm.
  *   op = FP8BLK_OP_FPROP: (a, sa, b, sb) = (qx, sx, qw, sw),    out [M][N]
  *   op = FP8BLK_OP_DGRAD: (a, sa, b, sb) = (qdy, sdy, qwT, sw), out [M][K]
  *   op = FP8BLK_OP_WGRAD: (a, sa, b, sb) = (qdyT, sdyT, qxT, sxT), out [N][K]
+ *   op = FP8BLK_OP_DGRAD_W: (a, sa, b, sb) = (qdy, sdy, qw, sw), out [M][K]
  * Operand layouts, workspace and errors are as for the named functions above
  * (which are this call with FP8BLK_ALGO_DEFAULT); a bad op or algo gives
  * FP8BLK_ERR_ARG.

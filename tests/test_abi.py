@@ -26,6 +26,7 @@ def test_exports_every_declared_function(lib):
         "fp8_quantize_rowgroup", "fp8_quantize_colgroup", "fp8_quantize_block", "fp8_quantize_dual",
         "fp8_quantize_block_batch",
         "fp8_block_gemm_fprop", "fp8_block_gemm_dgrad", "fp8_block_gemm_wgrad", "fp8_block_gemm_backward",
+        "fp8_block_gemm_dgrad_w", "fp8_block_gemm_backward_w",
         "fp8_block_gemm", "fp8_block_gemm_workspace_size", "fp8_status_string",
     }
     for n in names:
@@ -130,6 +131,15 @@ def test_gemm_errors(lib):
     assert f(256, 256, 256, P, P3 + 1, P2, P3, P, 0, None) == EALIGN
     g = lib.fp8_block_gemm
     assert g(3, 256, 256, 256, P, P3, P2, P3, P, 0, 0, None, 0, None) == EARG   # op
+    assert g(5, 256, 256, 256, P, P3, P2, P3, P, 0, 0, None, 0, None) == EARG
+    assert g(4, 256, 256, 256, P, P3, P2, P3, P, 0, 1, None, 0, None) in (EHIP, EDEV)   # Dgrad from qw
+    assert lib.fp8_block_gemm_workspace_size(4, 8192, 2048, 2048) == lib.fp8_block_gemm_workspace_size(1, 8192, 2048, 2048)
+    d = lib.fp8_block_gemm_dgrad_w
+    assert d(256, 256, 256, P, P3, P2, P3, P, 0, None) in (EHIP, EDEV)
+    assert d(256, 256, 256, P, P3, None, P3, P, 0, None) == ENULL
+    assert d(256, 200, 256, P, P3, P2, P3, P, 0, None) == EDIM
+    assert d(256, 256, 256, P, P3, MIS, P3, P, 0, None) == EALIGN
+    assert d(256, 256, 256, P, P3, P2, P3, P, 4, None) == EARG
     assert g(0, 256, 256, 256, P, P3, P2, P3, P, 0, 9, None, 0, None) == EARG   # algo
     # wgrad at a shape that splits the reduction needs a workspace
     need = lib.fp8_block_gemm_workspace_size(2, 8192, 256, 256)
@@ -140,8 +150,9 @@ def test_gemm_errors(lib):
     assert w(8192, 256, 256, P, P3, P2, P3, P, 0, MIS, need, None) == EALIGN
 
 
-def test_backward_errors(lib):
-    f = lib.fp8_block_gemm_backward
+@pytest.mark.parametrize("fn", ["fp8_block_gemm_backward", "fp8_block_gemm_backward_w"])
+def test_backward_errors(lib, fn):
+    f = getattr(lib, fn)
     P4, P5, P6, P7 = 0x400000, 0x500000, 0x600000, 0x700000
     need = lib.fp8_block_gemm_workspace_size(3, 8192, 2048, 2048)
     assert need > 0 and need != ctypes.c_size_t(-1).value

@@ -75,15 +75,17 @@ class Layer:
         g = self.g
         args = {"fprop": (g["qx"], g["sx"], g["qw"], g["sw"]),
                 "dgrad": (g["qdy"], g["sdy"], g["qwT"], g["sw"]),
+                "dgrad_w": (g["qdy"], g["sdy"], g["qw"], g["sw"]),
                 "wgrad": (g["qdyT"], g["sdyT"], g["qxT"], g["sxT"])}[op]
-        opc = {"fprop": fb.FP8BLK_OP_FPROP, "dgrad": fb.FP8BLK_OP_DGRAD, "wgrad": fb.FP8BLK_OP_WGRAD}[op]
+        opc = {"fprop": fb.FP8BLK_OP_FPROP, "dgrad": fb.FP8BLK_OP_DGRAD, "dgrad_w": fb.FP8BLK_OP_DGRAD_W,
+               "wgrad": fb.FP8BLK_OP_WGRAD}[op]
         return fb.fp8_block_gemm(opc, *args, self.M, self.N, self.K, out_dtype=out_dtype, algo=algo)
 
     def ref(self, op, rows):
         o = self.o
         if op == "fprop":
             return oracle.gemm_fprop(o["qx"], o["sx"], o["qw"], o["sw"], rows=rows)
-        if op == "dgrad":
+        if op in ("dgrad", "dgrad_w"):
             return oracle.gemm_dgrad(o["qdy"], o["sdy"], o["qw"], o["sw"], rows=rows)
         return oracle.gemm_wgrad(o["qdyT"], o["sdyT"], o["qxT"], o["sxT"], rows=rows)
 
@@ -382,3 +384,83 @@ def test_backward_decoder_layer_full_size(li):
     layer = Layer(lin["x"], lin["w"], lin["dy"])
     check_backward(layer, _sample_rows(layer.M, (71, li, 0), k=8), _sample_rows(layer.N, (71, li, 1), k=8),
                    f"layer {lin['name']}")
+
+
+# ---- Dgrad from the weight codes as quantized (fp8_block_gemm_dgrad_w,
+# FP8BLK_OP_DGRAD_W): the oracle's Dgrad reads W[n][k] directly; the kernels
+# stage [n][k] tiles and form fragments with LDS transpose reads.  Each lane
+# then holds the same bytes in the same reduction order as with the
+# transposed copy, so the result must also equal the qwT path bit for bit.
+
+def check_dgrad_w(layer, algo_name, rows=None, what=""):
+    import torch
+    stats = check_op(layer, "dgrad_w", algo_name, rows=rows, what=what)
+    for dt in (torch.float32, torch.bfloat16):
+        a = layer.gpu("dgrad_w", ALGOS[algo_name], dt)
+        b = layer.gpu("dgrad", ALGOS[algo_name], dt)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), f"{what} {algo_name} {dt}: dgrad from qw differs from dgrad from qwT"
+    return stats
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+# reductions N with 128-block counts that are / are not multiples of 4 (the
+# fast kernel / the general one), ragged M, and output widths K that end
+# half-way through a 256-wide tile (the clamped column chunks)
+@pytest.mark.parametrize("shape", [(384, 640, 512), (640, 512, 384), (1024, 384, 640), (256, 1152, 128),
+                                   (640, 1024, 1152), (128, 512, 896)])
+def test_dgrad_w_small_shapes(algo, shape):
+    M, N, K = shape
+    key = (68, M, N, K)
+    layer = Layer(varied((M, K), 1.0, key + (0,)), varied((N, K), 0.02, key + (1,)),
+                  varied((M, N), 1e-3, key + (2,)))
+    check_dgrad_w(layer, algo, what="dgrad_w small")
+
+
+@pytest.mark.parametrize("li", range(4))
+def test_dgrad_w_and_backward_w_decoder_layer_full_size(li):
+    """Each linear of the decoder layer at 8192 tokens: Dgrad from qw against
+    the oracle on sampled rows and against the qwT path bit for bit; the
+    fused backward from qw against the fused backward from qwT, both
+    outputs bit for bit."""
+    import torch
+    lin = synth.decoder_layer(linears=(synth.LAYER_LINEARS[li],))[0]
+    layer = Layer(lin["x"], lin["w"], lin["dy"])
+    rows = _sample_rows(layer.M, (69, li), k=8)
+    check_dgrad_w(layer, "scaled", rows=rows, what=f"layer {lin['name']}")
+    g = layer.g
+    for dxt in (torch.bfloat16, torch.float32):
+        a = fb.fp8_block_gemm_backward_w(g["qdy"], g["sdy"], g["qw"], g["sw"], g["qdyT"], g["sdyT"], g["qxT"],
+                                         g["sxT"], dx_dtype=dxt)
+        b = fb.fp8_block_gemm_backward(g["qdy"], g["sdy"], g["qwT"], g["sw"], g["qdyT"], g["sdyT"], g["qxT"],
+                                       g["sxT"], dx_dtype=dxt)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), f"backward_w {lin['name']} {dxt}"
+
+
+@pytest.mark.parametrize("shape", [(1024, 512, 384), (512, 1024, 640), (384, 640, 512)])
+def test_backward_w_small(shape):
+    """The fused backward from qw (and its two-call fallback shapes) against
+    the oracle for both outputs."""
+    import torch
+    M, N, K = shape
+    key = (70, M, N, K)
+    layer = Layer(varied((M, K), 1.0, key + (0,)), varied((N, K), 0.02, key + (1,)),
+                  varied((M, N), 1e-3, key + (2,)))
+    g = layer.g
+    dx, dw = fb.fp8_block_gemm_backward_w(g["qdy"], g["sdy"], g["qw"], g["sw"], g["qdyT"], g["sdyT"], g["qxT"],
+                                          g["sxT"], dx_dtype=torch.float32, dw_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for out, op in ((dx, "dgrad"), (dw, "wgrad")):
+        y32, _, bound = layer.ref(op, np.arange(layer.out_rows(op)))
+        check_f32(host_f32(out), y32, bound, f"backward_w {op} {shape}")
+
+
+def test_dgrad_w_fp32_scales_promote():
+    """amax / 448 scales: the promote kernel's transposed-B configuration."""
+    M, N, K = 640, 1024, 384
+    key = (71, M, N, K)
+    layer = Layer(varied((M, K), 1.0, key + (0,)), varied((N, K), 0.02, key + (1,)),
+                  varied((M, N), 1e-3, key + (2,)), mode=1)
+    check_dgrad_w(layer, "promote", what="dgrad_w fp32 scales")
+
