@@ -40,12 +40,16 @@ KERNEL_SOURCES = ("blockwise_fp8_linear_amd/csrc/gemm_mx.hip", "blockwise_fp8_li
 
 
 def kernel_of(kind, algo):
-    """The kernel function a timed launch runs (Fprop and Dgrad share one)."""
+    """The kernel function a timed launch runs (Fprop and Dgrad from the
+    transposed weight copy share one)."""
     fast = algo in ("default", "scaled")
-    if kind in ("gemm_fprop", "gemm_dgrad"):
-        return "gemm_mx_kernel<false>" if fast else "gemm_kernel<promote, weight-block scales>"
+    bt = "true" if DGRAD_W else "false"
+    if kind == "gemm_fprop" or (kind == "gemm_dgrad" and not DGRAD_W):
+        return "gemm_mx_kernel<false, false>" if fast else "gemm_kernel<promote, weight-block scales>"
+    if kind == "gemm_dgrad":
+        return "gemm_mx_kernel<false, true>" if fast else "gemm_kernel<promote, weight-block scales, W as quantized>"
     if kind == "gemm_bwd":
-        return "gemm_mx_bwd_kernel (+ bwd_fixup_kernel)"
+        return f"gemm_mx_bwd_kernel<{bt}> (+ bwd_fixup_kernel)"
     if kind == "gemm_wgrad":
         return ("gemm_mx_streamk_kernel<true> (+ sk_fixup_kernel)" if fast
                 else "gemm_kernel<promote, row scales> (+ splitk_reduce_kernel)")
@@ -97,6 +101,9 @@ def parse():
                          "instead of the one-pass kernel")
     ap.add_argument("--separate-bwd", action="store_true",
                     help="run Dgrad and Wgrad as two calls instead of fp8_block_gemm_backward")
+    ap.add_argument("--transposed-weights", action="store_true",
+                    help="Dgrad reads a transposed weight copy written by the block quantizer (default: Dgrad "
+                         "reads the weight codes as quantized, and no copy is written)")
     ap.add_argument("--separate-wquant", action="store_true",
                     help="quantize each weight in its own launch instead of one batched launch per layer")
     ap.add_argument("--no-ceilings", action="store_true",
@@ -164,7 +171,7 @@ def build_layer(torch, fb, synth, seed, linears=LINEARS, x_in=None):
         d["qxT"] = torch.empty((k, TOKENS), dtype=u8, device="cuda")
         d["sxT"] = torch.empty((k, TOKENS // 128), dtype=f32, device="cuda")
         d["qw"] = torch.empty((n, k), dtype=u8, device="cuda")
-        d["qwT"] = torch.empty((k, n), dtype=u8, device="cuda")
+        d["qwT"] = None if DGRAD_W else torch.empty((k, n), dtype=u8, device="cuda")
         d["sw"] = torch.empty((n // 128, k // 128), dtype=f32, device="cuda")
         d["qdy"] = torch.empty((TOKENS, n), dtype=u8, device="cuda")
         d["sdy"] = torch.empty((TOKENS, n // 128), dtype=f32, device="cuda")
@@ -198,6 +205,9 @@ FUSED_BWD = True
 BATCH_W = True
 # Scale rule of every quantizer call (FP8BLK_SCALE_POW2 or FP8BLK_SCALE_FP32).
 SCALE_MODE = 0
+# True: Dgrad reads the weight codes W[n][k] as quantized (no transposed copy
+# written); False: the block quantizer also writes W^T's codes for Dgrad.
+DGRAD_W = True
 
 
 def quantize_both(fb, T, x, q, s, qT, sT):
@@ -215,16 +225,20 @@ def quantize_both(fb, T, x, q, s, qT, sT):
 def quantize_weights(fb, T, L):
     """All the weights of a layer (with their transposed copies), known when
     the step starts: one batched launch, or one launch per weight."""
+    per = 3 if DGRAD_W else 4     # bytes per weight: bf16 read, codes (and the transposed codes) written
     if BATCH_W:
-        nbytes = sum(d["N"] * d["K"] * 4 + (d["N"] // 128) * (d["K"] // 128) * 4 for d in L)
+        nbytes = sum(d["N"] * d["K"] * per + (d["N"] // 128) * (d["K"] // 128) * 4 for d in L)
         T.run("quant_block_batch", 0, nbytes,
-              lambda: fb.fp8_quantize_block_batch([d["w"] for d in L], outs=[(d["qw"], d["qwT"], d["sw"]) for d in L],
+              lambda: fb.fp8_quantize_block_batch([d["w"] for d in L],
+                                                  outs=[(d["qw"], None if DGRAD_W else d["qwT"], d["sw"]) for d in L],
                                                   scale_mode=SCALE_MODE))
     else:
         for d in L:
             n, k = d["N"], d["K"]
-            T.run("quant_block", 0, n * k * 4 + (n // 128) * (k // 128) * 4,
-                  lambda d=d: fb.fp8_quantize_block(d["w"], q=d["qw"], qT=d["qwT"], s=d["sw"], scale_mode=SCALE_MODE))
+            T.run("quant_block", 0, n * k * per + (n // 128) * (k // 128) * 4,
+                  lambda d=d: fb.fp8_quantize_block(d["w"], transpose=not DGRAD_W, q=d["qw"],
+                                                    qT=None if DGRAD_W else d["qwT"], s=d["sw"],
+                                                    scale_mode=SCALE_MODE))
 
 
 def fwd_linear(fb, T, d, algo, x=None):
@@ -241,13 +255,14 @@ def bwd_linear(fb, T, d, algo):
     n, k = d["N"], d["K"]
     quantize_both(fb, T, d["dy"], d["qdy"], d["sdy"], d["qdyT"], d["sdyT"])
     if FUSED_BWD and algo == fb.FP8BLK_ALGO_DEFAULT:
+        bwd = fb.fp8_block_gemm_backward_w if DGRAD_W else fb.fp8_block_gemm_backward
         T.run("gemm_bwd", 2 * 2.0 * TOKENS * n * k, 0,
-              lambda: fb.fp8_block_gemm_backward(d["qdy"], d["sdy"], d["qwT"], d["sw"], d["qdyT"], d["sdyT"],
-                                                 d["qxT"], d["sxT"], dx=d["dx"], dw=d["dw"], workspace=d["ws"]))
+              lambda: bwd(d["qdy"], d["sdy"], d["qw"] if DGRAD_W else d["qwT"], d["sw"], d["qdyT"], d["sdyT"],
+                          d["qxT"], d["sxT"], dx=d["dx"], dw=d["dw"], workspace=d["ws"]))
         return
     T.run("gemm_dgrad", 2.0 * TOKENS * n * k, 0,
-          lambda: fb.fp8_block_gemm(fb.FP8BLK_OP_DGRAD, d["qdy"], d["sdy"], d["qwT"], d["sw"], TOKENS, n, k,
-                                    algo=algo, out=d["dx"]))
+          lambda: fb.fp8_block_gemm(fb.FP8BLK_OP_DGRAD_W if DGRAD_W else fb.FP8BLK_OP_DGRAD, d["qdy"], d["sdy"],
+                                    d["qw"] if DGRAD_W else d["qwT"], d["sw"], TOKENS, n, k, algo=algo, out=d["dx"]))
     T.run("gemm_wgrad", 2.0 * TOKENS * n * k, 0,
           lambda: fb.fp8_block_gemm(fb.FP8BLK_OP_WGRAD, d["qdyT"], d["sdyT"], d["qxT"], d["sxT"], TOKENS, n, k,
                                     algo=algo, out=d["dw"], workspace=d["ws"]))
@@ -438,7 +453,8 @@ def main():
 
     fb.load_library()
     torch.cuda.set_device(0)
-    global DUAL, FUSED_BWD, BATCH_W, SCALE_MODE
+    global DUAL, FUSED_BWD, BATCH_W, SCALE_MODE, DGRAD_W
+    DGRAD_W = not args.transposed_weights
     DUAL = not args.separate_quant
     FUSED_BWD = not args.separate_bwd
     BATCH_W = not args.separate_wquant
@@ -555,6 +571,7 @@ def main():
                    "quantizer": "separate" if args.separate_quant else "one-pass",
                    "backward": "separate" if args.separate_bwd else "fused",
                    "weight_quant": "per weight" if args.separate_wquant else "batched per layer",
+                   "dgrad_weights": "transposed copy" if args.transposed_weights else "codes as quantized",
                    "gemm_tflop_per_step": round(step_flops / 1e12, 4)},
         "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
         "gemm_only_TFLOP/s": round(gemm_flops_t / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
