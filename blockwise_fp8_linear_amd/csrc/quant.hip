@@ -246,7 +246,8 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_batch_kernel(BlockJob
 // amax is a DPP reduction and each lane stores 8 codes per row.  Column
 // groups: a packed per-column max over the thread's rows, then over the 16
 // row blocks (wave shuffles, then LDS across the 4 waves); the thread's 8x8
-// codes are transposed in registers and each column's 8 codes stored.
+// codes are transposed in registers and staged in LDS, from where whole
+// 128-byte lines of the transposed output are stored.
 // ---------------------------------------------------------------------------
 constexpr int kDualThreads = 256;
 
@@ -263,6 +264,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ s,
     uint8_t* __restrict__ qT, int64_t ld_qT, float* __restrict__ sT, uint32_t row_tiles, uint32_t col_tiles) {
   __shared__ uint32_t red[kDualThreads / 64][16][4];
+  __shared__ __attribute__((aligned(16))) uint2 tq[128][16];  // column codes: [column][8-row block]
   const uint32_t t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // consecutive workgroups walk along the rows, so that the ones in flight
   // together read whole rows of x (measured: a few per cent faster than
@@ -325,16 +327,29 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     lo[i] = quant4_cols(v[i].x, v[i].y, &inv[0]);
     hi[i] = quant4_cols(v[i].z, v[i].w, &inv[4]);
   }
+  // The thread's 8x8 codes, transposed in registers (8 rows of one column
+  // per 8 bytes), go through LDS as tq[column][row block], the 8-byte unit
+  // XOR-swizzled by the column block cb, and leave as whole 128-byte lines of
+  // qT: 8 lanes per column, 16 bytes (two row blocks) each.
   uint32_t ta[4], tb[4];
   const int64_t cc = c0 + cb * 8;
   transpose4x4(&lo[0], ta);
   transpose4x4(&lo[4], tb);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2*>(qT + (cc + j) * ld_qT + r0) = make_uint2(ta[j], tb[j]);
+  for (int j = 0; j < 4; ++j) tq[cb * 8 + j][rb ^ cb] = make_uint2(ta[j], tb[j]);
   transpose4x4(&hi[0], ta);
   transpose4x4(&hi[4], tb);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2*>(qT + (cc + 4 + j) * ld_qT + r0) = make_uint2(ta[j], tb[j]);
+  for (int j = 0; j < 4; ++j) tq[cb * 8 + 4 + j][rb ^ cb] = make_uint2(ta[j], tb[j]);
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t c = k * 32 + (t >> 3), p = t & 7;
+    const uint32_t pu = (2 * p) ^ (c >> 3);  // physical unit of row block 2p
+    u32x4 w = *reinterpret_cast<const u32x4*>(&tq[c][pu & ~1u]);
+    if (pu & 1) w = u32x4{w[2], w[3], w[0], w[1]};  // the pair is stored swapped
+    *reinterpret_cast<u32x4*>(qT + (c0 + c) * ld_qT + m0 + 16 * p) = w;
+  }
   if (rb == 0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) sT[(cc + j) * row_tiles + rt] = inv[j].s;
