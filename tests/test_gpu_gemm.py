@@ -293,7 +293,7 @@ def test_wgrad_streamk_partitions(shape):
 # both output dimensions: Fprop and Dgrad on 17 x 17 = 289 tiles; Wgrad on
 # 17 x 16 tiles = one data-parallel wave plus stream-K over a ragged tile
 # row.
-@pytest.mark.parametrize("shape,ops", [((4224, 4224, 1024), ("fprop",)), ((4224, 1024, 4224), ("dgrad",)),
+@pytest.mark.parametrize("shape,ops", [((4224, 4224, 1024), ("fprop",)), ((4224, 1024, 4224), ("dgrad", "dgrad_w")),
                                        ((2048, 4224, 4096), ("wgrad",))])
 def test_many_tiles_ragged(shape, ops):
     M, N, K = shape
@@ -302,7 +302,7 @@ def test_many_tiles_ragged(shape, ops):
                   varied((M, N), 1e-3, key + (2,)))
     for op in ops:
         n = layer.out_rows(op)
-        rows = np.unique(np.concatenate([_sample_rows(n, key + (OPS.index(op),), k=12),
+        rows = np.unique(np.concatenate([_sample_rows(n, key + (len(op),), k=12),
                                          np.arange(n - 140, n)]))   # the whole ragged last tile row
         check_op(layer, op, "scaled", rows=rows, what="many tiles")
 
@@ -311,7 +311,7 @@ def test_many_tiles_ragged(shape, ops):
 # main-gradient case): the result must be exactly fl32(old + r), r being what
 # FP8BLK_OUT_FP32 stores, for every op, both algorithms, and the Wgrad paths
 # that sum partial tiles (stream-K fix-up, split-K reduction).
-@pytest.mark.parametrize("shape", [(1024, 4096, 6144), (2048, 256, 256), (640, 384, 1024)])
+@pytest.mark.parametrize("shape", [(1024, 4096, 6144), (2048, 256, 256), (640, 384, 1024), (4224, 4224, 512)])
 def test_fp32_accumulate(shape):
     import torch
     M, N, K = shape
@@ -321,6 +321,7 @@ def test_fp32_accumulate(shape):
     g = layer.g
     args = {"fprop": (fb.FP8BLK_OP_FPROP, g["qx"], g["sx"], g["qw"], g["sw"], (M, N)),
             "dgrad": (fb.FP8BLK_OP_DGRAD, g["qdy"], g["sdy"], g["qwT"], g["sw"], (M, K)),
+            "dgrad_w": (fb.FP8BLK_OP_DGRAD_W, g["qdy"], g["sdy"], g["qw"], g["sw"], (M, K)),
             "wgrad": (fb.FP8BLK_OP_WGRAD, g["qdyT"], g["sdyT"], g["qxT"], g["sxT"], (N, K))}
     gen = torch.Generator(device="cuda").manual_seed(68)
     for op, (opc, a, sa, b, sb, oshape) in args.items():
