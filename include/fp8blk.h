@@ -164,7 +164,8 @@ int fp8_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_
  *        row stride ld_w (>= cols, multiple of 8)
  *   q    [rows][cols] E4M3 codes, dense
  *   qT   optional (NULL to skip): [cols][rows] E4M3 codes, dense -- the
- *        transposed copy that Dgrad reads (block scales are the same)
+ *        transposed copy that fp8_block_gemm_dgrad reads (block scales are
+ *        the same); fp8_block_gemm_dgrad_w reads q itself and needs none
  *   s    [rows/128][cols/128] fp32 scales, dense
  *   rows and cols positive multiples of 128.
  */
