@@ -465,3 +465,34 @@ def test_dgrad_w_fp32_scales_promote():
                   varied((M, N), 1e-3, key + (2,)), mode=1)
     check_dgrad_w(layer, "promote", what="dgrad_w fp32 scales")
 
+
+
+# ---- a seeded sweep of shapes through the default path: every contraction
+# (Dgrad in both forms, the fused backward from the weight codes) against the
+# oracle on sampled rows.  Ragged tile edges, reductions whose 128-block count
+# is or is not a multiple of 4, and more tiles than CUs all come up.
+
+def _sweep_shapes(n=16):
+    rng = synth.rng_for(72, 0)
+    return [tuple(int(v) * 128 for v in rng.integers(1, (33, 25, 25))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("shape", _sweep_shapes())
+def test_shape_sweep_default_path(shape):
+    import torch
+    M, N, K = shape
+    key = (73, M, N, K)
+    layer = Layer(varied((M, K), 1.0, key + (0,)), varied((N, K), 0.02, key + (1,)),
+                  varied((M, N), 1e-3, key + (2,)))
+    for op in ("fprop", "dgrad", "wgrad"):
+        rows = _sample_rows(layer.out_rows(op), key + (len(op),), k=6)
+        check_op(layer, op, "scaled", rows=rows, what="sweep")
+    check_dgrad_w(layer, "scaled", rows=_sample_rows(M, key + (9,), k=6), what="sweep")
+    g = layer.g
+    dx, dw = fb.fp8_block_gemm_backward_w(g["qdy"], g["sdy"], g["qw"], g["sw"], g["qdyT"], g["sdyT"], g["qxT"],
+                                          g["sxT"], dx_dtype=torch.float32, dw_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for out, op in ((dx, "dgrad"), (dw, "wgrad")):
+        rows = _sample_rows(layer.out_rows(op), key + (10 + len(op),), k=6)
+        y32, _, bound = layer.ref(op, rows)
+        check_f32(host_f32(out)[rows], y32, bound, f"sweep backward_w {op} {shape}")
