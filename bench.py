@@ -3,22 +3,27 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input.
 Default workload ("layer"): one decoder layer's four linears (QKV 2048->4096,
-O 2048->2048, gate/up 2048->12288, down 6144->2048) at 8192 tokens, each
-doing row-group + column-group quantization of X, block quantization of W
-(with the transposed copy for Dgrad), Fprop, row-group + column-group
-quantization of dY, Dgrad and Wgrad -- 2.474 TFLOP of FP8 GEMM per step.
+O 2048->2048, gate/up 2048->12288, down 6144->2048) at 8192 tokens: the four
+weights block-quantized in one launch (no transposed copy: Dgrad reads the
+codes as quantized), then per linear one-pass row-group + column-group
+quantization of X, Fprop, one-pass quantization of dY, and Dgrad + Wgrad in
+one fused launch -- 2.474 TFLOP of FP8 GEMM per step.  --separate-quant,
+--separate-wquant, --transposed-weights and --separate-bwd switch each of
+these back to its plain form.
 
 Other workloads: "linear" (the 8192 x 2048 -> 12288 gate/up linear, quantize
 + Fprop only) and "stack28" (28 decoder layers, forward chained through the
 layer outputs, then backward, timed against the same GEMMs in bf16).
 
 Prints ONE JSON line.  Inputs are seeded synthetic tensors generated on the
-device before timing.  Per-launch durations come from HIP events recorded on
-the launch stream around every kernel of the timed steps.
+device before timing.  Durations come from HIP events recorded on the launch
+stream: around every launch in an untimed breakdown pass, around the
+dominant kernel's launches and at the step boundaries in the timed steps.
 """
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import platform
@@ -88,8 +93,8 @@ def measured_traffic(kernel, workload, algo):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5,
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10,
                     help="untimed steps before the timed ones (at least 1: the first also counts the launches)")
     ap.add_argument("--workload", choices=("layer", "linear", "stack28"), default="layer")
     ap.add_argument("--algo", choices=("default", "promote", "scaled"), default="default")
@@ -526,13 +531,29 @@ def main():
 
     # Timed steps: events only around the dominant kernel's launches (the
     # roofline's durations are measured here, live).
+    # An event at every step boundary on the stream the steps run on gives the
+    # spread of single-step times (recording an event does not synchronise).
+    # The host enqueues a step in roughly 0.3-1.2 ms against about 1.35 ms of
+    # GPU time, so a pause of the Python garbage collector could starve the
+    # GPU: collect now and keep it off while the timed steps are enqueued.
     T = Timer(torch, True, per_step * args.steps, only=dom_kinds)
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    bounds[0].record()
+    for i in range(args.steps):
         step(T)
+        bounds[i + 1].record()
+    enqueued = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
+    per_step_ms = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps))
+
+    def pct(p):
+        return round(per_step_ms[min(len(per_step_ms) - 1, int(p * len(per_step_ms)))], 4)
     ms = wall / args.steps * 1e3
     value = step_flops / (ms * 1e-3) / 1e12
 
@@ -561,6 +582,11 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms_spread": {"p10": pct(0.1), "median": pct(0.5), "p90": pct(0.9),
+                           "mean": round(sum(per_step_ms) / len(per_step_ms), 4),
+                           "host_enqueue_ms": round(enqueued / args.steps * 1e3, 4),
+                           "what": "single-step times from events at the step boundaries of the timed steps; "
+                                   "host_enqueue_ms: host time per step to enqueue them"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -43,8 +43,11 @@
  *     patterns (uint16_t), E4M3 codes as uint8_t, scales as float.
  *   - Dimensions and leading dimensions are in elements, int64_t.
  *   - Pointers are DEVICE pointers on the current HIP device.  The caller
- *     owns every buffer; the library allocates nothing, keeps no pointer
- *     after returning and holds no mutable global state.
+ *     owns every buffer; the library allocates nothing and keeps no pointer
+ *     after returning.  Its only global state is a per-device record that a
+ *     GEMM kernel's dynamic-LDS limit has been raised (set once, on the
+ *     kernel's first launch on that device; concurrent first calls repeat
+ *     the same idempotent attribute call).
  *   - Every call only enqueues work on `stream` (0 = the null stream) and
  *     never synchronises; results are valid once the stream has progressed
  *     past the call.  Outputs must not alias inputs.
