@@ -19,6 +19,10 @@ std::atomic<int> g_device_ok[kMaxDevices];
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool mult128(int64_t v) { return v > 0 && v % kGroup == 0; }
+// a * b <= limit for a, b > 0, without forming the (possibly overflowing) product
+bool prod_le(int64_t a, int64_t b, int64_t limit) { return a <= limit / b; }
+// a * b < limit, likewise
+bool prod_lt(int64_t a, int64_t b, int64_t limit) { return a < (limit + b - 1) / b; }
 bool valid_scale_mode(int m) { return m == FP8BLK_SCALE_POW2 || m == FP8BLK_SCALE_FP32; }
 
 int check_device() {
@@ -64,7 +68,8 @@ int fp8_quantize_rowgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   if (!x || !q || !s) return FP8BLK_ERR_NULL;
   if (rows <= 0 || !mult128(cols)) return FP8BLK_ERR_DIM;
   if (ld_x < cols || ld_q < cols) return FP8BLK_ERR_ARG;
-  if (rows * (cols / kGroup) >= (int64_t(1) << 31) || rows * ld_x > kMaxElems || rows * ld_q > kMaxElems)
+  if (!prod_lt(rows, cols / kGroup, int64_t(1) << 31) || !prod_le(rows, ld_x, kMaxElems) ||
+      !prod_le(rows, ld_q, kMaxElems))
     return FP8BLK_ERR_ARG;
   if (!aligned16(x) || !aligned16(q) || !aligned4(s) || ld_x % 8 || ld_q % 16) return FP8BLK_ERR_ALIGN;
   if (int rc = check_device()) return rc;
@@ -77,7 +82,8 @@ int fp8_quantize_colgroup(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   if (!x || !qT || !sT) return FP8BLK_ERR_NULL;
   if (!mult128(rows) || !mult128(cols)) return FP8BLK_ERR_DIM;
   if (ld_x < cols || ld_qT < rows) return FP8BLK_ERR_ARG;
-  if ((rows / 128) * (cols / 64) >= (int64_t(1) << 31) || rows * ld_x > kMaxElems || cols * ld_qT > kMaxElems)
+  if (!prod_lt(rows / 128, cols / 64, int64_t(1) << 31) || !prod_le(rows, ld_x, kMaxElems) ||
+      !prod_le(cols, ld_qT, kMaxElems))
     return FP8BLK_ERR_ARG;
   if (!aligned16(x) || !aligned16(qT) || !aligned4(sT) || ld_x % 8 || ld_qT % 16) return FP8BLK_ERR_ALIGN;
   if (int rc = check_device()) return rc;
@@ -90,8 +96,8 @@ int fp8_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_
   if (!x || !q || !s || !qT || !sT) return FP8BLK_ERR_NULL;
   if (!mult128(rows) || !mult128(cols)) return FP8BLK_ERR_DIM;
   if (ld_x < cols || ld_q < cols || ld_qT < rows) return FP8BLK_ERR_ARG;
-  if ((rows / 128) * (cols / 128) >= (int64_t(1) << 31) || rows * ld_x > kMaxElems || rows * ld_q > kMaxElems ||
-      cols * ld_qT > kMaxElems)
+  if (!prod_lt(rows / 128, cols / 128, int64_t(1) << 31) || !prod_le(rows, ld_x, kMaxElems) ||
+      !prod_le(rows, ld_q, kMaxElems) || !prod_le(cols, ld_qT, kMaxElems))
     return FP8BLK_ERR_ARG;
   if (!aligned16(x) || !aligned16(q) || !aligned16(qT) || !aligned4(s) || !aligned4(sT) || ld_x % 8 || ld_q % 16 ||
       ld_qT % 16)
@@ -107,7 +113,8 @@ static int check_block(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld
   if (!w || !q || !s) return FP8BLK_ERR_NULL;
   if (!mult128(rows) || !mult128(cols)) return FP8BLK_ERR_DIM;
   if (ld_w < cols) return FP8BLK_ERR_ARG;
-  if ((rows / 128) * (cols / 128) >= (int64_t(1) << 31) || rows * ld_w > kMaxElems || rows * cols > kMaxElems)
+  if (!prod_lt(rows / 128, cols / 128, int64_t(1) << 31) || !prod_le(rows, ld_w, kMaxElems) ||
+      !prod_le(rows, cols, kMaxElems))
     return FP8BLK_ERR_ARG;
   if (!aligned16(w) || !aligned16(q) || (qT && !aligned16(qT)) || !aligned4(s) || ld_w % 8) return FP8BLK_ERR_ALIGN;
   return FP8BLK_OK;
@@ -142,8 +149,8 @@ static int check_gemm_common(int64_t M, int64_t N, int64_t K, const void* a, con
     return FP8BLK_ERR_ARG;
   if (!a || !sa || !b || !sb || !out) return FP8BLK_ERR_NULL;
   if (!mult128(M) || !mult128(N) || !mult128(K)) return FP8BLK_ERR_DIM;
-  if (M * N > kMaxElems || M * K > kMaxElems || N * K > kMaxElems || M / 128 >= (1 << 20) || N / 128 >= (1 << 20) ||
-      K / 128 >= (1 << 20))
+  if (M / 128 >= (1 << 20) || N / 128 >= (1 << 20) || K / 128 >= (1 << 20) || !prod_le(M, N, kMaxElems) ||
+      !prod_le(M, K, kMaxElems) || !prod_le(N, K, kMaxElems))
     return FP8BLK_ERR_ARG;
   if (!aligned16(a) || !aligned16(b) || !aligned16(out) || !aligned4(sa) || !aligned4(sb)) return FP8BLK_ERR_ALIGN;
   return FP8BLK_OK;

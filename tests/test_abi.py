@@ -58,6 +58,24 @@ def test_rowgroup_errors(lib):
     assert f(P, 4, 256, 256, P2, 256, P3 + 2, 0, None) == EALIGN
 
 
+def test_size_limits_without_overflow(lib):
+    """Sizes whose products overflow 64 bits, or exceed what the kernels'
+    index arithmetic covers, are rejected with FP8BLK_ERR_ARG."""
+    big = 1 << 40                                                      # a multiple of 128
+    huge = 1 << 61
+    assert lib.fp8_quantize_rowgroup(P, huge, 128, 128, P2, 128, P3, 0, None) == EARG
+    assert lib.fp8_quantize_rowgroup(P, 1 << 20, big, big, P2, big, P3, 0, None) == EARG
+    assert lib.fp8_quantize_rowgroup(P, 4, 256, huge, P2, 256, P3, 0, None) == EARG   # ld_x too large
+    assert lib.fp8_quantize_colgroup(P, big, big, big, P2, big, P3, 0, None) == EARG
+    assert lib.fp8_quantize_dual(P, big, big, big, P2, big, P3, P2, big, P3, 0, None) == EARG
+    assert lib.fp8_quantize_block(P, big, big, big, P2, None, P3, 0, None) == EARG
+    f = lib.fp8_block_gemm_fprop
+    assert f(huge, huge, 256, P, P3, P2, P3, P, 0, None) == EARG
+    assert f(1 << 26, 1 << 26, 1 << 26, P, P3, P2, P3, P, 0, None) == EARG            # M * N > 2^40
+    assert lib.fp8_block_gemm_backward(huge, 256, 256, P, P3, P2, P3, P, P3, P2, P3, P, 0, P + 64, 0,
+                                       None, 0, None) == EARG
+
+
 def test_colgroup_and_block_errors(lib):
     f = lib.fp8_quantize_colgroup
     assert f(P, 200, 256, 256, P2, 256, P3, 0, None) == EDIM    # rows must be a multiple of 128
