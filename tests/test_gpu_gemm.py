@@ -496,3 +496,31 @@ def test_shape_sweep_default_path(shape):
         rows = _sample_rows(layer.out_rows(op), key + (10 + len(op),), k=6)
         y32, _, bound = layer.ref(op, rows)
         check_f32(host_f32(out)[rows], y32, bound, f"sweep backward_w {op} {shape}")
+
+
+# ---- the longest reduction the 256x256 kernel takes with weight-block
+# scales (128 blocks, every scale of the tile's block column held in LDS) and
+# the next length up (132 blocks: the general kernel, and the fused backward
+# falls back to two calls).
+
+@pytest.mark.parametrize("R", [128 * 128, 132 * 128])
+def test_weight_block_reduction_limit(R):
+    import torch
+    key = (74, R)
+    rows = _sample_rows(512, key + (0,), k=8)
+    # Fprop with K = R
+    fwd = Layer(varied((512, R), 1.0, key + (1,)), varied((384, R), 0.02, key + (2,)),
+                varied((512, 384), 1e-3, key + (3,)))
+    check_op(fwd, "fprop", "scaled", rows=rows, what="limit")
+    # Dgrad with N = R, both forms, and the backward from the weight codes
+    bwd = Layer(varied((512, 384), 1.0, key + (4,)), varied((R, 384), 0.02, key + (5,)),
+                varied((512, R), 1e-3, key + (6,)))
+    check_op(bwd, "dgrad", "scaled", rows=rows, what="limit")
+    check_dgrad_w(bwd, "scaled", rows=rows, what="limit")
+    g = bwd.g
+    dx, dw = fb.fp8_block_gemm_backward_w(g["qdy"], g["sdy"], g["qw"], g["sw"], g["qdyT"], g["sdyT"], g["qxT"],
+                                          g["sxT"], dx_dtype=torch.float32, dw_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for out, op, rr in ((dx, "dgrad", rows), (dw, "wgrad", _sample_rows(R, key + (7,), k=8))):
+        y32, _, bound = bwd.ref(op, rr)
+        check_f32(host_f32(out)[rr], y32, bound, f"limit backward_w {op} R={R}")
