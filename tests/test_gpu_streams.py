@@ -1,0 +1,66 @@
+"""Two host threads driving the library on two streams at once (ctypes
+releases the interpreter lock during the calls): the results equal those of
+a single-stream run.  The library keeps no per-call state outside the
+caller's buffers, so calls on different streams do not interfere."""
+import threading
+
+import pytest
+
+import blockwise_fp8_linear_amd as fb
+from blockwise_fp8_linear_amd import synth
+from gpu_util import dev_bf16, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _linear(x, w, dy, stream):
+    import torch
+    qw, _, sw = fb.fp8_quantize_block(w, transpose=False, stream=stream)
+    qx, sx, qxT, sxT = fb.fp8_quantize_dual(x, stream=stream)
+    y = fb.fp8_block_gemm_fprop(qx, sx, qw, sw, stream=stream)
+    qdy, sdy, qdyT, sdyT = fb.fp8_quantize_dual(dy, stream=stream)
+    dx, dw = fb.fp8_block_gemm_backward_w(qdy, sdy, qw, sw, qdyT, sdyT, qxT, sxT, dw_dtype=torch.float32,
+                                          stream=stream)
+    return y, dx, dw
+
+
+def test_two_threads_two_streams():
+    import torch
+    shapes = ((1024, 1536, 1024), (2048, 1024, 512))
+    inputs = []
+    for i, (M, N, K) in enumerate(shapes):
+        inputs.append((dev_bf16(synth.normal_bf16((M, K), 1.0, 81, 3 * i)),
+                       dev_bf16(synth.normal_bf16((N, K), 0.02, 81, 3 * i + 1)),
+                       dev_bf16(synth.normal_bf16((M, N), 1e-3, 81, 3 * i + 2))))
+    ref = [_linear(*inp, None) for inp in inputs]
+    torch.cuda.synchronize()
+
+    out = [[] for _ in inputs]
+    errors = []
+
+    def run(i):
+        try:
+            s = torch.cuda.Stream()  # default priority
+            with torch.cuda.stream(s):
+                for _ in range(10):
+                    out[i].append(_linear(*inputs[i], s))
+            s.synchronize()
+        except Exception as exc:  # reported below, on the main thread
+            errors.append(exc)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(len(inputs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    assert all(len(o) == 10 for o in out)
+    for i in range(len(inputs)):
+        for rep, res in enumerate(out[i]):
+            for name, a, b in zip(("y", "dx", "dw"), res, ref[i]):
+                assert torch.equal(a, b), f"shape {shapes[i]}, repetition {rep}: {name} differs"
