@@ -181,6 +181,47 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
   return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
 }
 
+// 16-byte direct global->LDS load: lane p's 16 bytes from base + voff land at
+// LDS offset lds_addr + 16 p (lds_addr wave-uniform, in M0).  Written as
+// inline assembly on purpose: the compiler would otherwise treat every
+// later LDS read as depending on every such load and drain them all
+// (vmcnt(0)) before it, which defeats the prefetch ring.  The kernel waits for
+// these loads itself with explicit vmcnt counts.  The block has no register
+// outputs; it sets M0 itself and the kernel has no other M0 users.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds_addr) {
+  // the base is wave-uniform but may have been computed in vector registers
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  // (readfirstlane returns int: go through uint32_t so the low half is not
+  // sign-extended into the high half)
+  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+// 4-byte variant: lane p's dword lands at lds_addr + 4 p.
+__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sb),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt low 4 bits and
+// bits 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // Workgroup barrier that orders LDS only.  (__syncthreads() also waits for
 // every outstanding global access, which would drain loads issued ahead of
 // time; those are waited for where their data is used.)

@@ -15,7 +15,8 @@
 //
 // Structure (per workgroup): a BM x BN output tile, the reduction walked in
 // 128-deep blocks.  Each block's A and B tiles (BM x 128 and BN x 128 bytes)
-// are staged in LDS, double buffered, with the 16-byte chunks of a row
+// go to LDS by direct global->LDS loads, double buffered (the next block
+// loads while this one is computed), with the 16-byte chunks of a row
 // XOR-swizzled by (row & 7) so that the MFMA fragment reads are free of bank
 // conflicts.  One v_mfma_*_16x16x128_f8f6f4 consumes exactly one 128-deep
 // block for a 16x16 sub-tile, so the per-block scale product is applied
@@ -64,9 +65,8 @@ struct Cfg {
   static constexpr int SA_BYTES = kChunk * BM * (int)sizeof(SType);
   static constexpr int SB_BYTES = (BROW ? kChunk * BN : kChunk * (BN / 128 > 0 ? BN / 128 : 1)) * (int)sizeof(SType);
   static constexpr int LDS = 2 * STAGE + SA_BYTES + ((SB_BYTES + 15) / 16) * 16;
-  static constexpr int A_LOADS = A_BYTES / 16 / THREADS;  // 16-byte chunks per thread
-  static constexpr int B_LOADS = B_BYTES / 16 / THREADS;
-  static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0, "tile/threads");
+  static_assert(A_BYTES % (1024 * (THREADS / 64)) == 0 && B_BYTES % (1024 * (THREADS / 64)) == 0,
+                "whole KiB of direct loads per wave");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must sit inside one 128-block");
   static_assert(TM % 4 == 0 || TM < 4, "scale bytes are read in words");
 };
@@ -111,6 +111,23 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* tile, uint32_t row, uint
   return f;
 }
 
+// p = the product of one 128-deep block (v_mfma_f32_16x16x128_f8f6f4 from
+// zero; srcA b, srcB a), into vector registers.  Inline assembly so that the
+// MFMA is issued exactly here, in the promotion pipeline's order; prev, the
+// product of an earlier sub-tile (untouched), passes through the statement
+// so that its promotion cannot be scheduled ahead of this MFMA.  The
+// compiler does not see an MFMA here, so the hazard it would handle is
+// covered by the order: every product is first read three MFMAs and two
+// promotions after its MFMA (more than the 12 wait states an MFMA result
+// needs before a vector-ALU read; the operands come from LDS reads, which
+// the compiler waits for).
+__device__ __forceinline__ void mfma16_zero(v4f& p, const v8i& b, const v8i& a) {
+  asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "=&v"(p) : "v"(b), "v"(a));
+}
+__device__ __forceinline__ void mfma16_zero(v4f& p, const v8i& b, const v8i& a, v4f& prev) {
+  asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %2, %3, 0" : "=&v"(p), "+v"(prev) : "v"(b), "v"(a));
+}
+
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t tiles_m, int64_t tiles_n,
                                                           int64_t kb_per_split) {
@@ -145,47 +162,44 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
   const int64_t kb_end = (kb_begin + kb_per_split) < nkb ? (kb_begin + kb_per_split) : nkb;
   const int64_t R = g.R;
 
-  // ---- global -> register staging of one reduction block's tiles
-  u32x4 ra[C::A_LOADS], rb[C::B_LOADS];
-  auto gload = [&](int64_t kb) {
+  // ---- direct global->LDS loads of one reduction block's tiles into stage
+  // buf.  Wave instruction u fills 8 rows x 128 B: lane p writes LDS bytes
+  // 16 p of that KiB, row p/8, physical chunk p%8, which holds logical chunk
+  // (p%8) ^ (row & 7).  Rows past an edge read the last row (BT: chunks past
+  // the column edge read the last valid one); their results are never stored.
+  constexpr int A_DMA = C::A_BYTES / 1024 / (C::THREADS / 64), B_DMA = C::B_BYTES / 1024 / (C::THREADS / 64);
+  const uint32_t lds0 = lds_offset(lds);
+  uint32_t offA[A_DMA], offB[B_DMA];
 #pragma unroll
-    for (int u = 0; u < C::A_LOADS; ++u) {
-      const uint32_t c = tid + u * C::THREADS;
-      int64_t row = i0 + (c >> 3);
-      row = row < g.I ? row : g.I - 1;  // rows past the end of a half tile: valid memory, result unused
-      ra[u] = *reinterpret_cast<const u32x4*>(g.a + row * R + kb * 128 + (c & 7) * 16);
-    }
+  for (int u = 0; u < A_DMA; ++u) {
+    const uint32_t row = (wave * A_DMA + u) * 8 + (lane >> 3);
+    int64_t gr = i0 + row;
+    gr = gr < g.I ? gr : g.I - 1;
+    offA[u] = (uint32_t)((gr - i0) * R) + (((lane & 7) ^ (row & 7)) << 4);
+  }
 #pragma unroll
-    for (int u = 0; u < C::B_LOADS; ++u) {
-      const uint32_t c = tid + u * C::THREADS;
-      if constexpr (C::BT) {
-        // reduction row kb * 128 + c / 8, columns j0 + 16 (c % 8) .. (a chunk
-        // past a ragged column edge reads the last valid one, never stored)
-        int64_t col = j0 + (c & 7) * 16;
-        col = col < g.J - 16 ? col : g.J - 16;
-        rb[u] = *reinterpret_cast<const u32x4*>(g.b + (kb * 128 + (c >> 3)) * g.J + col);
-      } else {
-        int64_t row = j0 + (c >> 3);
-        row = row < g.J ? row : g.J - 1;
-        rb[u] = *reinterpret_cast<const u32x4*>(g.b + row * R + kb * 128 + (c & 7) * 16);
-      }
+  for (int u = 0; u < B_DMA; ++u) {
+    const uint32_t row = (wave * B_DMA + u) * 8 + (lane >> 3);
+    if constexpr (C::BT) {
+      // reduction row kb * 128 + row, columns j0 + 16 * logical chunk ..
+      int64_t col = 16 * (int64_t)((lane & 7) ^ (row & 7));
+      col = j0 + col < g.J - 16 ? col : g.J - 16 - j0;
+      offB[u] = (uint32_t)(row * g.J + col);
+    } else {
+      int64_t gr = j0 + row;
+      gr = gr < g.J ? gr : g.J - 1;
+      offB[u] = (uint32_t)((gr - j0) * R) + (((lane & 7) ^ (row & 7)) << 4);
     }
-  };
-  auto lstore = [&](int buf) {
-    uint8_t* ta = tiles + buf * C::STAGE;
-    uint8_t* tb = ta + C::A_BYTES;
+  }
+  const uint8_t* const baseA = g.a + i0 * R;
+  const uint8_t* const baseB = C::BT ? g.b + j0 : g.b + j0 * R;
+  auto dma_block = [&](int64_t kb, int buf) {
+    const uint32_t st = lds0 + (uint32_t)buf * C::STAGE;
 #pragma unroll
-    for (int u = 0; u < C::A_LOADS; ++u) {
-      const uint32_t c = tid + u * C::THREADS;
-      const uint32_t row = c >> 3;
-      *reinterpret_cast<u32x4*>(ta + row * 128 + (((c & 7) ^ (row & 7)) << 4)) = ra[u];
-    }
+    for (int u = 0; u < A_DMA; ++u) dma16(baseA + kb * 128, offA[u], st + (wave * A_DMA + u) * 1024);
 #pragma unroll
-    for (int u = 0; u < C::B_LOADS; ++u) {
-      const uint32_t c = tid + u * C::THREADS;
-      const uint32_t row = c >> 3;
-      *reinterpret_cast<u32x4*>(tb + row * 128 + (((c & 7) ^ (row & 7)) << 4)) = rb[u];
-    }
+    for (int u = 0; u < B_DMA; ++u)
+      dma16(C::BT ? baseB + kb * 128 * g.J : baseB + kb * 128, offB[u], st + C::A_BYTES + (wave * B_DMA + u) * 1024);
   };
   // ---- scales of reduction blocks [kb0, kb0 + n) -> LDS (fp32 or E8M0).
   // sa_lds[kbl][i % 16][i / 16]; row-mode B: promote keeps [kbl][j], the
@@ -232,15 +246,16 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
   const uint32_t wm0 = wm * C::WM, wn0 = wn * C::WN;
 
   if (kb_begin < kb_end) {
-    gload(kb_begin);
+    dma_block(kb_begin, 0);
     load_scales(kb_begin, (kb_end - kb_begin) < kChunk ? (kb_end - kb_begin) : kChunk);
-    lstore(0);
+    wait_vmcnt<0>();
     __syncthreads();
   }
   for (int64_t kb = kb_begin; kb < kb_end; ++kb) {
     const int cur = (int)((kb - kb_begin) & 1);
     const bool more = kb + 1 < kb_end;
-    if (more) gload(kb + 1);
+    // the other stage was last read in the previous block, before its barrier
+    if (more) dma_block(kb + 1, cur ^ 1);
 
     const uint8_t* ta = tiles + cur * C::STAGE;
     const uint8_t* tb = ta + C::A_BYTES;
@@ -269,22 +284,47 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
       } else {
         sbv[0][0] = sb_lds[kbl * (C::BN / 128) + (wn0 >> 7)];
       }
+      // One MFMA per (ms, ns) sub-tile from zero, into one of four register
+      // buffers; its scaled product is added to the accumulators three
+      // sub-tiles later, so that the matrix core and the vector ALU work side
+      // by side and each product is read well after its MFMA has written it.
+      // Row tile ms+1's A fragment and scale are read during row tile ms,
+      // into one of three buffers (row ms-2's, no longer in use).
+      constexpr int STEPS = C::TM * C::TN, LAG = 3;
+      static_assert(C::TN >= LAG, "the lagging promotions reach back at most one row tile");
+      v8i af[3];
+      float sa[3];
+      af[0] = read_frag(ta, wm0 + l16, g4);
+      sa[0] = sa_row[0];
+      v4f pp[4];
 #pragma unroll
-      for (int ms = 0; ms < C::TM; ++ms) {
-        const v8i af = read_frag(ta, wm0 + ms * 16 + l16, g4);
-        const float sa = sa_row[ms];
-#pragma unroll
-        for (int ns = 0; ns < C::TN; ++ns) {
-          const v4f z = {0.f, 0.f, 0.f, 0.f};
-          const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[ns], af, z, 0, 0, 0, 0, 0, 0);
+      for (int k = 0; k < STEPS + LAG; ++k) {
+        if (k < STEPS) {
+          const int ms = k / C::TN, ns = k % C::TN;
+          if (k < LAG) mfma16_zero(pp[k & 3], bf[ns], af[ms % 3]);
+          else mfma16_zero(pp[k & 3], bf[ns], af[ms % 3], pp[(k - LAG) & 3]);
+          if (ns == 0 && ms + 1 < C::TM) {
+            af[(ms + 1) % 3] = read_frag(ta, wm0 + (ms + 1) * 16 + l16, g4);
+            sa[(ms + 1) % 3] = sa_row[ms + 1];
+          }
+        }
+        if (k >= LAG) {
+          const int j = k - LAG, ms = j / C::TN, ns = j % C::TN;
+          // the block's first product: only LAG MFMAs (and no promotions)
+          // were issued since its MFMA, so add the missing wait states
+          if (k == LAG) asm volatile("s_nop 4" : "+v"(pp[j & 3]));
+          const v4f p = pp[j & 3];
           if constexpr (C::BROW) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[ms][ns][t] = __builtin_fmaf(p[t], sa * sbv[ns][t], acc[ms][ns][t]);
+            for (int t = 0; t < 4; ++t)
+              acc[ms][ns][t] = __builtin_fmaf(p[t], sa[ms % 3] * sbv[ns][t], acc[ms][ns][t]);
           } else {
-            const float sc = sa * sbv[0][0];
+            const float sc = sa[ms % 3] * sbv[0][0];
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[ms][ns][t] = __builtin_fmaf(p[t], sc, acc[ms][ns][t]);
           }
+          // an empty marker: this promotion stays ahead of the next MFMA
+          asm volatile("" : "+v"(acc[ms][ns]));
         }
       }
     } else {
@@ -334,15 +374,13 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
       }
     }
 
-    if (more) {
-      if ((kb + 1 - kb_begin) % kChunk == 0) {
-        __syncthreads();  // everyone is done with this chunk's scales
-        const int64_t rest = kb_end - (kb + 1);
-        load_scales(kb + 1, rest < kChunk ? rest : kChunk);
-      }
-      lstore(cur ^ 1);
+    if (more && (kb + 1 - kb_begin) % kChunk == 0) {
+      __syncthreads();  // everyone is done with this chunk's scales
+      const int64_t rest = kb_end - (kb + 1);
+      load_scales(kb + 1, rest < kChunk ? rest : kChunk);
     }
-    __syncthreads();
+    wait_vmcnt<0>();  // this wave's loads of block kb+1 have landed
+    __syncthreads();  // ... and every wave's; no wave reads stage cur any more
   }
 
   // ---- epilogue: lane holds out[i0+wm0+ms*16+l16][j0+wn0+ns*16+g4*4 .. +3]

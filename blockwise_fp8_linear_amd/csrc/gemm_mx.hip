@@ -58,42 +58,6 @@ constexpr int LOADS_A = A_SLOT / 1024 / (THREADS / 64);  // 1 KiB per wave instr
 constexpr int LOADS_B = B_SLOT / 1024 / (THREADS / 64);
 constexpr int LOADS_PER_PAIR = LOADS_A + LOADS_B;          // per wave
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16-byte direct global->LDS load: lane p's 16 bytes from base + voff land at
-// LDS offset lds_addr + 16 p (lds_addr wave-uniform, in M0).  Written as
-// inline assembly on purpose: the compiler would otherwise treat every
-// later LDS read as depending on every such load and drain them all
-// (vmcnt(0)) before it, which defeats the prefetch ring.  The kernel waits for
-// these loads itself with explicit vmcnt counts.  The block has no register
-// outputs; it sets M0 itself and the kernel has no other M0 users.
-__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds_addr) {
-  // the base is wave-uniform but may have been computed in vector registers
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  // (readfirstlane returns int: go through uint32_t so the low half is not
-  // sign-extended into the high half)
-  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
-                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb),
-               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory", "m0");
-}
-
-// 4-byte variant: lane p's dword lands at lds_addr + 4 p.
-__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, uint32_t lds_addr) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
-                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sb),
-               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
-}
-
-
 template <int V>
 struct IntC {
   static constexpr int value = V;
@@ -112,14 +76,6 @@ __device__ __forceinline__ uint32_t swz(uint32_t row) { return ((row & 31) ^ ((r
 // chunk positions, i.e. distinct banks.
 __device__ __forceinline__ uint32_t swz_bt(uint32_t row) { return 2 * (row & 7); }
 
-
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt low 4 bits and
-// bits 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 // fp32 power-of-two scales -> E8M0 bytes (their exponent fields), 4 packed.
 __device__ __forceinline__ uint32_t pack_e8(u32x4 s) {
