@@ -167,39 +167,46 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
   // 16 p of that KiB, row p/8, physical chunk p%8, which holds logical chunk
   // (p%8) ^ (row & 7).  Rows past an edge read the last row (BT: chunks past
   // the column edge read the last valid one); their results are never stored.
+  // Each instruction has its own wave-uniform base at its first row, so the
+  // per-lane 32-bit offsets stay below 8 rows (the reduction length is
+  // unrestricted here).
   constexpr int A_DMA = C::A_BYTES / 1024 / (C::THREADS / 64), B_DMA = C::B_BYTES / 1024 / (C::THREADS / 64);
   const uint32_t lds0 = lds_offset(lds);
+  const uint8_t* baseA[A_DMA];
+  const uint8_t* baseB[B_DMA];
   uint32_t offA[A_DMA], offB[B_DMA];
 #pragma unroll
   for (int u = 0; u < A_DMA; ++u) {
-    const uint32_t row = (wave * A_DMA + u) * 8 + (lane >> 3);
-    int64_t gr = i0 + row;
-    gr = gr < g.I ? gr : g.I - 1;
-    offA[u] = (uint32_t)((gr - i0) * R) + (((lane & 7) ^ (row & 7)) << 4);
+    const uint32_t r8 = (wave * A_DMA + u) * 8, row = r8 + (lane >> 3);
+    const int64_t g0 = (i0 + r8) < g.I ? (i0 + r8) : g.I - 1;
+    const int64_t gr = (i0 + row) < g.I ? (i0 + row) : g.I - 1;
+    baseA[u] = g.a + g0 * R;
+    offA[u] = (uint32_t)((gr - g0) * R) + (((lane & 7) ^ (row & 7)) << 4);
   }
 #pragma unroll
   for (int u = 0; u < B_DMA; ++u) {
-    const uint32_t row = (wave * B_DMA + u) * 8 + (lane >> 3);
+    const uint32_t r8 = (wave * B_DMA + u) * 8, row = r8 + (lane >> 3);
     if constexpr (C::BT) {
       // reduction row kb * 128 + row, columns j0 + 16 * logical chunk ..
       int64_t col = 16 * (int64_t)((lane & 7) ^ (row & 7));
       col = j0 + col < g.J - 16 ? col : g.J - 16 - j0;
-      offB[u] = (uint32_t)(row * g.J + col);
+      baseB[u] = g.b + (int64_t)r8 * g.J + j0;
+      offB[u] = (uint32_t)((lane >> 3) * g.J + col);
     } else {
-      int64_t gr = j0 + row;
-      gr = gr < g.J ? gr : g.J - 1;
-      offB[u] = (uint32_t)((gr - j0) * R) + (((lane & 7) ^ (row & 7)) << 4);
+      const int64_t g0 = (j0 + r8) < g.J ? (j0 + r8) : g.J - 1;
+      const int64_t gr = (j0 + row) < g.J ? (j0 + row) : g.J - 1;
+      baseB[u] = g.b + g0 * R;
+      offB[u] = (uint32_t)((gr - g0) * R) + (((lane & 7) ^ (row & 7)) << 4);
     }
   }
-  const uint8_t* const baseA = g.a + i0 * R;
-  const uint8_t* const baseB = C::BT ? g.b + j0 : g.b + j0 * R;
   auto dma_block = [&](int64_t kb, int buf) {
     const uint32_t st = lds0 + (uint32_t)buf * C::STAGE;
 #pragma unroll
-    for (int u = 0; u < A_DMA; ++u) dma16(baseA + kb * 128, offA[u], st + (wave * A_DMA + u) * 1024);
+    for (int u = 0; u < A_DMA; ++u) dma16(baseA[u] + kb * 128, offA[u], st + (wave * A_DMA + u) * 1024);
 #pragma unroll
     for (int u = 0; u < B_DMA; ++u)
-      dma16(C::BT ? baseB + kb * 128 * g.J : baseB + kb * 128, offB[u], st + C::A_BYTES + (wave * B_DMA + u) * 1024);
+      dma16(C::BT ? baseB[u] + kb * 128 * g.J : baseB[u] + kb * 128, offB[u],
+            st + C::A_BYTES + (wave * B_DMA + u) * 1024);
   };
   // ---- scales of reduction blocks [kb0, kb0 + n) -> LDS (fp32 or E8M0).
   // sa_lds[kbl][i % 16][i / 16]; row-mode B: promote keeps [kbl][j], the
