@@ -24,6 +24,8 @@
 //   PROMOTE = true : P = MFMA(A_b, B_b) from zero, then
 //                    acc = fma(P, fl32(sa*sb), acc) on the VALU, in fp32 --
 //                    any fp32 scales, so it also serves the amax / 448 rule;
+//                    each sub-tile's promotion runs three MFMAs behind its
+//                    MFMA, so the matrix core and the VALU overlap;
 //   PROMOTE = false: the gfx950 block-scaled MFMA, which multiplies each
 //                    operand row by its power-of-two scale (an E8M0 byte:
 //                    the fp32 scale's exponent field) inside the matrix core
