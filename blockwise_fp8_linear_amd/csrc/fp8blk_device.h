@@ -185,9 +185,10 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
 // LDS offset lds_addr + 16 p (lds_addr wave-uniform, in M0).  Written as
 // inline assembly on purpose: the compiler would otherwise treat every
 // later LDS read as depending on every such load and drain them all
-// (vmcnt(0)) before it, which defeats the prefetch ring.  The kernel waits for
-// these loads itself with explicit vmcnt counts.  The block has no register
-// outputs; it sets M0 itself and the kernel has no other M0 users.
+// (vmcnt(0)) before it, which defeats loading ahead.  The GEMM kernels wait
+// for these loads themselves with explicit vmcnt counts.  The block has no
+// register outputs; it sets M0 itself, and those kernels have no other M0
+// users.
 __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds_addr) {
   // the base is wave-uniform but may have been computed in vector registers
   const uint64_t b = reinterpret_cast<uint64_t>(base);
@@ -210,6 +211,7 @@ __device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, uint32_
                : "memory", "m0");
 }
 
+// The LDS byte address of a pointer into the workgroup's shared memory.
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
 }
