@@ -1,5 +1,8 @@
-"""Hazard bookkeeping of the inline-assembly MFMAs in gemm.hip's promotion
-pipeline, checked on the gfx950 assembly the compiler produces (host only).
+"""Assumptions the GEMM kernels make about the code the compiler produces,
+checked on the gfx950 assembly (host only).
+
+1. Hazard bookkeeping of the inline-assembly MFMAs in gemm.hip's promotion
+pipeline.
 
 Those MFMAs are written as inline assembly, so the compiler does not insert
 the wait states an MFMA result needs before a vector-ALU read (12 for this
@@ -10,7 +13,12 @@ every such MFMA in every instantiation, that
   * its destination registers are first read at least 12 wait states later
     (each instruction counts one, s_nop N counts N + 1), and
   * no vector-ALU instruction writes its A or B operand within the 3 wait
-    states before it."""
+    states before it.
+
+2. gemm_mx.hip's kernels count their direct global->LDS loads with partial
+vmcnt waits, which holds because loads complete in order.  A register spill
+would put scratch stores among them, and stores may complete out of order
+with loads, so those kernels must use no scratch memory."""
 import os
 import re
 import shutil
@@ -115,3 +123,20 @@ def test_operands_not_written_by_valu_just_before(asm):
             seen += _states(op2, ops2)
             if seen >= 3:
                 break
+
+
+def test_gemm_mx_kernels_use_no_scratch(tmp_path):
+    if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
+        pytest.skip("no hipcc")
+    out = str(tmp_path / "gemm_mx.s")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Wno-inline-asm", "-Wno-unused-function",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
+           "--cuda-device-only", "-S", "-o", out, os.path.join(CSRC, "gemm_mx.hip")]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    text = open(out).read()
+    kernels = re.findall(r"\.name:\s+(\S+)\n(?:.*\n)*?\s+\.private_segment_fixed_size:\s+(\d+)", text)
+    assert any("gemm_mx" in k for k, _ in kernels)
+    assert len(kernels) == text.count(".private_segment_fixed_size:")
+    for name, priv in kernels:
+        assert int(priv) == 0, f"{name} uses {priv} bytes of scratch"
+    assert "scratch_store" not in text and "buffer_store_dword" not in text.replace("buffer_store_dwordx", "")
