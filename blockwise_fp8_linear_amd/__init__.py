@@ -107,6 +107,9 @@ def _dev(t, dtype, name, ndim=2):
         raise TypeError(f"{name}: expected a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name}: must be a device tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name}: on {t.device}, but the library launches on the current device "
+                         f"cuda:{torch.cuda.current_device()}")
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
     if t.dim() != ndim:

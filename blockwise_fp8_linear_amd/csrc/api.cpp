@@ -278,6 +278,7 @@ int fp8_block_gemm_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* qdyT, c
 
 size_t fp8_block_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
   if (!mult128(M) || !mult128(N) || !mult128(K)) return (size_t)-1;
+  if (M / 128 >= (1 << 20) || N / 128 >= (1 << 20) || K / 128 >= (1 << 20)) return (size_t)-1;
   switch (op) {
     case FP8BLK_OP_FPROP: return fp8blk::gemm_workspace_bytes(M, N, K, fp8blk::BScale::Block);
     case FP8BLK_OP_DGRAD:

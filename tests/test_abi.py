@@ -209,6 +209,11 @@ def test_workspace_query(lib):
     assert n >= 2 * 256 * 256 * 256 * 4 and n >= 2 * 2048 * 2048 * 4
     # a 512-token reduction is one unit per tile: no tile is shared
     assert q(2, 512, 5120, 7680) == 0
+    # dimensions the GEMM entry points reject are invalid shapes here too
+    big = 128 << 20
+    for op in (0, 1, 2, 3, 4):
+        assert q(op, big, 256, 256) == ctypes.c_size_t(-1).value
+        assert q(op, 256, 256, big) == ctypes.c_size_t(-1).value
 
 
 def test_valid_call_without_gpu_reports_device_error(lib):
