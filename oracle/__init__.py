@@ -37,9 +37,14 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_SO):
-        build()
-    lib = ctypes.CDLL(_SO)
+    # The mutation tests point this at a deliberately broken build of
+    # oracle.c, to show that the pins catch the mistake.
+    path = os.environ.get("FP8BLK_ORACLE_LIB")
+    if path is None:
+        if not os.path.exists(_SO):
+            build()
+        path = _SO
+    lib = ctypes.CDLL(path)
     u8p = ctypes.POINTER(ctypes.c_uint8)
     u16p = ctypes.POINTER(ctypes.c_uint16)
     f32p = ctypes.POINTER(ctypes.c_float)
