@@ -44,10 +44,11 @@
  *   - Dimensions and leading dimensions are in elements, int64_t.
  *   - Pointers are DEVICE pointers on the current HIP device.  The caller
  *     owns every buffer; the library allocates nothing and keeps no pointer
- *     after returning.  Its only global state is a per-device record that a
- *     GEMM kernel's dynamic-LDS limit has been raised (set once, on the
- *     kernel's first launch on that device; concurrent first calls repeat
- *     the same idempotent attribute call).
+ *     after returning.  Its only global state is two per-device records,
+ *     each set once: whether the device is a gfx950 (looked up on the first
+ *     call on it) and whether a GEMM kernel's dynamic-LDS limit has been
+ *     raised (on the kernel's first launch there).  Concurrent first calls
+ *     only repeat the same idempotent lookup or attribute call.
  *   - Every call only enqueues work on `stream` (0 = the null stream) and
  *     never synchronises; results are valid once the stream has progressed
  *     past the call.  Outputs must not alias inputs.

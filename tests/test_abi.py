@@ -3,10 +3,15 @@ function include/fp8blk.h declares, and every host-side argument check
 returns its documented status before anything is launched (the pointers
 below are never dereferenced: each call fails validation first)."""
 import ctypes
+import os
+import shutil
+import subprocess
 
 import pytest
 
 import blockwise_fp8_linear_amd as fb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 OK, ENULL, EDIM, EALIGN, EARG, EWS, EHIP, EDEV = 0, -1, -2, -3, -4, -5, -6, -7
 P = 0x100000          # a fake, 16-byte aligned device address (never used)
@@ -249,3 +254,19 @@ def test_probe_library():
     assert p.fp8probe_mfma(0, 10, 1, P, None) == -1
     assert p.fp8probe_mfma(256, 0, 1, P, None) == -1
     assert p.fp8probe_mfma(256, 10, 1, None, None) == -1
+
+
+def test_c_program_against_the_header(tmp_path):
+    """include/fp8blk.h compiles as strict C99, every entry point links, and
+    each rejects a bad argument with the documented status (no GPU needed:
+    no call reaches the device)."""
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    libdir = os.path.dirname(fb.LIB_PATH)
+    exe = str(tmp_path / "abi_from_c")
+    subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-isystem", "/opt/rocm/include",
+                    os.path.join(ROOT, "tests", "abi_from_c.c"), "-o", exe,
+                    "-L", libdir, "-l:libfp8blk.so", f"-Wl,-rpath,{libdir}"], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
