@@ -100,7 +100,7 @@ def _killed(so):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *PINS],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     if r.returncode not in (0, 1):
-        # 1 is "some test failed"; anything else (a crash, a usage error) is not a verdict
+        # 1 is "some test failed"; anything else (a crash, a usage error) decides nothing
         raise RuntimeError(f"pin run ended with {r.returncode}:\n{r.stdout[-2000:]}\n{r.stderr[-2000:]}")
     return r.returncode == 1
 
