@@ -99,7 +99,17 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 //    contrasts with the power-of-two one): s = fl32(amax / 448), 1 for an
 //    all-zero group, and the value fl32(x / s), clamped to +-448 (the cast
 //    saturates; the rounded quotient of the amax itself may exceed 448 by
-//    an ulp).  Both divisions are IEEE-correctly rounded.
+//    an ulp).  The scale is an IEEE-correctly rounded division.  The
+//    quotient is not divided per element: y = x * r with r = fl32(1 / s),
+//    then one Newton-Markstein correction y + (x - s y) r, whose residual
+//    the fused multiply-add forms exactly.  Tiny scales are first brought
+//    up by 2^64 together with x (both products exact, the quotient
+//    unchanged), so that 1 / s cannot overflow and the residual cannot
+//    underflow.  The sign is copied from x, which keeps the sign of zero.
+//    Fp32ScaleDiv is the same rule with a plain division per element; the
+//    measurement probe checks that the two give the same E4M3 code for
+//    every bf16 amax and every bf16 x with |x| <= amax, i.e. for every
+//    element a quantizer can see.
 struct Pow2Scale {
   float s, inv;
   __device__ __forceinline__ explicit Pow2Scale(uint32_t amax_bits) {
@@ -111,8 +121,27 @@ struct Pow2Scale {
 };
 
 struct Fp32Scale {
-  float s;
+  float s;      // the stored scale
+  float f;      // 2^64 if s < 2^-64, else 1
+  float sf, r;  // s * f (exact) and fl32(1 / (s * f))
   __device__ __forceinline__ explicit Fp32Scale(uint32_t amax_bits) {
+    s = amax_bits == 0 ? 1.0f : __uint_as_float(amax_bits << 16) / 448.0f;
+    f = s < 0x1p-64f ? 0x1p64f : 1.0f;
+    sf = s * f;
+    r = 1.0f / sf;
+  }
+  __device__ __forceinline__ float operator()(float x) const {
+    const float xf = x * f;
+    const float y = xf * r;
+    const float e = __builtin_fmaf(-sf, y, xf);
+    const float v = __builtin_copysignf(__builtin_fmaf(e, r, y), x);
+    return __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
+  }
+};
+
+struct Fp32ScaleDiv {
+  float s;
+  __device__ __forceinline__ explicit Fp32ScaleDiv(uint32_t amax_bits) {
     s = amax_bits == 0 ? 1.0f : __uint_as_float(amax_bits << 16) / 448.0f;
   }
   __device__ __forceinline__ float operator()(float x) const {

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fp8blk_device.h"
 #include "fp8probe.h"
 
 namespace {
@@ -59,7 +60,35 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, uint32_t see
   out[gid] = s;
 }
 
+// Every element a quantizer under the amax / 448 rule can see: block
+// (x, y) takes the group amax with bf16 bits y (0 .. 0x7F7F, every
+// non-negative finite value) and thread t the magnitude bits
+// m = 256 x + t <= y, with both signs.  The quantizers' reciprocal-based
+// quotient (Fp32Scale) and a plain IEEE division (Fp32ScaleDiv) must give
+// the same stored scale and the same E4M3 code; each block writes how many
+// of its threads found a difference.
+__global__ __launch_bounds__(256) void quotient_check_kernel(uint32_t* counts) {
+  const uint32_t a = blockIdx.y, m = blockIdx.x * 256 + threadIdx.x;
+  bool bad = false;
+  if (m <= a) {
+    const fp8blk::Fp32Scale fast(a);
+    const fp8blk::Fp32ScaleDiv ref(a);
+    const float xp = __uint_as_float(m << 16);
+    const int cf = __builtin_amdgcn_cvt_pk_fp8_f32(fast(xp), fast(-xp), 0, false);
+    const int cr = __builtin_amdgcn_cvt_pk_fp8_f32(ref(xp), ref(-xp), 0, false);
+    bad = ((cf ^ cr) & 0xFFFF) != 0 || __float_as_uint(fast.s) != __float_as_uint(ref.s);
+  }
+  const int n = __syncthreads_count(bad);
+  if (threadIdx.x == 0) counts[blockIdx.y * gridDim.x + blockIdx.x] = (uint32_t)n;
+}
+
 }  // namespace
+
+extern "C" int fp8probe_fp32_quotient_check(uint32_t* counts, hipStream_t stream) {
+  if (counts == nullptr) return -1;
+  hipLaunchKernelGGL(quotient_check_kernel, dim3(128, 0x7F80), dim3(256), 0, stream, counts);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
 
 extern "C" int fp8probe_mfma(int workgroups, int iters, uint32_t seed, float* out, hipStream_t stream) {
   if (workgroups <= 0 || iters <= 0 || out == nullptr) return -1;

@@ -1,7 +1,8 @@
 /*
  * fp8probe.h -- measurement probe shipped beside libfp8blk (libfp8probe.so).
  * Not part of the hot path: the benchmark uses it to state an on-box ceiling
- * for the block-scaled FP8 matrix-core work of the GEMM kernels.
+ * for the block-scaled FP8 matrix-core work of the GEMM kernels, and a test
+ * uses it to check the amax / 448 quantizers' quotient exhaustively.
  */
 #ifndef FP8PROBE_H
 #define FP8PROBE_H
@@ -25,6 +26,19 @@ int fp8probe_mfma(int workgroups, int iters, uint32_t seed, float *out, hipStrea
 
 /* The FLOP count of one fp8probe_mfma call (2 per multiply-add). */
 double fp8probe_mfma_flops(int workgroups, int iters);
+
+/*
+ * Check, on the device, the quantizers' quotient under FP8BLK_SCALE_FP32
+ * against a plain IEEE division, for every element a quantizer can see:
+ * every non-negative finite bf16 group amax a (bits 0 .. 0x7F7F) with every
+ * bf16 x, |x| <= a, of either sign.  Both must give the same stored scale
+ * fl32(a / 448) (1 for a = 0) and the same E4M3 code of x / s (clamped to
+ * +-448).  counts: device buffer of FP8PROBE_QCHECK_BLOCKS uint32; entry
+ * 128 a + j receives how many of the magnitudes 256 j .. 256 j + 255 differ.
+ * Returns 0, -1 for a NULL buffer, -6 if the launch failed.
+ */
+#define FP8PROBE_QCHECK_BLOCKS (128 * 0x7F80)
+int fp8probe_fp32_quotient_check(uint32_t *counts, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -376,3 +376,28 @@ def test_fp32_scale_block():
     _, w = synth.single_linear()
     _assert_block(w, "12288x2048 W", mode=FP32)
 
+
+
+def test_fp32_scale_quotient_exhaustive():
+    """Under the amax/448 rule the quantizers form x/s from a reciprocal and
+    one fused-multiply-add correction.  The probe compares that with a plain
+    IEEE division for every non-negative finite bf16 amax and every bf16 x
+    with |x| <= amax, both signs (about 10^9 elements, every element a
+    quantizer can see): the stored scale and the E4M3 code must agree.  The
+    oracle divides; the tests above tie the quantizers to it on their inputs,
+    and this check extends the agreement to all inputs."""
+    import ctypes
+    import os
+    import torch
+    import blockwise_fp8_linear_amd as fb
+    note("fp8probe_fp32_quotient_check: grid 128 x 32640")
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(fb.LIB_PATH), "libfp8probe.so"))
+    lib.fp8probe_fp32_quotient_check.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.fp8probe_fp32_quotient_check.restype = ctypes.c_int
+    counts = torch.full((128 * 0x7F80,), -1, dtype=torch.int32, device="cuda")
+    assert lib.fp8probe_fp32_quotient_check(counts.data_ptr(), torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    c = host(counts)
+    assert c.min() >= 0, "the probe left blocks unwritten"
+    bad = np.flatnonzero(c)
+    assert bad.size == 0, f"{int(c.sum())} elements differ; first at amax bits {hex(int(bad[0]) // 128)}"
