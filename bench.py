@@ -259,7 +259,7 @@ def fwd_linear(fb, T, d, algo, x=None):
     quantize_both(fb, T, x, d["qx"], d["sx"], d["qxT"], d["sxT"])
     T.run("gemm_fprop", 2.0 * TOKENS * n * k, 0,
           lambda: fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, d["qx"], d["sx"], d["qw"], d["sw"], TOKENS, n, k,
-                                    algo=algo, out=d["y"]))
+                                    algo=algo, out=d["y"], scale_mode=SCALE_MODE))
     return d["y"]
 
 
@@ -274,10 +274,11 @@ def bwd_linear(fb, T, d, algo):
         return
     T.run("gemm_dgrad", 2.0 * TOKENS * n * k, 0,
           lambda: fb.fp8_block_gemm(fb.FP8BLK_OP_DGRAD_W if DGRAD_W else fb.FP8BLK_OP_DGRAD, d["qdy"], d["sdy"],
-                                    d["qw"] if DGRAD_W else d["qwT"], d["sw"], TOKENS, n, k, algo=algo, out=d["dx"]))
+                                    d["qw"] if DGRAD_W else d["qwT"], d["sw"], TOKENS, n, k, algo=algo, out=d["dx"],
+                                    scale_mode=SCALE_MODE))
     T.run("gemm_wgrad", 2.0 * TOKENS * n * k, 0,
           lambda: fb.fp8_block_gemm(fb.FP8BLK_OP_WGRAD, d["qdyT"], d["sdyT"], d["qxT"], d["sxT"], TOKENS, n, k,
-                                    algo=algo, out=d["dw"], workspace=d["ws"]))
+                                    algo=algo, out=d["dw"], workspace=d["ws"], scale_mode=SCALE_MODE))
 
 
 def layer_step(fb, T, L, algo):
@@ -296,7 +297,7 @@ def linear_step(fb, T, d, algo):
           lambda: fb.fp8_quantize_block(d["w"], transpose=False, q=d["qw"], s=d["sw"], scale_mode=SCALE_MODE))
     T.run("gemm_fprop", 2.0 * TOKENS * n * k, 0,
           lambda: fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, d["qx"], d["sx"], d["qw"], d["sw"], TOKENS, n, k,
-                                    algo=algo, out=d["y"]))
+                                    algo=algo, out=d["y"], scale_mode=SCALE_MODE))
 
 
 def stack_step(fb, T, layers, algo):

@@ -61,10 +61,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fp8_block_gemm_fprop": [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp],
         "fp8_block_gemm_dgrad": [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp],
         "fp8_block_gemm_wgrad": [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, sz, vp],
-        "fp8_block_gemm": [i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp],
-        "fp8_block_gemm_backward": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, vp, sz, vp],
+        "fp8_block_gemm": [i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, i32, i32, vp, sz, vp],
+        "fp8_block_gemm_backward": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, sz,
+                                    vp],
         "fp8_block_gemm_dgrad_w": [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp],
-        "fp8_block_gemm_backward_w": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, vp, sz, vp],
+        "fp8_block_gemm_backward_w": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, sz,
+                                      vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -126,6 +128,30 @@ def _dense(t, dtype, name):
     return t
 
 
+def _shape(t, shape, name):
+    """The kernels read and write exactly the extents the C call is given, so
+    every tensor must have the shape those extents imply: a smaller one would
+    be accessed out of bounds on the device."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _on(stream):
+    """Context in which tensors the call allocates belong to the stream it
+    launches on, so that torch's caching allocator never hands their memory
+    to other work before that stream has finished with it."""
+    import contextlib
+    import torch
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _new(shape, dtype, device, stream):
+    import torch
+    with _on(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 # -------------------------------------------------------------- quantizers --
 
 def fp8_quantize_rowgroup(x, q=None, s=None, stream=None, scale_mode=FP8BLK_SCALE_POW2):
@@ -136,8 +162,10 @@ def fp8_quantize_rowgroup(x, q=None, s=None, stream=None, scale_mode=FP8BLK_SCAL
     import torch
     _dev(x, torch.bfloat16, "x")
     rows, cols = x.shape
-    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else _dev(q, torch.uint8, "q")
-    s = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device) if s is None else _dense(s, torch.float32, "s")
+    q = _new((rows, cols), torch.uint8, x.device, stream) if q is None else _dev(q, torch.uint8, "q")
+    s = _new((rows, cols // 128), torch.float32, x.device, stream) if s is None else _dense(s, torch.float32, "s")
+    _shape(q, (rows, cols), "q")
+    _shape(s, (rows, cols // 128), "s")
     _check(load_library().fp8_quantize_rowgroup(x.data_ptr(), rows, cols, x.stride(0), q.data_ptr(), q.stride(0),
                                                 s.data_ptr(), scale_mode, _stream(stream)))
     return q, s
@@ -149,9 +177,10 @@ def fp8_quantize_colgroup(x, qT=None, sT=None, stream=None, scale_mode=FP8BLK_SC
     import torch
     _dev(x, torch.bfloat16, "x")
     rows, cols = x.shape
-    qT = torch.empty((cols, rows), dtype=torch.uint8, device=x.device) if qT is None else _dev(qT, torch.uint8, "qT")
-    sT = (torch.empty((cols, rows // 128), dtype=torch.float32, device=x.device) if sT is None
-          else _dense(sT, torch.float32, "sT"))
+    qT = _new((cols, rows), torch.uint8, x.device, stream) if qT is None else _dev(qT, torch.uint8, "qT")
+    sT = _new((cols, rows // 128), torch.float32, x.device, stream) if sT is None else _dense(sT, torch.float32, "sT")
+    _shape(qT, (cols, rows), "qT")
+    _shape(sT, (cols, rows // 128), "sT")
     _check(load_library().fp8_quantize_colgroup(x.data_ptr(), rows, cols, x.stride(0), qT.data_ptr(), qT.stride(0),
                                                 sT.data_ptr(), scale_mode, _stream(stream)))
     return qT, sT
@@ -163,11 +192,14 @@ def fp8_quantize_dual(x, q=None, s=None, qT=None, sT=None, stream=None, scale_mo
     import torch
     _dev(x, torch.bfloat16, "x")
     rows, cols = x.shape
-    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else _dev(q, torch.uint8, "q")
-    s = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device) if s is None else _dense(s, torch.float32, "s")
-    qT = torch.empty((cols, rows), dtype=torch.uint8, device=x.device) if qT is None else _dev(qT, torch.uint8, "qT")
-    sT = (torch.empty((cols, rows // 128), dtype=torch.float32, device=x.device) if sT is None
-          else _dense(sT, torch.float32, "sT"))
+    q = _new((rows, cols), torch.uint8, x.device, stream) if q is None else _dev(q, torch.uint8, "q")
+    s = _new((rows, cols // 128), torch.float32, x.device, stream) if s is None else _dense(s, torch.float32, "s")
+    qT = _new((cols, rows), torch.uint8, x.device, stream) if qT is None else _dev(qT, torch.uint8, "qT")
+    sT = _new((cols, rows // 128), torch.float32, x.device, stream) if sT is None else _dense(sT, torch.float32, "sT")
+    _shape(q, (rows, cols), "q")
+    _shape(s, (rows, cols // 128), "s")
+    _shape(qT, (cols, rows), "qT")
+    _shape(sT, (cols, rows // 128), "sT")
     _check(load_library().fp8_quantize_dual(x.data_ptr(), rows, cols, x.stride(0), q.data_ptr(), q.stride(0),
                                             s.data_ptr(), qT.data_ptr(), qT.stride(0), sT.data_ptr(),
                                             scale_mode, _stream(stream)))
@@ -187,14 +219,14 @@ def fp8_quantize_block_batch(weights, transpose=True, outs=None, stream=None, sc
         rows, cols = w.shape
         if outs is not None:
             q, qT, s = outs[k]
-            _dense(q, torch.uint8, "q")
-            _dense(s, torch.float32, "s")
+            _shape(_dense(q, torch.uint8, f"outs[{k}] q"), (rows, cols), f"outs[{k}] q")
+            _shape(_dense(s, torch.float32, f"outs[{k}] s"), (rows // 128, cols // 128), f"outs[{k}] s")
             if qT is not None:
-                _dense(qT, torch.uint8, "qT")
+                _shape(_dense(qT, torch.uint8, f"outs[{k}] qT"), (cols, rows), f"outs[{k}] qT")
         else:
-            q = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
-            qT = torch.empty((cols, rows), dtype=torch.uint8, device=w.device) if transpose else None
-            s = torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=w.device)
+            q = _new((rows, cols), torch.uint8, w.device, stream)
+            qT = _new((cols, rows), torch.uint8, w.device, stream) if transpose else None
+            s = _new((rows // 128, cols // 128), torch.float32, w.device, stream)
         jobs[k] = _BlockJob(w.data_ptr(), rows, cols, w.stride(0), q.data_ptr(),
                             qT.data_ptr() if qT is not None else None, s.data_ptr())
         res.append((q, qT, s))
@@ -208,14 +240,15 @@ def fp8_quantize_block(w, transpose=True, q=None, qT=None, s=None, stream=None, 
     import torch
     _dev(w, torch.bfloat16, "w")
     rows, cols = w.shape
-    q = torch.empty((rows, cols), dtype=torch.uint8, device=w.device) if q is None else _dense(q, torch.uint8, "q")
+    q = _new((rows, cols), torch.uint8, w.device, stream) if q is None else _dense(q, torch.uint8, "q")
     if transpose:
-        qT = (torch.empty((cols, rows), dtype=torch.uint8, device=w.device) if qT is None
-              else _dense(qT, torch.uint8, "qT"))
+        qT = _new((cols, rows), torch.uint8, w.device, stream) if qT is None else _dense(qT, torch.uint8, "qT")
+        _shape(qT, (cols, rows), "qT")
     else:
         qT = None
-    s = (torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=w.device) if s is None
-         else _dense(s, torch.float32, "s"))
+    s = _new((rows // 128, cols // 128), torch.float32, w.device, stream) if s is None else _dense(s, torch.float32, "s")
+    _shape(q, (rows, cols), "q")
+    _shape(s, (rows // 128, cols // 128), "s")
     _check(load_library().fp8_quantize_block(w.data_ptr(), rows, cols, w.stride(0), q.data_ptr(),
                                              qT.data_ptr() if qT is not None else None, s.data_ptr(),
                                              scale_mode, _stream(stream)))
@@ -224,11 +257,10 @@ def fp8_quantize_block(w, transpose=True, q=None, qT=None, s=None, stream=None, 
 
 # ------------------------------------------------------------------- GEMMs --
 
-def _out(shape, out_dtype, device, out):
-    import torch
+def _out(shape, out_dtype, device, out, stream):
     if out is not None:
-        return _dense(out, out_dtype, "out")
-    return torch.empty(shape, dtype=out_dtype, device=device)
+        return _shape(_dense(out, out_dtype, "out"), shape, "out")
+    return _new(shape, out_dtype, device, stream)
 
 
 def _odt(out_dtype, accumulate=False, out=None):
@@ -244,30 +276,63 @@ def _odt(out_dtype, accumulate=False, out=None):
     raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
 
 
+def _operands(named, M, N, K):
+    """Check each (tensor, name, role) of a contraction: codes are dense uint8
+    and scales dense fp32 of exactly the shape the op's M, N, K imply.
+    Roles: 'x' [M,K] + [M,K/128]; 'dy' [M,N] + [M,N/128]; 'w' [N,K] +
+    [N/128,K/128] block scales; 'wT' [K,N]; 'dyT' [N,M] + [N,M/128];
+    'xT' [K,M] + [K,M/128]."""
+    import torch
+    code_shape = {"x": (M, K), "dy": (M, N), "w": (N, K), "wT": (K, N), "dyT": (N, M), "xT": (K, M)}
+    scale_shape = {"x": (M, K // 128), "dy": (M, N // 128), "w": (N // 128, K // 128),
+                   "wT": (N // 128, K // 128), "dyT": (N, M // 128), "xT": (K, M // 128)}
+    for codes, scales, role, name in named:
+        _shape(_dense(codes, torch.uint8, name), code_shape[role], name)
+        _shape(_dense(scales, torch.float32, name + " scales"), scale_shape[role], name + " scales")
+
+
+def _workspace(op, M, N, K, workspace, device, stream):
+    import torch
+    need = fp8_block_gemm_workspace_size(op, M, N, K)
+    if need and workspace is None:
+        # belongs to `stream`: freed when this call returns, its memory is
+        # reused only by work queued behind the kernels that use it
+        workspace = _new(need, torch.uint8, device, stream)
+    if workspace is None:
+        return None, 0
+    _dev(workspace, workspace.dtype, "workspace", ndim=workspace.dim())
+    if not workspace.is_contiguous():
+        raise ValueError("workspace: must be contiguous")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def fp8_block_gemm_workspace_size(op: int, M: int, N: int, K: int) -> int:
     return int(load_library().fp8_block_gemm_workspace_size(op, M, N, K))
 
 
+# operand roles of (a, b) per op of the generic entry point, and the output shape
+_GEMM_ROLES = {FP8BLK_OP_FPROP: ("x", "w"), FP8BLK_OP_DGRAD: ("dy", "wT"), FP8BLK_OP_WGRAD: ("dyT", "xT"),
+               FP8BLK_OP_DGRAD_W: ("dy", "w")}
+
+
 def fp8_block_gemm(op, a, sa, b, sb, M, N, K, out_dtype=None, algo=FP8BLK_ALGO_DEFAULT, out=None,
-                   workspace=None, stream=None, accumulate=False):
+                   workspace=None, stream=None, accumulate=False, scale_mode=FP8BLK_SCALE_POW2):
     """Any of the three contractions with an explicit algorithm (see
     fp8_block_gemm in include/fp8blk.h for the operand roles).  accumulate:
-    out += result in fp32 (out_dtype float32, `out` given)."""
+    out += result in fp32 (out_dtype float32, `out` given).  scale_mode: the
+    rule that made sa and sb (FP8BLK_SCALE_FP32 scales run PROMOTE)."""
     import torch
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
-    for t, n in ((a, "a"), (b, "b")):
-        _dense(t, torch.uint8, n)
-    for t, n in ((sa, "sa"), (sb, "sb")):
-        _dense(t, torch.float32, n)
+    if op not in _GEMM_ROLES:
+        raise ValueError(f"op {op}: not a contraction of fp8_block_gemm")
+    ra, rb = _GEMM_ROLES[op]
+    _operands(((a, sa, ra, "a"), (b, sb, rb, "b")), M, N, K)
     shape = {FP8BLK_OP_FPROP: (M, N), FP8BLK_OP_DGRAD: (M, K), FP8BLK_OP_WGRAD: (N, K), FP8BLK_OP_DGRAD_W: (M, K)}[op]
-    y = _out(shape, out_dtype, a.device, out)
-    need = fp8_block_gemm_workspace_size(op, M, N, K)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
-    wptr = workspace.data_ptr() if workspace is not None else None
-    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    y = _out(shape, out_dtype, a.device, out, stream)
+    wptr, wbytes = _workspace(op, M, N, K, workspace, a.device, stream)
     _check(load_library().fp8_block_gemm(op, M, N, K, a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(),
-                                         y.data_ptr(), _odt(out_dtype, accumulate, out), algo, wptr, wbytes, _stream(stream)))
+                                         y.data_ptr(), _odt(out_dtype, accumulate, out), algo, scale_mode, wptr,
+                                         wbytes, _stream(stream)))
     return y
 
 
@@ -277,11 +342,8 @@ def fp8_block_gemm_fprop(qx, sx, qw, sw, out_dtype=None, out=None, stream=None, 
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     M, K = qx.shape
     N = qw.shape[0]
-    for t, n in ((qx, "qx"), (qw, "qw")):
-        _dense(t, torch.uint8, n)
-    for t, n in ((sx, "sx"), (sw, "sw")):
-        _dense(t, torch.float32, n)
-    y = _out((M, N), out_dtype, qx.device, out)
+    _operands(((qx, sx, "x", "qx"), (qw, sw, "w", "qw")), M, N, K)
+    y = _out((M, N), out_dtype, qx.device, out, stream)
     _check(load_library().fp8_block_gemm_fprop(M, N, K, qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(),
                                                y.data_ptr(), _odt(out_dtype, accumulate, out), _stream(stream)))
     return y
@@ -293,13 +355,11 @@ def fp8_block_gemm_dgrad(qdy, sdy, qwT, sw, out_dtype=None, out=None, stream=Non
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     M, N = qdy.shape
     K = qwT.shape[0]
-    for t, n in ((qdy, "qdy"), (qwT, "qwT")):
-        _dense(t, torch.uint8, n)
-    for t, n in ((sdy, "sdy"), (sw, "sw")):
-        _dense(t, torch.float32, n)
-    y = _out((M, K), out_dtype, qdy.device, out)
+    _operands(((qdy, sdy, "dy", "qdy"), (qwT, sw, "wT", "qwT")), M, N, K)
+    y = _out((M, K), out_dtype, qdy.device, out, stream)
     _check(load_library().fp8_block_gemm_dgrad(M, N, K, qdy.data_ptr(), sdy.data_ptr(), qwT.data_ptr(),
-                                               sw.data_ptr(), y.data_ptr(), _odt(out_dtype, accumulate, out), _stream(stream)))
+                                               sw.data_ptr(), y.data_ptr(), _odt(out_dtype, accumulate, out),
+                                               _stream(stream)))
     return y
 
 
@@ -310,11 +370,8 @@ def fp8_block_gemm_dgrad_w(qdy, sdy, qw, sw, out_dtype=None, out=None, stream=No
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     M, N = qdy.shape
     K = qw.shape[1]
-    for t, n in ((qdy, "qdy"), (qw, "qw")):
-        _dense(t, torch.uint8, n)
-    for t, n in ((sdy, "sdy"), (sw, "sw")):
-        _dense(t, torch.float32, n)
-    y = _out((M, K), out_dtype, qdy.device, out)
+    _operands(((qdy, sdy, "dy", "qdy"), (qw, sw, "w", "qw")), M, N, K)
+    y = _out((M, K), out_dtype, qdy.device, out, stream)
     _check(load_library().fp8_block_gemm_dgrad_w(M, N, K, qdy.data_ptr(), sdy.data_ptr(), qw.data_ptr(),
                                                  sw.data_ptr(), y.data_ptr(), _odt(out_dtype, accumulate, out),
                                                  _stream(stream)))
@@ -328,60 +385,48 @@ def fp8_block_gemm_wgrad(qdyT, sdyT, qxT, sxT, out_dtype=None, out=None, workspa
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     N, M = qdyT.shape
     K = qxT.shape[0]
-    for t, n in ((qdyT, "qdyT"), (qxT, "qxT")):
-        _dense(t, torch.uint8, n)
-    for t, n in ((sdyT, "sdyT"), (sxT, "sxT")):
-        _dense(t, torch.float32, n)
-    y = _out((N, K), out_dtype, qdyT.device, out)
-    need = fp8_block_gemm_workspace_size(FP8BLK_OP_WGRAD, M, N, K)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=qdyT.device)
-    wptr = workspace.data_ptr() if workspace is not None else None
-    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _operands(((qdyT, sdyT, "dyT", "qdyT"), (qxT, sxT, "xT", "qxT")), M, N, K)
+    y = _out((N, K), out_dtype, qdyT.device, out, stream)
+    wptr, wbytes = _workspace(FP8BLK_OP_WGRAD, M, N, K, workspace, qdyT.device, stream)
     _check(load_library().fp8_block_gemm_wgrad(M, N, K, qdyT.data_ptr(), sdyT.data_ptr(), qxT.data_ptr(),
-                                               sxT.data_ptr(), y.data_ptr(), _odt(out_dtype, accumulate, out), wptr, wbytes,
-                                               _stream(stream)))
+                                               sxT.data_ptr(), y.data_ptr(), _odt(out_dtype, accumulate, out), wptr,
+                                               wbytes, _stream(stream)))
     return y
 
 
 def fp8_block_gemm_backward(qdy, sdy, qwT, sw, qdyT, sdyT, qxT, sxT, dx_dtype=None, dw_dtype=None, dx=None,
-                            dw=None, workspace=None, stream=None, accumulate_dw=False):
+                            dw=None, workspace=None, stream=None, accumulate_dw=False, scale_mode=FP8BLK_SCALE_POW2):
     """Dgrad and Wgrad of one linear in one call.  Operands as for
     fp8_block_gemm_dgrad and fp8_block_gemm_wgrad; returns (dx [M,K], dw [N,K]).
-    accumulate_dw: dw += dY^T X in fp32 (dw_dtype float32, `dw` given)."""
-    return _backward("fp8_block_gemm_backward", qdy, sdy, qwT, qwT.shape[0], sw, qdyT, sdyT, qxT, sxT, dx_dtype,
-                     dw_dtype, dx, dw, workspace, stream, accumulate_dw)
+    accumulate_dw: dw += dY^T X in fp32 (dw_dtype float32, `dw` given).
+    scale_mode: the rule that made the scales (FP8BLK_SCALE_FP32 runs PROMOTE)."""
+    return _backward("fp8_block_gemm_backward", qdy, sdy, qwT, "wT", sw, qdyT, sdyT, qxT, sxT, dx_dtype,
+                     dw_dtype, dx, dw, workspace, stream, accumulate_dw, scale_mode)
 
 
 def fp8_block_gemm_backward_w(qdy, sdy, qw, sw, qdyT, sdyT, qxT, sxT, dx_dtype=None, dw_dtype=None, dx=None,
-                              dw=None, workspace=None, stream=None, accumulate_dw=False):
+                              dw=None, workspace=None, stream=None, accumulate_dw=False, scale_mode=FP8BLK_SCALE_POW2):
     """fp8_block_gemm_backward with Dgrad reading the weight codes qw [N,K] as
     quantized (no transposed copy)."""
-    return _backward("fp8_block_gemm_backward_w", qdy, sdy, qw, qw.shape[1], sw, qdyT, sdyT, qxT, sxT, dx_dtype,
-                     dw_dtype, dx, dw, workspace, stream, accumulate_dw)
+    return _backward("fp8_block_gemm_backward_w", qdy, sdy, qw, "w", sw, qdyT, sdyT, qxT, sxT, dx_dtype,
+                     dw_dtype, dx, dw, workspace, stream, accumulate_dw, scale_mode)
 
 
-def _backward(fn, qdy, sdy, qwT, K, sw, qdyT, sdyT, qxT, sxT, dx_dtype, dw_dtype, dx, dw, workspace, stream,
-              accumulate_dw):
+def _backward(fn, qdy, sdy, wcodes, wrole, sw, qdyT, sdyT, qxT, sxT, dx_dtype, dw_dtype, dx, dw, workspace, stream,
+              accumulate_dw, scale_mode):
     import torch
     dx_dtype = torch.bfloat16 if dx_dtype is None else dx_dtype
     dw_dtype = torch.bfloat16 if dw_dtype is None else dw_dtype
     M, N = qdy.shape
-    for t, n in ((qdy, "qdy"), (qwT, "weight codes"), (qdyT, "qdyT"), (qxT, "qxT")):
-        _dense(t, torch.uint8, n)
-    for t, n in ((sdy, "sdy"), (sw, "sw"), (sdyT, "sdyT"), (sxT, "sxT")):
-        _dense(t, torch.float32, n)
-    x = _out((M, K), dx_dtype, qdy.device, dx)
-    w = _out((N, K), dw_dtype, qdy.device, dw)
-    need = fp8_block_gemm_workspace_size(FP8BLK_OP_BACKWARD, M, N, K)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=qdy.device)
-    wptr = workspace.data_ptr() if workspace is not None else None
-    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(getattr(load_library(), fn)(M, N, K, qdy.data_ptr(), sdy.data_ptr(), qwT.data_ptr(),
+    K = wcodes.shape[1] if wrole == "w" else wcodes.shape[0]
+    _operands(((qdy, sdy, "dy", "qdy"), (wcodes, sw, wrole, "weight codes"), (qdyT, sdyT, "dyT", "qdyT"),
+               (qxT, sxT, "xT", "qxT")), M, N, K)
+    x = _out((M, K), dx_dtype, qdy.device, dx, stream)
+    w = _out((N, K), dw_dtype, qdy.device, dw, stream)
+    wptr, wbytes = _workspace(FP8BLK_OP_BACKWARD, M, N, K, workspace, qdy.device, stream)
+    _check(getattr(load_library(), fn)(M, N, K, qdy.data_ptr(), sdy.data_ptr(), wcodes.data_ptr(),
                                        sw.data_ptr(), qdyT.data_ptr(), sdyT.data_ptr(), qxT.data_ptr(),
                                        sxT.data_ptr(), x.data_ptr(), _odt(dx_dtype),
-                                       w.data_ptr(), _odt(dw_dtype, accumulate_dw, dw), wptr, wbytes,
+                                       w.data_ptr(), _odt(dw_dtype, accumulate_dw, dw), scale_mode, wptr, wbytes,
                                        _stream(stream)))
     return x, w
-

@@ -185,13 +185,30 @@ static fp8blk::GemmArgs make_args(int op, int64_t M, int64_t N, int64_t K, const
   return g;
 }
 
+// The kernel algorithm for an (algo, scale_mode) pair, or -1 for a pair that
+// cannot run: amax / 448 scales are not powers of two, and the block-scaled
+// MFMA would keep only their exponent fields.
+static int resolve_algo(int algo, int scale_mode, fp8blk::GemmAlgo* out) {
+  if (algo != FP8BLK_ALGO_DEFAULT && algo != FP8BLK_ALGO_PROMOTE && algo != FP8BLK_ALGO_SCALED_MFMA) return -1;
+  if (!valid_scale_mode(scale_mode)) return -1;
+  if (scale_mode == FP8BLK_SCALE_FP32) {
+    if (algo == FP8BLK_ALGO_SCALED_MFMA) return -1;
+    *out = fp8blk::GemmAlgo::Promote;
+    return 0;
+  }
+  *out = algo == FP8BLK_ALGO_PROMOTE      ? fp8blk::GemmAlgo::Promote
+         : algo == FP8BLK_ALGO_SCALED_MFMA ? fp8blk::GemmAlgo::ScaledMfma
+                                           : kDefaultAlgo;
+  return 0;
+}
+
 int fp8_block_gemm(int op, int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa, const uint8_t* b,
-                   const float* sb, void* out, int out_dtype, int algo, void* workspace, size_t ws_bytes,
-                   hipStream_t stream) {
+                   const float* sb, void* out, int out_dtype, int algo, int scale_mode, void* workspace,
+                   size_t ws_bytes, hipStream_t stream) {
   if (op != FP8BLK_OP_FPROP && op != FP8BLK_OP_DGRAD && op != FP8BLK_OP_WGRAD && op != FP8BLK_OP_DGRAD_W)
     return FP8BLK_ERR_ARG;
-  if (algo != FP8BLK_ALGO_DEFAULT && algo != FP8BLK_ALGO_PROMOTE && algo != FP8BLK_ALGO_SCALED_MFMA)
-    return FP8BLK_ERR_ARG;
+  fp8blk::GemmAlgo al;
+  if (resolve_algo(algo, scale_mode, &al) != 0) return FP8BLK_ERR_ARG;
   if (int rc = check_gemm_common(M, N, K, a, sa, b, sb, out, out_dtype)) return rc;
   fp8blk::GemmArgs g = make_args(op, M, N, K, a, sa, b, sb, out, out_dtype);
   const size_t need = fp8blk::gemm_workspace_bytes(g.I, g.J, g.R, g.bmode);
@@ -199,9 +216,6 @@ int fp8_block_gemm(int op, int64_t M, int64_t N, int64_t K, const uint8_t* a, co
   if (need > 0 && !aligned16(workspace)) return FP8BLK_ERR_ALIGN;
   if (int rc = check_device()) return rc;
   g.ws = static_cast<float*>(workspace);
-  const fp8blk::GemmAlgo al = algo == FP8BLK_ALGO_PROMOTE      ? fp8blk::GemmAlgo::Promote
-                              : algo == FP8BLK_ALGO_SCALED_MFMA ? fp8blk::GemmAlgo::ScaledMfma
-                                                                : kDefaultAlgo;
   return finish(fp8blk::launch_gemm(g, al, stream));
 }
 
@@ -217,8 +231,9 @@ static size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 // or FP8BLK_OP_DGRAD_W (w = qw [N][K]).
 static int backward(int dgrad_op, int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy,
                     const uint8_t* w, const float* sw, const uint8_t* qdyT, const float* sdyT, const uint8_t* qxT,
-                    const float* sxT, void* dx, int dx_dtype, void* dw, int dw_dtype, void* workspace,
-                    size_t ws_bytes, hipStream_t stream) {
+                    const float* sxT, void* dx, int dx_dtype, void* dw, int dw_dtype, int scale_mode,
+                    void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_scale_mode(scale_mode)) return FP8BLK_ERR_ARG;
   if (int rc = check_gemm_common(M, N, K, qdy, sdy, w, sw, dx, dx_dtype)) return rc;
   if (int rc = check_gemm_common(M, N, K, qdyT, sdyT, qxT, sxT, dw, dw_dtype)) return rc;
   if (dx == dw) return FP8BLK_ERR_ARG;
@@ -229,51 +244,55 @@ static int backward(int dgrad_op, int64_t M, int64_t N, int64_t K, const uint8_t
   fp8blk::GemmArgs gd = make_args(dgrad_op, M, N, K, qdy, sdy, w, sw, dx, dx_dtype);
   fp8blk::GemmArgs gw = make_args(FP8BLK_OP_WGRAD, M, N, K, qdyT, sdyT, qxT, sxT, dw, dw_dtype);
   gw.ws = static_cast<float*>(workspace);
-  if (fp8blk::gemm_mx_bwd_eligible(gd, gw)) return finish(fp8blk::launch_gemm_mx_bwd(gd, gw, stream));
-  // shapes the fused launch does not take: the two contractions in turn
-  if (hipError_t e = fp8blk::launch_gemm(gd, kDefaultAlgo, stream)) return finish(e);
-  return finish(fp8blk::launch_gemm(gw, kDefaultAlgo, stream));
+  // amax / 448 scales: the promote algorithm, which reads the whole scales
+  const fp8blk::GemmAlgo al = scale_mode == FP8BLK_SCALE_FP32 ? fp8blk::GemmAlgo::Promote : kDefaultAlgo;
+  if (al == fp8blk::GemmAlgo::ScaledMfma && fp8blk::gemm_mx_bwd_eligible(gd, gw))
+    return finish(fp8blk::launch_gemm_mx_bwd(gd, gw, stream));
+  // shapes the fused launch does not take, and amax / 448 scales: the two
+  // contractions in turn
+  if (hipError_t e = fp8blk::launch_gemm(gd, al, stream)) return finish(e);
+  return finish(fp8blk::launch_gemm(gw, al, stream));
 }
 
 int fp8_block_gemm_backward(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy,
                             const uint8_t* qwT, const float* sw, const uint8_t* qdyT, const float* sdyT,
                             const uint8_t* qxT, const float* sxT, void* dx, int dx_dtype, void* dw, int dw_dtype,
-                            void* workspace, size_t ws_bytes, hipStream_t stream) {
+                            int scale_mode, void* workspace, size_t ws_bytes, hipStream_t stream) {
   return backward(FP8BLK_OP_DGRAD, M, N, K, qdy, sdy, qwT, sw, qdyT, sdyT, qxT, sxT, dx, dx_dtype, dw, dw_dtype,
-                  workspace, ws_bytes, stream);
+                  scale_mode, workspace, ws_bytes, stream);
 }
 
 int fp8_block_gemm_backward_w(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy,
                               const uint8_t* qw, const float* sw, const uint8_t* qdyT, const float* sdyT,
                               const uint8_t* qxT, const float* sxT, void* dx, int dx_dtype, void* dw, int dw_dtype,
-                              void* workspace, size_t ws_bytes, hipStream_t stream) {
+                              int scale_mode, void* workspace, size_t ws_bytes, hipStream_t stream) {
   return backward(FP8BLK_OP_DGRAD_W, M, N, K, qdy, sdy, qw, sw, qdyT, sdyT, qxT, sxT, dx, dx_dtype, dw, dw_dtype,
-                  workspace, ws_bytes, stream);
+                  scale_mode, workspace, ws_bytes, stream);
 }
 
 int fp8_block_gemm_fprop(int64_t M, int64_t N, int64_t K, const uint8_t* qx, const float* sx, const uint8_t* qw,
                          const float* sw, void* y, int out_dtype, hipStream_t stream) {
-  return fp8_block_gemm(FP8BLK_OP_FPROP, M, N, K, qx, sx, qw, sw, y, out_dtype, FP8BLK_ALGO_DEFAULT, nullptr, 0,
-                        stream);
+  return fp8_block_gemm(FP8BLK_OP_FPROP, M, N, K, qx, sx, qw, sw, y, out_dtype, FP8BLK_ALGO_DEFAULT,
+                        FP8BLK_SCALE_POW2, nullptr, 0, stream);
 }
 
 int fp8_block_gemm_dgrad(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy, const uint8_t* qwT,
                          const float* sw, void* dx, int out_dtype, hipStream_t stream) {
-  return fp8_block_gemm(FP8BLK_OP_DGRAD, M, N, K, qdy, sdy, qwT, sw, dx, out_dtype, FP8BLK_ALGO_DEFAULT, nullptr, 0,
-                        stream);
+  return fp8_block_gemm(FP8BLK_OP_DGRAD, M, N, K, qdy, sdy, qwT, sw, dx, out_dtype, FP8BLK_ALGO_DEFAULT,
+                        FP8BLK_SCALE_POW2, nullptr, 0, stream);
 }
 
 int fp8_block_gemm_dgrad_w(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy, const uint8_t* qw,
                            const float* sw, void* dx, int out_dtype, hipStream_t stream) {
-  return fp8_block_gemm(FP8BLK_OP_DGRAD_W, M, N, K, qdy, sdy, qw, sw, dx, out_dtype, FP8BLK_ALGO_DEFAULT, nullptr, 0,
-                        stream);
+  return fp8_block_gemm(FP8BLK_OP_DGRAD_W, M, N, K, qdy, sdy, qw, sw, dx, out_dtype, FP8BLK_ALGO_DEFAULT,
+                        FP8BLK_SCALE_POW2, nullptr, 0, stream);
 }
 
 int fp8_block_gemm_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* qdyT, const float* sdyT,
                          const uint8_t* qxT, const float* sxT, void* dw, int out_dtype, void* workspace,
                          size_t ws_bytes, hipStream_t stream) {
-  return fp8_block_gemm(FP8BLK_OP_WGRAD, M, N, K, qdyT, sdyT, qxT, sxT, dw, out_dtype, FP8BLK_ALGO_DEFAULT, workspace,
-                        ws_bytes, stream);
+  return fp8_block_gemm(FP8BLK_OP_WGRAD, M, N, K, qdyT, sdyT, qxT, sxT, dw, out_dtype, FP8BLK_ALGO_DEFAULT,
+                        FP8BLK_SCALE_POW2, workspace, ws_bytes, stream);
 }
 
 size_t fp8_block_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K) {

@@ -1,0 +1,80 @@
+// Host-side launch plans of libfp8blk's persistent GEMM kernels: how the
+// reduction work of a contraction's output tiles is cut into ranges, one per
+// workgroup, and where the partial tiles of shared output tiles go in the
+// workspace.  Plain C++ (plan.cpp), shared by the kernels' launchers and by
+// the C ABI layer's workspace queries.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8blk {
+
+// The persistent grid: one workgroup per CU of an MI355X (fewer for tiny
+// shapes).  At most this many ranges, so slot tables have this many entries.
+constexpr int64_t kSkGrid = 256;
+// Output tile edge of the block-scaled-MFMA kernels (gemm_mx.hip).
+constexpr int64_t kMxTile = 256;
+// 128-blocks of a reduction whose weight-block scales those kernels hold in
+// LDS at once.
+constexpr int64_t kMxMaxKb = 128;
+
+// Range w of a grid of G over W units: [w W / G, (w + 1) W / G).
+inline int64_t h_start(int64_t w, int64_t W, int64_t G) { return w * W / G; }
+// The range that holds unit u: the largest w with start(w) <= u.
+inline int64_t h_owner(int64_t u, int64_t W, int64_t G) { return ((u + 1) * G - 1) / W; }
+
+// A workgroup's range is a run of segments, one per output tile it touches;
+// only its first and last segment can cover part of a tile.  Such a partial
+// tile is stored, in fp32, to a tile-sized slot of the workspace, and a
+// fix-up kernel adds the pieces of every shared tile in reduction order.
+// Slots are numbered densely over the partial segments, in range order:
+// slot[r] = (P(r) << 1) | f(r), with P(r) the number of partial segments of
+// ranges 0 .. r-1 and f(r) = 1 if range r's first segment is partial.  Range
+// r's first segment (if partial) uses slot P(r), its last one (if partial
+// and not also the first) P(r) + f(r).
+
+// Wgrad alone on the persistent grid (gemm_mx_streamk_kernel): whole waves of
+// tiles run data-parallel, the rest stream-K over 512-deep units.
+struct SkGeom {
+  int64_t tiles_m, tiles_n;
+  int64_t dp_tiles;  // tiles [0, dp_tiles) are data-parallel
+  int64_t units;     // W: stream-K units (of the tiles from dp_tiles on)
+  int64_t sk_grid;   // Gs = min(G, W): workgroups with stream-K work
+  int64_t sk_tiles;  // T' when the ranges are permuted (see gemm_mx.hip), else 0
+  uint16_t slot[kSkGrid];
+};
+
+struct SkPlan {
+  SkGeom geom;
+  int64_t grid;
+  int64_t slots;  // partial segments (workspace slots); 0: no tile is shared
+  size_t bytes;   // workspace bytes
+};
+
+SkPlan sk_plan(int64_t I, int64_t J, int64_t R);
+
+// Dgrad (problem 0: I = M, J = K, R = N, weight-block scales) and Wgrad
+// (problem 1: I = N, J = K, R = M, row scales) of one linear in one
+// persistent launch (gemm_mx_bwd_kernel).
+struct BwdGeom {
+  int64_t tm0, tn0, u0, t0;  // problem 0: tile grid, units per tile, tiles
+  int64_t tm1, tn1, u1;      // problem 1
+  int64_t w0;                // units of problem 0
+  int64_t units;             // W, all units
+  // k0, k1: when a problem's tiles fall whole into ranges, k of them per
+  // range (else 0); the ranges' tiles are then dealt out round-robin.
+  int64_t k0, k1;
+  uint16_t slot[kSkGrid];
+};
+
+struct BwdPlan {
+  BwdGeom geom;
+  int64_t grid;
+  int64_t slots;
+  size_t bytes;
+};
+
+BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K);
+
+}  // namespace fp8blk

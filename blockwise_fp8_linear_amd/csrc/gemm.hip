@@ -458,8 +458,6 @@ using ScaledRow = Cfg<256, 128, 2, 2, false, true>;
 using PromoteBlockBT = Cfg<256, 128, 2, 2, true, false, true>;
 using ScaledBlockBT = Cfg<256, 128, 2, 2, false, false, true>;
 
-constexpr int kCUs = 256;
-
 hipError_t ensure_lds_limit(const void* kernel, int bytes, std::atomic<uint64_t>* done) {
   int dev = 0;
   if (hipError_t e = hipGetDevice(&dev)) return e;
@@ -468,25 +466,6 @@ hipError_t ensure_lds_limit(const void* kernel, int bytes, std::atomic<uint64_t>
   if (hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)) return e;
   if (bit) done->fetch_or(bit, std::memory_order_release);
   return hipSuccess;
-}
-
-int gemm_splits(int64_t I, int64_t J, int64_t R, BScale bmode) {
-  if (bmode == BScale::Block) return 1;
-  const int64_t tiles = ((I + 255) / 256) * ((J + 255) / 256);
-  const int64_t nkb = R / 128;
-  int s = 1;
-  // split the reduction until the grid covers the CUs, keeping >= 8 blocks per slice
-  while (tiles * s < kCUs && nkb / (2 * s) >= 8) s *= 2;
-  return s;
-}
-
-size_t gemm_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode) {
-  // enough for either path: split-K partials of this kernel, or the
-  // stream-K counters and partial tiles of the block-scaled-MFMA kernel
-  const int s = gemm_splits(I, J, R, bmode);
-  const size_t split_bytes = s > 1 ? (size_t)s * (size_t)I * (size_t)J * sizeof(float) : 0;
-  const size_t mx_bytes = gemm_mx_workspace_bytes(I, J, R, bmode);
-  return split_bytes > mx_bytes ? split_bytes : mx_bytes;
 }
 
 template <class C>

@@ -33,6 +33,7 @@
 // weight-block scales) and the per-row scale arrays are 16-byte aligned.
 #include "fp8blk_device.h"
 #include "fp8blk_launch.h"
+#include "fp8blk_plan.h"
 
 namespace fp8blk {
 
@@ -41,7 +42,7 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 256, BK = 64, THREADS = 256;
+constexpr int BM = (int)kMxTile, BN = (int)kMxTile, BK = 64, THREADS = 256;
 constexpr int WM = 128, WN = 128;          // wave tile
 constexpr int TM = WM / 32, TN = WN / 32;  // 32x32 MFMA tiles per wave
 // The LDS ring holds two "pair slots"; a pair slot holds two consecutive
@@ -51,7 +52,7 @@ constexpr int PK = 2 * BK;                         // bytes of a row in a pair s
 constexpr int A_SLOT = BM * PK, B_SLOT = BN * PK, SLOT = A_SLOT + B_SLOT;  // 64 KiB
 constexpr int SLOTS = 2;
 constexpr int SC_BYTES = 8192;            // one group of raw scales: A rows, then B rows
-constexpr int MAX_KB = 128;               // 128-blocks per segment with weight-block scales (held in LDS)
+constexpr int MAX_KB = (int)kMxMaxKb;     // 128-blocks per segment with weight-block scales (held in LDS)
 constexpr int BS_BYTES = 4 * MAX_KB * 4;  // the 4 waves' weight-block scales of a segment, fp32
 constexpr int LDS_BYTES = SLOTS * SLOT + 2 * SC_BYTES + BS_BYTES;  // 146 KiB
 constexpr int LOADS_A = A_SLOT / 1024 / (THREADS / 64);  // 1 KiB per wave instruction
@@ -532,21 +533,19 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(GemmArgs g, int64_t ti
 // the same depth, sharing operand panels in L2, as a split-K launch would.
 // A stream-K range is a run of segments: whole tiles are stored directly; a
 // piece of a tile shared by several workgroups is stored, in fp32, to a
-// tile-sized slot of the workspace -- slot 2r for the first segment of
-// range r, 2r + 1 for its last one (the only segments that can be partial)
-// -- and a second kernel adds the pieces of every shared tile in reduction
-// order (deterministic) and stores it.  No workgroup ever waits for another.
-struct SkGeom {
-  int64_t tiles_m, tiles_n;
-  int64_t dp_tiles;  // tiles [0, dp_tiles) are data-parallel
-  int64_t units;     // W: stream-K units (of the tiles from dp_tiles on)
-  int64_t sk_grid;   // Gs = min(G, W): workgroups with stream-K work
-  int64_t sk_tiles;  // T' when the ranges are permuted as above, else 0
-};
-
+// tile-sized slot of the workspace (numbered densely over the partial
+// segments, see fp8blk_plan.h) and a second kernel adds the pieces of every
+// shared tile in reduction order (deterministic) and stores it.  No
+// workgroup ever waits for another.
 __device__ __forceinline__ int64_t sk_start(int64_t w, int64_t W, int64_t G) { return w * W / G; }
 // the workgroup whose range holds unit u: the largest w with start(w) <= u
 __device__ __forceinline__ int64_t sk_owner(int64_t u, int64_t W, int64_t G) { return ((u + 1) * G - 1) / W; }
+
+// The slot of range r's first (first = true) or last partial segment.
+__device__ __forceinline__ int64_t slot_of(const uint16_t* table, int64_t r, bool first) {
+  const uint32_t e = table[r];
+  return (int64_t)(e >> 1) + (first ? 0 : (int64_t)(e & 1));
+}
 
 template <bool BROW>
 __global__ __launch_bounds__(THREADS) void gemm_mx_streamk_kernel(GemmArgs g, SkGeom sg, float* partials) {
@@ -578,7 +577,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_streamk_kernel(GemmArgs g, Sk
     if (lo == 0 && hi == U) {
       store_tile<1>(out, lds, i0, j0, acc);
     } else {
-      float* const slot = partials + (2 * r + (u == ubeg ? 0 : 1)) * (int64_t)(BM * BN);
+      float* const slot = partials + slot_of(sg.slot, r, u == ubeg) * (int64_t)(BM * BN);
       store_tile<1>(Dst{slot, BN, BM, BN, true, false}, lds, 0, 0, acc);
     }
     u = ts * U + hi;
@@ -587,9 +586,9 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_streamk_kernel(GemmArgs g, Sk
 
 // The shared stream-K tiles: block (ts, r) sums rows 16r..16r+15 of
 // stream-K tile ts over its pieces in reduction order and stores them.
-// Piece 0 sits in slot 2 f + 1 if range f (the tile's first) started in an
-// earlier tile (the piece is its last segment), else in slot 2 f; piece
-// k >= 1 is the first segment of range f + k, slot 2 (f + k).
+// Piece 0 is the last segment of range f (the tile's first) if f started in
+// an earlier tile, else f's first segment; piece k >= 1 is the first
+// segment of range f + k.
 constexpr int FIX_ROWS = 16;
 
 __global__ __launch_bounds__(256) void sk_fixup_kernel(GemmArgs g, SkGeom sg, const float* __restrict__ partials) {
@@ -599,13 +598,13 @@ __global__ __launch_bounds__(256) void sk_fixup_kernel(GemmArgs g, SkGeom sg, co
   const int64_t f = sk_owner(ts * U, W, G);
   const int pieces = (int)(sk_owner(ts * U + U - 1, W, G) - f + 1);
   if (pieces == 1) return;  // stored by the GEMM itself
-  const int64_t first_slot = 2 * f + (sk_start(f, W, G) < ts * U ? 1 : 0);
+  const int64_t first_slot = slot_of(sg.slot, f, !(sk_start(f, W, G) < ts * U));
   int64_t i0, j0;
   tile_origin(sg.dp_tiles + ts, sg.tiles_m, sg.tiles_n, i0, j0);
   constexpr int PER = FIX_ROWS * BN / 4 / 256;  // float4 per thread
   v4f sum[PER];
   for (int pc = 0; pc < pieces; ++pc) {
-    const int64_t slot = pc == 0 ? first_slot : 2 * (f + pc);
+    const int64_t slot = pc == 0 ? first_slot : slot_of(sg.slot, f + pc, true);
     const v4f* src = reinterpret_cast<const v4f*>(partials + slot * (int64_t)(BM * BN) + r0 * BN);
     v4f v[PER];
 #pragma unroll
@@ -645,19 +644,10 @@ __global__ __launch_bounds__(256) void sk_fixup_kernel(GemmArgs g, SkGeom sg, co
 // units of four 128-blocks, problem 0's tiles first, and range r of G takes
 // units [r W / G, (r + 1) W / G) of all W of them, so every workgroup does
 // the same work and the CUs stay busy across both GEMMs.  Segments, slots
-// and the fix-up of shared tiles work as in the Wgrad kernel above.
-struct BwdGeom {
-  int64_t tm0, tn0, u0, t0;  // problem 0: tile grid, units per tile, tiles
-  int64_t tm1, tn1, u1;      // problem 1
-  int64_t w0;                // units of problem 0
-  int64_t units;             // W, all units
-  // k0, k1: when a problem's tiles fall whole into ranges, k of them per
-  // range (else 0); the ranges' tiles are then dealt out round-robin -- the
-  // j-th tile of the problem's i-th range is tile j R + i (R ranges) -- so
-  // that the ranges running side by side work on neighbouring tiles and
-  // share operand panels in L2.  Whole tiles never reach the fix-up.
-  int64_t k0, k1;
-};
+// and the fix-up of shared tiles work as in the Wgrad kernel above; when a
+// problem's tiles fall whole into ranges (BwdGeom k0, k1), the j-th tile of
+// its i-th range is tile j R + i (R ranges), so that the ranges running side
+// by side work on neighbouring tiles and share operand panels in L2.
 
 // BT: Dgrad reads the weight codes as quantized (gd.b is W[N][K]).
 template <bool BT>
@@ -690,7 +680,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_bwd_kernel(GemmArgs gd, GemmA
                   p1 ? gw.out_f32 : gd.out_f32, p1 ? gw.accumulate : gd.accumulate};
       store_tile<1>(d, lds, i0, j0, acc);
     } else {
-      float* const slot = partials + (2 * r + (u == ubeg ? 0 : 1)) * (int64_t)(BM * BN);
+      float* const slot = partials + slot_of(bg.slot, r, u == ubeg) * (int64_t)(BM * BN);
       store_tile<1>(Dst{slot, BN, BM, BN, true, false}, lds, 0, 0, acc);
     }
     u = base + ts * U + hi;
@@ -710,7 +700,7 @@ __global__ __launch_bounds__(256) void bwd_fixup_kernel(GemmArgs gd, GemmArgs gw
   const int64_t f = sk_owner(first, W, G);
   const int pieces = (int)(sk_owner(first + U - 1, W, G) - f + 1);
   if (pieces == 1) return;  // stored by the GEMM itself
-  const int64_t first_slot = 2 * f + (sk_start(f, W, G) < first ? 1 : 0);
+  const int64_t first_slot = slot_of(bg.slot, f, !(sk_start(f, W, G) < first));
   int64_t i0, j0;
   tile_origin(ts, p1 ? bg.tm1 : bg.tm0, p1 ? bg.tn1 : bg.tn0, i0, j0);
   const int64_t I = p1 ? gw.I : gd.I, J = p1 ? gw.J : gd.J;
@@ -719,7 +709,7 @@ __global__ __launch_bounds__(256) void bwd_fixup_kernel(GemmArgs gd, GemmArgs gw
   constexpr int PER = FIX_ROWS * BN / 4 / 256;  // float4 per thread
   v4f sum[PER];
   for (int pc = 0; pc < pieces; ++pc) {
-    const int64_t slot = pc == 0 ? first_slot : 2 * (f + pc);
+    const int64_t slot = pc == 0 ? first_slot : slot_of(bg.slot, f + pc, true);
     const v4f* src = reinterpret_cast<const v4f*>(partials + slot * (int64_t)(BM * BN) + r0 * BN);
     v4f v[PER];
 #pragma unroll
@@ -752,79 +742,6 @@ __global__ __launch_bounds__(256) void bwd_fixup_kernel(GemmArgs gd, GemmArgs gw
   }
 }
 
-struct BwdPlan {
-  BwdGeom geom;
-  int64_t grid;
-  bool partial;  // some tile is shared by several workgroups (workspace needed)
-  size_t bytes;
-};
-
-// Host mirrors of the range arithmetic above.
-inline int64_t h_start(int64_t w, int64_t W, int64_t G) { return w * W / G; }
-inline int64_t h_owner(int64_t u, int64_t W, int64_t G) { return ((u + 1) * G - 1) / W; }
-
-// Persistent grid: one workgroup per CU of an MI355X (fewer for tiny shapes).
-constexpr int64_t kSkGrid = 256;
-
-struct SkPlan {
-  SkGeom geom;
-  int64_t grid;
-  bool partial;  // some stream-K tile is shared by several workgroups (workspace needed)
-  size_t bytes;
-};
-
-SkPlan sk_plan(int64_t I, int64_t J, int64_t R) {
-  SkPlan p{};
-  p.geom.tiles_m = (I + BM - 1) / BM;
-  p.geom.tiles_n = (J + BN - 1) / BN;
-  const int64_t T = p.geom.tiles_m * p.geom.tiles_n, U = R / 512;
-  p.grid = T * U < kSkGrid ? T * U : kSkGrid;
-  p.geom.dp_tiles = (T / p.grid) * p.grid;
-  const int64_t W = (T - p.geom.dp_tiles) * U;
-  const int64_t Gs = W < p.grid ? W : p.grid;
-  p.geom.units = W;
-  p.geom.sk_grid = Gs;
-  // no tile is shared when there is no stream-K part, when a tile is one
-  // unit, or when Gs divides W and U divides W / Gs (whole tiles per workgroup)
-  p.partial = !(W == 0 || U == 1 || (W % Gs == 0 && (W / Gs) % U == 0));
-  p.geom.sk_tiles = (W > 0 && W % Gs == 0 && U % (W / Gs) == 0) ? T - p.geom.dp_tiles : 0;
-  p.bytes = p.partial ? (size_t)(2 * p.grid) * BM * BN * sizeof(float) : 0;
-  return p;
-}
-
-// Dgrad (I = M, J = K, R = N) and Wgrad (I = N, J = K, R = M) of one linear.
-BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K) {
-  BwdPlan p{};
-  BwdGeom& b = p.geom;
-  b.tm0 = (M + BM - 1) / BM;
-  b.tn0 = (K + BN - 1) / BN;
-  b.u0 = N / 512;
-  b.t0 = b.tm0 * b.tn0;
-  b.tm1 = (N + BM - 1) / BM;
-  b.tn1 = (K + BN - 1) / BN;
-  b.u1 = M / 512;
-  b.w0 = b.t0 * b.u0;
-  b.units = b.w0 + b.tm1 * b.tn1 * b.u1;
-  p.grid = b.units < kSkGrid ? b.units : kSkGrid;
-  // round-robin tiles for a problem whose ranges all hold whole tiles: every
-  // range of the grid holds the same number q of units (G divides W), the
-  // problem starts and ends on range boundaries, and U divides q
-  if (b.units % p.grid == 0) {
-    const int64_t q = b.units / p.grid;
-    if (b.w0 % q == 0 && q % b.u0 == 0) b.k0 = q / b.u0;
-    if ((b.units - b.w0) % q == 0 && q % b.u1 == 0) b.k1 = q / b.u1;
-  }
-  // a tile is shared when its first and last units fall in different ranges
-  const int64_t T = b.t0 + b.tm1 * b.tn1;
-  for (int64_t t = 0; t < T && !p.partial; ++t) {
-    const bool p1 = t >= b.t0;
-    const int64_t U = p1 ? b.u1 : b.u0, first = (p1 ? b.w0 + (t - b.t0) * U : t * U);
-    p.partial = h_owner(first, b.units, p.grid) != h_owner(first + U - 1, b.units, p.grid);
-  }
-  p.bytes = p.partial ? (size_t)(2 * p.grid) * BM * BN * sizeof(float) : 0;
-  return p;
-}
-
 template <class K>
 hipError_t set_lds_attr(K* kernel, std::atomic<uint64_t>* done) {
   return ensure_lds_limit(reinterpret_cast<const void*>(kernel), LDS_BYTES, done);
@@ -846,11 +763,11 @@ hipError_t launch_mx_streamk(const GemmArgs& g, hipStream_t stream) {
   const SkPlan p = sk_plan(g.I, g.J, g.R);
   static std::atomic<uint64_t> attr_set{0};
   if (hipError_t e = set_lds_attr(&gemm_mx_streamk_kernel<BROW>, &attr_set)) return e;
-  float* const partials = p.partial ? g.ws : nullptr;
+  float* const partials = p.slots > 0 ? g.ws : nullptr;
   hipLaunchKernelGGL(gemm_mx_streamk_kernel<BROW>, dim3((uint32_t)p.grid), dim3(THREADS), LDS_BYTES, stream, g, p.geom,
                      partials);
   if (hipError_t e = hipGetLastError()) return e;
-  if (!p.partial) return hipSuccess;
+  if (p.slots == 0) return hipSuccess;
   const int64_t sk_tiles = p.geom.tiles_m * p.geom.tiles_n - p.geom.dp_tiles;
   hipLaunchKernelGGL(sk_fixup_kernel, dim3((uint32_t)(sk_tiles * (BM / FIX_ROWS))), dim3(256), 0, stream, g, p.geom,
                      partials);
@@ -862,11 +779,11 @@ hipError_t launch_bwd(const GemmArgs& gd, const GemmArgs& gw, float* ws, hipStre
   const BwdPlan p = bwd_plan(gd.I, gd.R, gd.J);
   static std::atomic<uint64_t> attr_set{0};
   if (hipError_t e = set_lds_attr(&gemm_mx_bwd_kernel<BT>, &attr_set)) return e;
-  float* const partials = p.partial ? ws : nullptr;
+  float* const partials = p.slots > 0 ? ws : nullptr;
   hipLaunchKernelGGL(gemm_mx_bwd_kernel<BT>, dim3((uint32_t)p.grid), dim3(THREADS), LDS_BYTES, stream, gd, gw, p.geom,
                      partials);
   if (hipError_t e = hipGetLastError()) return e;
-  if (!p.partial) return hipSuccess;
+  if (p.slots == 0) return hipSuccess;
   const int64_t T = p.geom.t0 + p.geom.tm1 * p.geom.tn1;
   hipLaunchKernelGGL(bwd_fixup_kernel, dim3((uint32_t)(T * (BM / FIX_ROWS))), dim3(256), 0, stream, gd, gw, p.geom,
                      p.grid, partials);
@@ -875,38 +792,9 @@ hipError_t launch_bwd(const GemmArgs& gd, const GemmArgs& gw, float* ws, hipStre
 
 }  // namespace
 
-bool gemm_mx_eligible(const GemmArgs& g) {
-  const int64_t nkb = g.R / 128;
-  if (nkb % 4 != 0) return false;
-  // weight-block mode keeps the tile's whole column of block scales in LDS
-  if (g.bmode == BScale::Block && nkb > MAX_KB) return false;
-  // per-lane 32-bit offsets: 256 rows x R bytes of codes, 256 rows of scales
-  // (the transposed-B layout: 128 rows x J bytes)
-  if (g.R > (int64_t(1) << 22)) return false;
-  if (g.bt && (g.bmode != BScale::Block || g.J > (int64_t(1) << 22))) return false;
-  if ((reinterpret_cast<uintptr_t>(g.sa) & 15) != 0) return false;
-  if (g.bmode == BScale::Row && (reinterpret_cast<uintptr_t>(g.sb) & 15) != 0) return false;
-  return true;
-}
-
-size_t gemm_mx_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode) {
-  if (bmode != BScale::Row || (R / 128) % 4 != 0) return 0;
-  return sk_plan(I, J, R).bytes;
-}
-
 hipError_t launch_gemm_mx(const GemmArgs& g, hipStream_t stream) {
   if (g.bmode == BScale::Row) return launch_mx_streamk<true>(g, stream);
   return g.bt ? launch_mx<false, true>(g, stream) : launch_mx<false, false>(g, stream);
-}
-
-bool gemm_mx_bwd_eligible(const GemmArgs& gd, const GemmArgs& gw) {
-  return gd.bmode == BScale::Block && gw.bmode == BScale::Row && gemm_mx_eligible(gd) && gemm_mx_eligible(gw) &&
-         gd.I == gw.R && gd.R == gw.I && gd.J == gw.J;
-}
-
-size_t gemm_mx_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if ((N / 128) % 4 != 0 || (M / 128) % 4 != 0) return 0;
-  return bwd_plan(M, N, K).bytes;
 }
 
 hipError_t launch_gemm_mx_bwd(const GemmArgs& gd, const GemmArgs& gw, hipStream_t stream) {

@@ -1,8 +1,8 @@
 // Quantizer kernels for gfx950: bf16 -> E4M3 codes + fp32 scales.
 //
 // What is computed ("Puro-2B ... part 3/7", section 3.2, second and third
-// paragraphs): one scale per 128 consecutive values along the GEMM reduction
-// dimension for activations and gradients, one per 128x128 block for weights;
+// paragraphs): activations and gradients carry a scale for every 128-element
+// run along K (the contraction's K), weights one per 128x128 tile;
 // each scale a power of two (Pow2Scale), or, as a numerics variant, the
 // unconstrained fp32 amax / 448 of the DeepSeek-V3 recipe that the same
 // paragraph sets against it (Fp32Scale).  The scale rules and the cast are

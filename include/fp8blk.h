@@ -8,9 +8,9 @@
  *     - Transformer linear layers take E4M3 operands; the BF16 inputs and
  *       weights are quantized right before each GEMM and a BF16 output is
  *       materialised (fourth paragraph);
- *     - activations and activation gradients get one scale per 128
- *       consecutive values along the GEMM reduction dimension, weights one
- *       scale per 128x128 block (second paragraph);
+ *     - activations and their gradients carry a scale for every
+ *       128-element group taken along K, the contracted dimension; weights
+ *       carry one per 128x128 tile (second paragraph);
  *     - every block scale is a power of two, i.e. it has the expressiveness
  *       of an E8M0 exponent (third paragraph);
  *     - Fprop, Dgrad and Wgrad of the QKV, attention-output and MLP
@@ -55,12 +55,14 @@
  *   - Return value: FP8BLK_OK (0), or a negative FP8BLK_ERR_* code.  All
  *     argument checks run on the host before any launch: on an error nothing
  *     is enqueued and no output is touched.  No C++ exception crosses the ABI.
- *   - Scales handed to the GEMMs with FP8BLK_ALGO_DEFAULT or
- *     FP8BLK_ALGO_SCALED_MFMA (and to the named GEMM functions, which use
- *     DEFAULT) must be exact powers of two in [2^-126, 2^127], as the
- *     FP8BLK_SCALE_POW2 quantizers produce: those paths use only their
- *     exponent bits.  FP8BLK_ALGO_PROMOTE takes any positive finite fp32
- *     scales; FP8BLK_SCALE_FP32 operands need it.
+ *   - The scale arrays do not say which rule made them, so the GEMMs that
+ *     can take either are told: fp8_block_gemm and the two backward calls
+ *     take a scale_mode argument.  With FP8BLK_SCALE_FP32 they run the
+ *     PROMOTE algorithm (FP8BLK_ALGO_DEFAULT is resolved to it, and an
+ *     explicit FP8BLK_ALGO_SCALED_MFMA is refused with FP8BLK_ERR_ARG,
+ *     because the block-scaled MFMA keeps only a scale's exponent field).
+ *     The named Fprop / Dgrad / Wgrad functions take FP8BLK_SCALE_POW2
+ *     operands only: exact powers of two in [2^-126, 2^127].
  */
 #ifndef FP8BLK_H
 #define FP8BLK_H
@@ -75,7 +77,8 @@ extern "C" {
 #endif
 
 /* Scale rule of the quantizers (the readings above): POW2, the pages' rule,
- * or FP32, s = amax / 448 unconstrained (GEMMs with FP8BLK_ALGO_PROMOTE only). */
+ * or FP32, s = amax / 448 unconstrained.  The GEMMs that take a scale_mode
+ * are told with the same values which rule made their operands' scales. */
 enum fp8blk_scale_mode { FP8BLK_SCALE_POW2 = 0, FP8BLK_SCALE_FP32 = 1 };
 
 /* GEMM output element type.  FP32_ACCUM: fp32 output that the result is
@@ -270,9 +273,14 @@ int fp8_block_gemm_wgrad(int64_t M, int64_t N, int64_t K,
  * (deterministic).  Shapes the fused launch does not take (the 128-block
  * count of M or N not a multiple of 4, N > 16384) run as the two separate
  * contractions.
+ *   scale_mode: the rule that made all the operands' scales.
+ *     FP8BLK_SCALE_POW2 takes the fused launch above; FP8BLK_SCALE_FP32
+ *     (amax / 448 scales) runs Dgrad and then Wgrad with the PROMOTE
+ *     algorithm, which reads the whole fp32 scales.  Anything else:
+ *     FP8BLK_ERR_ARG.
  *   workspace: at least fp8_block_gemm_workspace_size(FP8BLK_OP_BACKWARD,
- *     M, N, K) bytes, 16-byte aligned, contents on entry irrelevant; NULL
- *     when that size is 0.
+ *     M, N, K) bytes (enough for either scale_mode), 16-byte aligned,
+ *     contents on entry irrelevant; NULL when that size is 0.
  *   dx and dw must not be the same buffer (FP8BLK_ERR_ARG).
  */
 int fp8_block_gemm_backward(int64_t M, int64_t N, int64_t K,
@@ -280,7 +288,7 @@ int fp8_block_gemm_backward(int64_t M, int64_t N, int64_t K,
                             const uint8_t *qwT, const float *sw,
                             const uint8_t *qdyT, const float *sdyT,
                             const uint8_t *qxT, const float *sxT,
-                            void *dx, int dx_dtype, void *dw, int dw_dtype,
+                            void *dx, int dx_dtype, void *dw, int dw_dtype, int scale_mode,
                             void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
@@ -293,7 +301,7 @@ int fp8_block_gemm_backward_w(int64_t M, int64_t N, int64_t K,
                               const uint8_t *qw, const float *sw,
                               const uint8_t *qdyT, const float *sdyT,
                               const uint8_t *qxT, const float *sxT,
-                              void *dx, int dx_dtype, void *dw, int dw_dtype,
+                              void *dx, int dx_dtype, void *dw, int dw_dtype, int scale_mode,
                               void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
@@ -303,12 +311,17 @@ int fp8_block_gemm_backward_w(int64_t M, int64_t N, int64_t K,
  *   op = FP8BLK_OP_WGRAD: (a, sa, b, sb) = (qdyT, sdyT, qxT, sxT), out [N][K]
  *   op = FP8BLK_OP_DGRAD_W: (a, sa, b, sb) = (qdy, sdy, qw, sw), out [M][K]
  * Operand layouts, workspace and errors are as for the named functions above
- * (which are this call with FP8BLK_ALGO_DEFAULT); a bad op or algo gives
- * FP8BLK_ERR_ARG.
+ * (which are this call with FP8BLK_ALGO_DEFAULT and FP8BLK_SCALE_POW2); a
+ * bad op or algo gives FP8BLK_ERR_ARG.
+ *   scale_mode: the rule that made sa and sb.  FP8BLK_SCALE_POW2: any algo.
+ *     FP8BLK_SCALE_FP32 (amax / 448): FP8BLK_ALGO_DEFAULT runs PROMOTE,
+ *     FP8BLK_ALGO_PROMOTE is taken as is, and FP8BLK_ALGO_SCALED_MFMA gives
+ *     FP8BLK_ERR_ARG (it would keep only the scales' exponent bits).
+ *     Anything else: FP8BLK_ERR_ARG.
  */
 int fp8_block_gemm(int op, int64_t M, int64_t N, int64_t K,
                    const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
-                   void *out, int out_dtype, int algo,
+                   void *out, int out_dtype, int algo, int scale_mode,
                    void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes that the given contraction needs at this shape (0 if none;

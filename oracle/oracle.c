@@ -20,8 +20,9 @@
  * What is computed (readings where the pages are silent are marked READING):
  *   - E4M3 operands [P1 s3.2 para 1; P3 s2.3 table], OCP "fn" variant [OCP
  *     Table 1]: bias 7, no infinities, S.1111.111 is NaN, max 448.
- *   - activations / gradients: one scale per 128 consecutive values along the
- *     GEMM reduction dimension [P1 s3.2 para 2; P3 s2.3 table; P5 Method];
+ *   - activations / gradients: a scale for every 128-element group taken
+ *     along K, the contracted dimension [P1 s3.2 para 2; P3 s2.3 table;
+ *     P5 Method];
  *     weights: one scale per 128x128 block [same places].
  *   - every scale is a power of two (E8M0-like) [P1 s3.2 para 3; P3 s2.3].
  *     READING: s = 2^e with e the smallest integer such that amax <= 448*2^e

@@ -81,17 +81,30 @@ int main(void)
            FP8BLK_ERR_WORKSPACE);
     expect("backward dx == dw",
            fp8_block_gemm_backward(256, 256, 256, q, s, qT, sT, qT, sT, q, s, out, FP8BLK_OUT_BF16, out,
-                                   FP8BLK_OUT_BF16, NULL, 0, st),
+                                   FP8BLK_OUT_BF16, FP8BLK_SCALE_POW2, NULL, 0, st),
            FP8BLK_ERR_ARG);
     expect("backward_w misaligned dY codes",
            fp8_block_gemm_backward_w(256, 256, 256, q + 1, s, qT, sT, qT, sT, q, s, out, FP8BLK_OUT_BF16, out2,
-                                     FP8BLK_OUT_FP32, NULL, 0, st),
+                                     FP8BLK_OUT_FP32, FP8BLK_SCALE_POW2, NULL, 0, st),
            FP8BLK_ERR_ALIGN);
     expect("gemm bad op", fp8_block_gemm(9, 256, 256, 256, q, s, qT, sT, out, FP8BLK_OUT_BF16, FP8BLK_ALGO_DEFAULT,
-                                         NULL, 0, st),
+                                         FP8BLK_SCALE_POW2, NULL, 0, st),
            FP8BLK_ERR_ARG);
     expect("gemm bad algo", fp8_block_gemm(FP8BLK_OP_FPROP, 256, 256, 256, q, s, qT, sT, out, FP8BLK_OUT_BF16, 5,
-                                           NULL, 0, st),
+                                           FP8BLK_SCALE_POW2, NULL, 0, st),
+           FP8BLK_ERR_ARG);
+    /* amax / 448 scales keep their mantissa only in the promote algorithm */
+    expect("gemm fp32 scales, scaled MFMA",
+           fp8_block_gemm(FP8BLK_OP_FPROP, 256, 256, 256, q, s, qT, sT, out, FP8BLK_OUT_BF16,
+                          FP8BLK_ALGO_SCALED_MFMA, FP8BLK_SCALE_FP32, NULL, 0, st),
+           FP8BLK_ERR_ARG);
+    expect("gemm bad scale mode",
+           fp8_block_gemm(FP8BLK_OP_FPROP, 256, 256, 256, q, s, qT, sT, out, FP8BLK_OUT_BF16, FP8BLK_ALGO_DEFAULT,
+                          2, NULL, 0, st),
+           FP8BLK_ERR_ARG);
+    expect("backward bad scale mode",
+           fp8_block_gemm_backward_w(256, 256, 256, q, s, qT, sT, qT, sT, q, s, out, FP8BLK_OUT_BF16, out2,
+                                     FP8BLK_OUT_FP32, -1, NULL, 0, st),
            FP8BLK_ERR_ARG);
 
     /* helpers */

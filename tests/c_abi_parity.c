@@ -245,7 +245,7 @@ int main(void)
     FP8(fp8_block_gemm_wgrad(M, N, K, qdyT, sdyT, qxT, sxT, dw, FP8BLK_OUT_FP32, ws, ws_bytes, 0));
     FP8(fp8_block_gemm_wgrad(M, N, K, qdyT, sdyT, qxT, sxT, dwh, FP8BLK_OUT_BF16, ws, ws_bytes, 0));
     FP8(fp8_block_gemm_backward_w(M, N, K, qdy, sdy, qw, sw, qdyT, sdyT, qxT, sxT, dx2, FP8BLK_OUT_FP32, dw2,
-                                  FP8BLK_OUT_FP32, ws, ws_bytes, 0));
+                                  FP8BLK_OUT_FP32, FP8BLK_SCALE_POW2, ws, ws_bytes, 0));
     HIP(hipDeviceSynchronize());
     within_tolerance("fprop fp32", y, 0, M, N, y32, yb);
     within_tolerance("fprop bf16", yh, 1, M, N, y32, yb);

@@ -41,6 +41,15 @@ def host_f32(t) -> np.ndarray:
     return t.detach().float().cpu().numpy()
 
 
+def sample_rows(n: int, rng, k: int = 8) -> np.ndarray:
+    """Output rows for the oracle to recompute: the edges, one random row in
+    every 256-row band (so every 256x256 output tile is compared, each row
+    over all its columns) and k more random rows."""
+    fixed = [r for r in (0, 1, 127, 128, 255, 256, n // 2 + 17, n - 129, n - 1) if 0 <= r < n]
+    bands = [b + int(rng.integers(0, min(256, n - b))) for b in range(0, n, 256)]
+    return np.unique(np.concatenate([fixed, bands, rng.choice(n, min(k, n), replace=False)])).astype(np.int64)
+
+
 def note(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 

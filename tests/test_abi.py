@@ -77,7 +77,7 @@ def test_size_limits_without_overflow(lib):
     f = lib.fp8_block_gemm_fprop
     assert f(huge, huge, 256, P, P3, P2, P3, P, 0, None) == EARG
     assert f(1 << 26, 1 << 26, 1 << 26, P, P3, P2, P3, P, 0, None) == EARG            # M * N > 2^40
-    assert lib.fp8_block_gemm_backward(huge, 256, 256, P, P3, P2, P3, P, P3, P2, P3, P, 0, P + 64, 0,
+    assert lib.fp8_block_gemm_backward(huge, 256, 256, P, P3, P2, P3, P, P3, P2, P3, P, 0, P + 64, 0, 0,
                                        None, 0, None) == EARG
 
 
@@ -153,9 +153,9 @@ def test_gemm_errors(lib):
     assert f(256, 256, 256, MIS, P3, P2, P3, P, 0, None) == EALIGN
     assert f(256, 256, 256, P, P3 + 1, P2, P3, P, 0, None) == EALIGN
     g = lib.fp8_block_gemm
-    assert g(3, 256, 256, 256, P, P3, P2, P3, P, 0, 0, None, 0, None) == EARG   # op
-    assert g(5, 256, 256, 256, P, P3, P2, P3, P, 0, 0, None, 0, None) == EARG
-    assert g(4, 256, 256, 256, P, P3, P2, P3, P, 0, 1, None, 0, None) in (EHIP, EDEV)   # Dgrad from qw
+    assert g(3, 256, 256, 256, P, P3, P2, P3, P, 0, 0, 0, None, 0, None) == EARG   # op
+    assert g(5, 256, 256, 256, P, P3, P2, P3, P, 0, 0, 0, None, 0, None) == EARG
+    assert g(4, 256, 256, 256, P, P3, P2, P3, P, 0, 1, 0, None, 0, None) in (EHIP, EDEV)   # Dgrad from qw
     assert lib.fp8_block_gemm_workspace_size(4, 8192, 2048, 2048) == lib.fp8_block_gemm_workspace_size(1, 8192, 2048, 2048)
     d = lib.fp8_block_gemm_dgrad_w
     assert d(256, 256, 256, P, P3, P2, P3, P, 0, None) in (EHIP, EDEV)
@@ -163,7 +163,7 @@ def test_gemm_errors(lib):
     assert d(256, 200, 256, P, P3, P2, P3, P, 0, None) == EDIM
     assert d(256, 256, 256, P, P3, MIS, P3, P, 0, None) == EALIGN
     assert d(256, 256, 256, P, P3, P2, P3, P, 4, None) == EARG
-    assert g(0, 256, 256, 256, P, P3, P2, P3, P, 0, 9, None, 0, None) == EARG   # algo
+    assert g(0, 256, 256, 256, P, P3, P2, P3, P, 0, 9, 0, None, 0, None) == EARG   # algo
     # wgrad at a shape that splits the reduction needs a workspace
     need = lib.fp8_block_gemm_workspace_size(2, 8192, 256, 256)
     assert need > 0
@@ -180,8 +180,8 @@ def test_backward_errors(lib, fn):
     need = lib.fp8_block_gemm_workspace_size(3, 8192, 2048, 2048)
     assert need > 0 and need != ctypes.c_size_t(-1).value
     names = ("M", "N", "K", "qdy", "sdy", "qwT", "sw", "qdyT", "sdyT", "qxT", "sxT", "dx", "dxt", "dw", "dwt",
-             "ws", "wsb", "stream")
-    ok = (8192, 2048, 2048, P, P3, P2, P3, P4, P5, P6, P7, 0x800000, 0, 0x900000, 1, 0xA00000, need, None)
+             "mode", "ws", "wsb", "stream")
+    ok = (8192, 2048, 2048, P, P3, P2, P3, P4, P5, P6, P7, 0x800000, 0, 0x900000, 1, 0, 0xA00000, need, None)
 
     def call(**kw):
         a = dict(zip(names, ok))
@@ -200,6 +200,37 @@ def test_backward_errors(lib, fn):
     assert call(qxT=MIS) == EALIGN
 
 
+@pytest.mark.parametrize("op", [0, 1, 2, 4])
+def test_gemm_scale_mode(lib, op):
+    """amax / 448 scales are not powers of two: the block-scaled MFMA would
+    keep only their exponent bits, so that pairing is refused before any
+    launch, DEFAULT resolves to PROMOTE (valid: fails later, on the device
+    check), and an unknown scale mode is refused."""
+    g = lib.fp8_block_gemm
+    need = lib.fp8_block_gemm_workspace_size(op, 8192, 2048, 2048)
+    ws = P if need else None
+    args = lambda algo, mode: (op, 8192, 2048, 2048, P, P3, P2, P3, P, 0, algo, mode, ws, need, None)
+    assert g(*args(2, 1)) == EARG                       # SCALED_MFMA with amax / 448 scales
+    for algo in (0, 1):                                 # DEFAULT (-> PROMOTE) and PROMOTE: valid
+        assert g(*args(algo, 1)) in (EHIP, EDEV)
+    for algo in (0, 1, 2):                              # power-of-two scales: every algorithm
+        assert g(*args(algo, 0)) in (EHIP, EDEV)
+    for mode in (-1, 2, 7):
+        assert g(*args(0, mode)) == EARG
+
+
+@pytest.mark.parametrize("fn", ["fp8_block_gemm_backward", "fp8_block_gemm_backward_w"])
+def test_backward_scale_mode(lib, fn):
+    f = getattr(lib, fn)
+    need = lib.fp8_block_gemm_workspace_size(3, 8192, 2048, 2048)
+    args = lambda mode: (8192, 2048, 2048, P, P3, P2, P3, 0x400000, 0x500000, 0x600000, 0x700000, 0x800000, 0,
+                         0x900000, 1, mode, 0xA00000, need, None)
+    assert f(*args(0)) in (EHIP, EDEV)
+    assert f(*args(1)) in (EHIP, EDEV)                  # amax / 448: the promote algorithm
+    for mode in (-1, 2):
+        assert f(*args(mode)) == EARG
+
+
 def test_workspace_query(lib):
     q = lib.fp8_block_gemm_workspace_size
     assert q(0, 8192, 12288, 2048) == 0                 # fprop never needs one
@@ -207,11 +238,14 @@ def test_workspace_query(lib):
     assert q(2, 100, 256, 256) == ctypes.c_size_t(-1).value
     assert q(7, 256, 256, 256) == ctypes.c_size_t(-1).value
     # O-projection wgrad: 64 output tiles of 256x256 whose 8192-token
-    # reduction is shared by several workgroups: enough for the stream-K
-    # partial tiles (two 256x256 fp32 slots per workgroup of at most 256)
-    # and for the general kernel's split-K partials
+    # reduction (16 units of 512) is cut into 4 pieces each by the 256
+    # workgroups: one 256x256 fp32 slot per partial segment (256 of them),
+    # and enough for the general kernel's split-K partials too
     n = q(2, 8192, 2048, 2048)
-    assert n >= 2 * 256 * 256 * 256 * 4 and n >= 2 * 2048 * 2048 * 4
+    assert n == max(256 * 256 * 256 * 4, 2 * 2048 * 2048 * 4)
+    # the fused backward of the same linear: Dgrad's 256 tiles fall whole
+    # into ranges, Wgrad's 64 tiles are cut in two -- 128 partial segments
+    assert q(3, 8192, 2048, 2048) == max(128 * 256 * 256 * 4, n)
     # a 512-token reduction is one unit per tile: no tile is shared
     assert q(2, 512, 5120, 7680) == 0
     # dimensions the GEMM entry points reject are invalid shapes here too

@@ -24,7 +24,7 @@ import pytest
 import oracle
 import blockwise_fp8_linear_amd as fb
 from blockwise_fp8_linear_amd import synth
-from gpu_util import check_bf16, check_f32, dev_bf16, host, host_f32, note, require_gpu
+from gpu_util import check_bf16, check_f32, dev_bf16, host, host_f32, note, require_gpu, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +56,7 @@ class Layer:
         import torch
         self.M, self.K = x.shape
         self.N = w.shape[0]
+        self.mode = mode
         xt, wt, dyt = dev_bf16(x), dev_bf16(w), dev_bf16(dy)
         self.g = {}
         self.g["qx"], self.g["sx"] = fb.fp8_quantize_rowgroup(xt, scale_mode=mode)
@@ -71,7 +72,7 @@ class Layer:
         self.o["qdy"], self.o["sdy"] = oracle.quantize_rowgroup(dy, mode=mode)
         self.o["qdyT"], self.o["sdyT"] = oracle.quantize_colgroup(dy, mode=mode)
 
-    def gpu(self, op, algo, out_dtype):
+    def gpu(self, op, algo, out_dtype, out=None):
         g = self.g
         args = {"fprop": (g["qx"], g["sx"], g["qw"], g["sw"]),
                 "dgrad": (g["qdy"], g["sdy"], g["qwT"], g["sw"]),
@@ -79,7 +80,8 @@ class Layer:
                 "wgrad": (g["qdyT"], g["sdyT"], g["qxT"], g["sxT"])}[op]
         opc = {"fprop": fb.FP8BLK_OP_FPROP, "dgrad": fb.FP8BLK_OP_DGRAD, "dgrad_w": fb.FP8BLK_OP_DGRAD_W,
                "wgrad": fb.FP8BLK_OP_WGRAD}[op]
-        return fb.fp8_block_gemm(opc, *args, self.M, self.N, self.K, out_dtype=out_dtype, algo=algo)
+        return fb.fp8_block_gemm(opc, *args, self.M, self.N, self.K, out_dtype=out_dtype, algo=algo, out=out,
+                                 scale_mode=self.mode)
 
     def ref(self, op, rows):
         o = self.o
@@ -92,6 +94,18 @@ class Layer:
     def out_rows(self, op):
         return self.N if op == "wgrad" else self.M
 
+    def out_shape(self, op):
+        return {"fprop": (self.M, self.N), "wgrad": (self.N, self.K)}.get(op, (self.M, self.K))
+
+
+def nan_filled(shape, dtype):
+    """An output buffer holding NaN everywhere (bf16 0xFFFF, fp32 0xFFFFFFFF),
+    so that any element a kernel fails to write shows up as non-finite."""
+    import torch
+    t = torch.empty(shape, dtype=dtype, device="cuda")
+    t.view(torch.uint8).fill_(0xFF)
+    return t
+
 
 def check_op(layer, op, algo_name, rows=None, what=""):
     import torch
@@ -99,9 +113,13 @@ def check_op(layer, op, algo_name, rows=None, what=""):
     nrows = layer.out_rows(op)
     rows = np.arange(nrows) if rows is None else np.asarray(rows)
     y32, _, bound = layer.ref(op, rows)
-    yf = layer.gpu(op, algo, torch.float32)
-    yb = layer.gpu(op, algo, torch.bfloat16)
+    # NaN-filled outputs: every element of both must be written (finite),
+    # including the rows the oracle does not recompute
+    yf = layer.gpu(op, algo, torch.float32, out=nan_filled(layer.out_shape(op), torch.float32))
+    yb = layer.gpu(op, algo, torch.bfloat16, out=nan_filled(layer.out_shape(op), torch.bfloat16))
     torch.cuda.synchronize()
+    assert bool(torch.isfinite(yf).all()) and bool(torch.isfinite(yb).all()), f"{op} {algo_name}: unwritten outputs"
+
     yf_h = host_f32(yf)[rows]
     yb_h = host(yb)[rows]
     tag = f"{what} {op} {algo_name} M={layer.M} N={layer.N} K={layer.K}"
@@ -156,9 +174,11 @@ def test_tiny_fprop_config():
 
 
 def _sample_rows(n, key, k=24):
-    rng = synth.rng_for(*key)
-    fixed = [r for r in (0, 1, 127, 128, 255, 256, n // 2 + 17, n - 129, n - 1) if 0 <= r < n]
-    return np.unique(np.concatenate([fixed, rng.choice(n, min(k, n), replace=False)]))
+    """Output rows for the oracle to recompute: the edges, k random rows, and
+    one random row in every 256-row band, so that every output tile (and, in
+    the stream-K kernels, every shared tile and its fix-up) is compared; each
+    row is compared over all its columns."""
+    return sample_rows(n, synth.rng_for(*key), k)
 
 
 def test_single_linear_fprop_full_size():
@@ -174,9 +194,12 @@ def test_single_linear_fprop_full_size():
     rows = _sample_rows(8192, (62, 0))
     y32, _, bound = oracle.gemm_fprop(ox, osx, ow, osw, rows=rows)
     for algo_name, algo in ALGOS.items():
-        yf = fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, qx, sx, qw, sw, 8192, 12288, 2048, out_dtype=torch.float32, algo=algo)
-        yb = fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, qx, sx, qw, sw, 8192, 12288, 2048, algo=algo)
+        yf = fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, qx, sx, qw, sw, 8192, 12288, 2048, out_dtype=torch.float32, algo=algo,
+                               out=nan_filled((8192, 12288), torch.float32))
+        yb = fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, qx, sx, qw, sw, 8192, 12288, 2048, algo=algo,
+                               out=nan_filled((8192, 12288), torch.bfloat16))
         torch.cuda.synchronize()
+        assert bool(torch.isfinite(yf).all()) and bool(torch.isfinite(yb).all()), "unwritten outputs"
         yf_h, yb_h = host_f32(yf)[rows], host(yb)[rows]
         st = check_f32(yf_h, y32, bound, f"single linear {algo_name}")
         check_bf16(yb_h, yf_h, y32, bound, f"single linear {algo_name}")
@@ -194,9 +217,12 @@ def test_outlier_stress_fprop_full_size():
     rows = _sample_rows(8192, (63, 0))
     y32, _, bound = oracle.gemm_fprop(ox, osx, ow, osw, rows=rows)
     for algo_name, algo in ALGOS.items():
-        yf = fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, qx, sx, qw, sw, 8192, 12288, 2048, out_dtype=torch.float32, algo=algo)
-        yb = fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, qx, sx, qw, sw, 8192, 12288, 2048, algo=algo)
+        yf = fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, qx, sx, qw, sw, 8192, 12288, 2048, out_dtype=torch.float32, algo=algo,
+                               out=nan_filled((8192, 12288), torch.float32))
+        yb = fb.fp8_block_gemm(fb.FP8BLK_OP_FPROP, qx, sx, qw, sw, 8192, 12288, 2048, algo=algo,
+                               out=nan_filled((8192, 12288), torch.bfloat16))
         torch.cuda.synchronize()
+        assert bool(torch.isfinite(yf).all()) and bool(torch.isfinite(yb).all()), "unwritten outputs"
         yf_h, yb_h = host_f32(yf)[rows], host(yb)[rows]
         st = check_f32(yf_h, y32, bound, f"outlier {algo_name}")
         check_bf16(yb_h, yf_h, y32, bound, f"outlier {algo_name}")
@@ -343,9 +369,15 @@ def check_backward(layer, rows_dx, rows_dw, what):
     import torch
     g = layer.g
     args = (g["qdy"], g["sdy"], g["qwT"], g["sw"], g["qdyT"], g["sdyT"], g["qxT"], g["sxT"])
-    dxf, dwf = fb.fp8_block_gemm_backward(*args, dx_dtype=torch.float32, dw_dtype=torch.float32)
-    dxb, dwb = fb.fp8_block_gemm_backward(*args)
+    M, N, K = layer.M, layer.N, layer.K
+    dxf, dwf = fb.fp8_block_gemm_backward(*args, dx_dtype=torch.float32, dw_dtype=torch.float32,
+                                          dx=nan_filled((M, K), torch.float32), dw=nan_filled((N, K), torch.float32),
+                                          scale_mode=layer.mode)
+    dxb, dwb = fb.fp8_block_gemm_backward(*args, dx=nan_filled((M, K), torch.bfloat16),
+                                          dw=nan_filled((N, K), torch.bfloat16), scale_mode=layer.mode)
     torch.cuda.synchronize()
+    for t in (dxf, dwf, dxb, dwb):
+        assert bool(torch.isfinite(t).all()), f"{what}: unwritten backward outputs"
     for op, rows, yf, yb in (("dgrad", rows_dx, dxf, dxb), ("wgrad", rows_dw, dwf, dwb)):
         y32, _, bound = layer.ref(op, rows)
         tag = f"{what} backward/{op} M={layer.M} N={layer.N} K={layer.K}"
@@ -375,6 +407,32 @@ def test_backward_small(shape):
     torch.cuda.synchronize()
     assert torch.equal(dxf, dx2) and torch.equal(dwf, dw2), "backward is not deterministic"
     assert np.array_equal(host_f32(acc), host_f32(old) + host_f32(dwf)), "dW accumulation differs"
+
+
+@pytest.mark.parametrize("shape", [(1024, 512, 384), (384, 640, 512)])
+def test_fp32_scales_route_to_promote(shape):
+    """amax / 448 scales told to the GEMMs by scale_mode: DEFAULT runs the
+    promote algorithm (bit-identical to asking for it), the block-scaled MFMA
+    is refused before any launch, and the backward call runs both
+    contractions with the promote algorithm, within the tolerance of the
+    oracle's fp32-scale results."""
+    import torch
+    M, N, K = shape
+    key = (72, M, N, K)
+    layer = Layer(varied((M, K), 1.0, key + (0,)), varied((N, K), 0.02, key + (1,)),
+                  varied((M, N), 1e-3, key + (2,)), mode=1)
+    for op in OPS:
+        a = layer.gpu(op, fb.FP8BLK_ALGO_DEFAULT, torch.float32)
+        b = layer.gpu(op, fb.FP8BLK_ALGO_PROMOTE, torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), f"{op}: DEFAULT with fp32 scales is not PROMOTE"
+        with pytest.raises(RuntimeError, match="bad enum"):
+            layer.gpu(op, fb.FP8BLK_ALGO_SCALED_MFMA, torch.float32)
+    dxf, dwf = check_backward(layer, np.arange(M), np.arange(N), "fp32 scales")
+    dx = layer.gpu("dgrad", fb.FP8BLK_ALGO_PROMOTE, torch.float32)
+    dw = layer.gpu("wgrad", fb.FP8BLK_ALGO_PROMOTE, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(dxf, dx) and torch.equal(dwf, dw), "backward with fp32 scales is not the promote pair"
 
 
 @pytest.mark.parametrize("li", range(4))

@@ -64,3 +64,39 @@ def test_two_threads_two_streams():
         for rep, res in enumerate(out[i]):
             for name, a, b in zip(("y", "dx", "dw"), res, ref[i]):
                 assert torch.equal(a, b), f"shape {shapes[i]}, repetition {rep}: {name} differs"
+
+
+def test_non_current_stream_owns_what_the_call_allocates():
+    """A call given a stream other than the current one, with its outputs and
+    workspace left for the binding to allocate: the workspace is released to
+    torch's caching allocator when the wrapper returns, while the stream-K
+    kernels and their fix-up still use it on that stream.  It must belong to
+    that stream, so that the current stream's own allocations (made and
+    written at once, below) cannot reuse it before the stream is done."""
+    import torch
+    M, N, K = 1024, 1536, 1024          # Wgrad and the fused backward share tiles here: a workspace is used
+    assert fb.fp8_block_gemm_workspace_size(fb.FP8BLK_OP_WGRAD, M, N, K) > 0
+    assert fb.fp8_block_gemm_workspace_size(fb.FP8BLK_OP_BACKWARD, M, N, K) > 0
+    x = dev_bf16(synth.normal_bf16((M, K), 1.0, 82, 0))
+    w = dev_bf16(synth.normal_bf16((N, K), 0.02, 82, 1))
+    dy = dev_bf16(synth.normal_bf16((M, N), 1e-3, 82, 2))
+    ref = _linear(x, w, dy, None)
+    qx, sx, qxT, sxT = fb.fp8_quantize_dual(x)
+    qdy, sdy, qdyT, sdyT = fb.fp8_quantize_dual(dy)
+    ref_dw = fb.fp8_block_gemm_wgrad(qdyT, sdyT, qxT, sxT, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()              # default priority; never made current here
+    nbytes = fb.fp8_block_gemm_workspace_size(fb.FP8BLK_OP_BACKWARD, M, N, K)
+    for rep in range(4):
+        side.wait_stream(torch.cuda.current_stream())
+        y, dx, dw = _linear(x, w, dy, side)
+        dw2 = fb.fp8_block_gemm_wgrad(qdyT, sdyT, qxT, sxT, out_dtype=torch.float32, stream=side)
+        # the current stream allocates blocks of the workspace's size and
+        # overwrites them while the side stream may still be running
+        junk = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(0xFF) for _ in range(4)]
+        side.synchronize()
+        torch.cuda.synchronize()
+        del junk
+        for name, a, b in zip(("y", "dx", "dw"), (y, dx, dw), ref):
+            assert torch.equal(a, b), f"repetition {rep}: {name} differs from the single-stream result"
+        assert torch.equal(dw2, ref_dw), f"repetition {rep}: Wgrad differs from the single-stream result"
