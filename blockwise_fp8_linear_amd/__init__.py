@@ -33,6 +33,8 @@ FP8BLK_OP_DGRAD_W = 4
 FP8BLK_ALGO_DEFAULT = 0
 FP8BLK_ALGO_PROMOTE = 1
 FP8BLK_ALGO_SCALED_MFMA = 2
+FP8BLK_ERR_SCRATCH = -8
+FP8BLK_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 _lib = None
 
@@ -67,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fp8_block_gemm_dgrad_w": [i64, i64, i64, vp, vp, vp, vp, vp, i32, vp],
         "fp8_block_gemm_backward_w": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, sz,
                                       vp],
+        "fp8_block_gemm_backward_w_noalloc": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
+                                              vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -430,3 +434,30 @@ def _backward(fn, qdy, sdy, wcodes, wrole, sw, qdyT, sdyT, qxT, sxT, dx_dtype, d
                                        w.data_ptr(), _odt(dw_dtype, accumulate_dw, dw), scale_mode, wptr, wbytes,
                                        _stream(stream)))
     return x, w
+
+
+def fp8_block_gemm_backward_w_noalloc(qdy, sdy, qw, sw, qdyT, sdyT, qxT, sxT, dx, dw, stream=None,
+                                      accumulate_dw=False, scale_mode=FP8BLK_SCALE_POW2):
+    """fp8_block_gemm_backward_w for callers that cannot allocate: the
+    library's static device scratch stands in for the workspace, and the
+    outputs dx [M,K] and dw [N,K] (bf16 or fp32) must be given -- nothing is
+    allocated, here or in the library.  Calls that overlap on one GPU share
+    that scratch and race: order them on one stream.  Raises RuntimeError
+    (FP8BLK_ERR_SCRATCH) if the launch would need more scratch than
+    FP8BLK_NOALLOC_SCRATCH_BYTES."""
+    import torch
+    M, N = qdy.shape
+    K = qw.shape[1]
+    _operands(((qdy, sdy, "dy", "qdy"), (qw, sw, "w", "weight codes"), (qdyT, sdyT, "dyT", "qdyT"),
+               (qxT, sxT, "xT", "qxT")), M, N, K)
+    for t, name, shape in ((dx, "dx", (M, K)), (dw, "dw", (N, K))):
+        if t is None:
+            raise ValueError(f"{name}: the no-allocation call needs its outputs")
+        if t.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError(f"{name}: bfloat16 or float32 expected")
+        _shape(_dense(t, t.dtype, name), shape, name)
+    _check(load_library().fp8_block_gemm_backward_w_noalloc(
+        M, N, K, qdy.data_ptr(), sdy.data_ptr(), qw.data_ptr(), sw.data_ptr(), qdyT.data_ptr(), sdyT.data_ptr(),
+        qxT.data_ptr(), sxT.data_ptr(), dx.data_ptr(), _odt(dx.dtype), dw.data_ptr(),
+        _odt(dw.dtype, accumulate_dw, dw), scale_mode, _stream(stream)))
+    return dx, dw

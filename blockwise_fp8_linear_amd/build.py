@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8blk.so")
-SOURCES = ["quant.hip", "gemm.hip", "gemm_mx.hip", "plan.cpp", "api.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "gemm_mx.hip", "scratch.hip", "plan.cpp", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -58,6 +58,8 @@ const char* fp8_status_string(int status) {
     case FP8BLK_ERR_WORKSPACE: return "fp8blk: workspace smaller than fp8_block_gemm_workspace_size()";
     case FP8BLK_ERR_HIP: return "fp8blk: HIP runtime error at launch";
     case FP8BLK_ERR_DEVICE: return "fp8blk: the current device is not gfx950";
+    case FP8BLK_ERR_SCRATCH:
+      return "fp8blk: the call needs more scratch than the library's static buffer (FP8BLK_NOALLOC_SCRATCH_BYTES) holds";
     default: return "fp8blk: unknown status";
   }
 }
@@ -227,31 +229,63 @@ static size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return fused > wgrad ? fused : wgrad;
 }
 
-// Both backward entry points: dgrad_op is FP8BLK_OP_DGRAD (w = qwT [K][N])
-// or FP8BLK_OP_DGRAD_W (w = qw [N][K]).
-static int backward(int dgrad_op, int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy,
-                    const uint8_t* w, const float* sw, const uint8_t* qdyT, const float* sdyT, const uint8_t* qxT,
-                    const float* sxT, void* dx, int dx_dtype, void* dw, int dw_dtype, int scale_mode,
-                    void* workspace, size_t ws_bytes, hipStream_t stream) {
+// One backward call, checked and planned: Dgrad (gd) and Wgrad (gw), the
+// algorithm, and whether they run as one fused launch.
+struct BackwardCall {
+  fp8blk::GemmArgs gd, gw;
+  fp8blk::GemmAlgo al;
+  bool fused;
+};
+
+// Checks shared by the backward entry points: dgrad_op is FP8BLK_OP_DGRAD
+// (w = qwT [K][N]) or FP8BLK_OP_DGRAD_W (w = qw [N][K]).
+static int backward_prepare(int dgrad_op, int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy,
+                            const uint8_t* w, const float* sw, const uint8_t* qdyT, const float* sdyT,
+                            const uint8_t* qxT, const float* sxT, void* dx, int dx_dtype, void* dw, int dw_dtype,
+                            int scale_mode, BackwardCall* c) {
   if (!valid_scale_mode(scale_mode)) return FP8BLK_ERR_ARG;
   if (int rc = check_gemm_common(M, N, K, qdy, sdy, w, sw, dx, dx_dtype)) return rc;
   if (int rc = check_gemm_common(M, N, K, qdyT, sdyT, qxT, sxT, dw, dw_dtype)) return rc;
   if (dx == dw) return FP8BLK_ERR_ARG;
+  c->gd = make_args(dgrad_op, M, N, K, qdy, sdy, w, sw, dx, dx_dtype);
+  c->gw = make_args(FP8BLK_OP_WGRAD, M, N, K, qdyT, sdyT, qxT, sxT, dw, dw_dtype);
+  // amax / 448 scales: the promote algorithm, which reads the whole scales
+  c->al = scale_mode == FP8BLK_SCALE_FP32 ? fp8blk::GemmAlgo::Promote : kDefaultAlgo;
+  c->fused = c->al == fp8blk::GemmAlgo::ScaledMfma && fp8blk::gemm_mx_bwd_eligible(c->gd, c->gw);
+  return FP8BLK_OK;
+}
+
+// Workspace bytes the planned launches themselves use.
+static size_t backward_path_bytes(const BackwardCall& c) {
+  if (c.fused) return fp8blk::gemm_mx_bwd_workspace_bytes(c.gd.I, c.gd.R, c.gd.J);
+  const size_t d = fp8blk::gemm_path_workspace_bytes(c.gd, c.al), w = fp8blk::gemm_path_workspace_bytes(c.gw, c.al);
+  return d > w ? d : w;
+}
+
+static int backward_run(BackwardCall& c, void* workspace, hipStream_t stream) {
+  c.gd.ws = static_cast<float*>(workspace);
+  c.gw.ws = static_cast<float*>(workspace);
+  if (c.fused) return finish(fp8blk::launch_gemm_mx_bwd(c.gd, c.gw, stream));
+  // shapes the fused launch does not take, and amax / 448 scales: the two
+  // contractions in turn (on one stream, so they may share the workspace)
+  if (hipError_t e = fp8blk::launch_gemm(c.gd, c.al, stream)) return finish(e);
+  return finish(fp8blk::launch_gemm(c.gw, c.al, stream));
+}
+
+static int backward(int dgrad_op, int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy,
+                    const uint8_t* w, const float* sw, const uint8_t* qdyT, const float* sdyT, const uint8_t* qxT,
+                    const float* sxT, void* dx, int dx_dtype, void* dw, int dw_dtype, int scale_mode,
+                    void* workspace, size_t ws_bytes, hipStream_t stream) {
+  BackwardCall c;
+  if (int rc = backward_prepare(dgrad_op, M, N, K, qdy, sdy, w, sw, qdyT, sdyT, qxT, sxT, dx, dx_dtype, dw,
+                                dw_dtype, scale_mode, &c))
+    return rc;
+  // the documented size covers every path, whatever the operands' alignment
   const size_t need = backward_workspace_bytes(M, N, K);
   if (need > 0 && (workspace == nullptr || ws_bytes < need)) return FP8BLK_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return FP8BLK_ERR_ALIGN;
   if (int rc = check_device()) return rc;
-  fp8blk::GemmArgs gd = make_args(dgrad_op, M, N, K, qdy, sdy, w, sw, dx, dx_dtype);
-  fp8blk::GemmArgs gw = make_args(FP8BLK_OP_WGRAD, M, N, K, qdyT, sdyT, qxT, sxT, dw, dw_dtype);
-  gw.ws = static_cast<float*>(workspace);
-  // amax / 448 scales: the promote algorithm, which reads the whole scales
-  const fp8blk::GemmAlgo al = scale_mode == FP8BLK_SCALE_FP32 ? fp8blk::GemmAlgo::Promote : kDefaultAlgo;
-  if (al == fp8blk::GemmAlgo::ScaledMfma && fp8blk::gemm_mx_bwd_eligible(gd, gw))
-    return finish(fp8blk::launch_gemm_mx_bwd(gd, gw, stream));
-  // shapes the fused launch does not take, and amax / 448 scales: the two
-  // contractions in turn
-  if (hipError_t e = fp8blk::launch_gemm(gd, al, stream)) return finish(e);
-  return finish(fp8blk::launch_gemm(gw, al, stream));
+  return backward_run(c, workspace, stream);
 }
 
 int fp8_block_gemm_backward(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy,
@@ -268,6 +302,22 @@ int fp8_block_gemm_backward_w(int64_t M, int64_t N, int64_t K, const uint8_t* qd
                               int scale_mode, void* workspace, size_t ws_bytes, hipStream_t stream) {
   return backward(FP8BLK_OP_DGRAD_W, M, N, K, qdy, sdy, qw, sw, qdyT, sdyT, qxT, sxT, dx, dx_dtype, dw, dw_dtype,
                   scale_mode, workspace, ws_bytes, stream);
+}
+
+int fp8_block_gemm_backward_w_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, const float* sdy,
+                                      const uint8_t* qw, const float* sw, const uint8_t* qdyT, const float* sdyT,
+                                      const uint8_t* qxT, const float* sxT, void* dx, int dx_dtype, void* dw,
+                                      int dw_dtype, int scale_mode, hipStream_t stream) {
+  BackwardCall c;
+  if (int rc = backward_prepare(FP8BLK_OP_DGRAD_W, M, N, K, qdy, sdy, qw, sw, qdyT, sdyT, qxT, sxT, dx, dx_dtype, dw,
+                                dw_dtype, scale_mode, &c))
+    return rc;
+  if (backward_path_bytes(c) > FP8BLK_NOALLOC_SCRATCH_BYTES) return FP8BLK_ERR_SCRATCH;
+  if (int rc = check_device()) return rc;
+  void* scratch = nullptr;
+  size_t bytes = 0;
+  if (fp8blk::static_scratch(&scratch, &bytes) != hipSuccess) return FP8BLK_ERR_HIP;
+  return backward_run(c, scratch, stream);
 }
 
 int fp8_block_gemm_fprop(int64_t M, int64_t N, int64_t K, const uint8_t* qx, const float* sx, const uint8_t* qw,

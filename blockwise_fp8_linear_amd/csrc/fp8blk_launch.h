@@ -76,6 +76,14 @@ bool gemm_mx_eligible(const GemmArgs& g);
 size_t gemm_mx_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode);
 hipError_t launch_gemm_mx(const GemmArgs& g, hipStream_t stream);
 
+// Workspace bytes that launch_gemm(g, algo) itself uses (the general
+// kernel's split-K partials, or the 256x256 kernel's stream-K partial tiles).
+size_t gemm_path_workspace_bytes(const GemmArgs& g, GemmAlgo algo);
+
+// The library's static device scratch on the current device (scratch.hip):
+// its device address and size.
+hipError_t static_scratch(void** ptr, size_t* bytes);
+
 // Dgrad (gd: I = M, J = K, R = N, weight-block scales) and Wgrad (gw: I = N,
 // J = K, R = M, row scales) of one linear in one launch; the workspace is
 // gw.ws.

@@ -136,6 +136,12 @@ size_t gemm_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode) {
   return split_bytes > mx_bytes ? split_bytes : mx_bytes;
 }
 
+size_t gemm_path_workspace_bytes(const GemmArgs& g, GemmAlgo algo) {
+  if (algo == GemmAlgo::ScaledMfma && gemm_mx_eligible(g))
+    return g.bmode == BScale::Row ? sk_plan(g.I, g.J, g.R).bytes : 0;
+  return g.splits > 1 ? (size_t)g.splits * (size_t)g.I * (size_t)g.J * sizeof(float) : 0;
+}
+
 bool gemm_mx_bwd_eligible(const GemmArgs& gd, const GemmArgs& gw) {
   return gd.bmode == BScale::Block && gw.bmode == BScale::Row && gemm_mx_eligible(gd) && gemm_mx_eligible(gw) &&
          gd.I == gw.R && gd.R == gw.I && gd.J == gw.J;

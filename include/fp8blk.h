@@ -115,8 +115,13 @@ enum fp8blk_status {
     FP8BLK_ERR_ARG = -4,       /* bad enum, leading dimension smaller than the row, or too large */
     FP8BLK_ERR_WORKSPACE = -5, /* workspace smaller than fp8_block_gemm_workspace_size() */
     FP8BLK_ERR_HIP = -6,       /* the HIP runtime reported an error at launch */
-    FP8BLK_ERR_DEVICE = -7     /* the current device is not gfx950 */
+    FP8BLK_ERR_DEVICE = -7,    /* the current device is not gfx950 */
+    FP8BLK_ERR_SCRATCH = -8    /* the call needs more than FP8BLK_NOALLOC_SCRATCH_BYTES of scratch */
 };
+
+/* Size of the library's static device scratch buffer (one per GPU), used by
+ * fp8_block_gemm_backward_w_noalloc in place of a caller's workspace. */
+#define FP8BLK_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
 
 /*
  * Every quantizer takes scale_mode = FP8BLK_SCALE_POW2 or FP8BLK_SCALE_FP32
@@ -303,6 +308,37 @@ int fp8_block_gemm_backward_w(int64_t M, int64_t N, int64_t K,
                               const uint8_t *qxT, const float *sxT,
                               void *dx, int dx_dtype, void *dw, int dw_dtype, int scale_mode,
                               void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * fp8_block_gemm_backward_w for callers that cannot allocate memory or hand
+ * over a workspace: code being captured into a HIP graph, tight training or
+ * serving loops, harnesses that forbid allocation.  The same contraction,
+ * kernels and results, bit for bit, as fp8_block_gemm_backward_w with any
+ * sufficient workspace; the caller still passes every input and output.
+ * Where the other call would use the workspace (fp32 partial tiles of output
+ * tiles whose reduction several workgroups share), this one uses a static
+ * device array of FP8BLK_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library:
+ * each GPU the library runs on holds its own copy until the process ends.
+ * The call allocates nothing, neither through HIP nor otherwise; its first
+ * call on a device looks up that device's copy once.
+ *   Limit: a call whose launch needs more scratch than that returns
+ *     FP8BLK_ERR_SCRATCH before launching anything.  The fused launch of
+ *     power-of-two scales needs at most 32 MiB at the decoder layer's
+ *     shapes; the two-launch paths (amax / 448 scales, shapes the fused
+ *     launch does not take) can need more.
+ *   Concurrency: every call on a GPU shares that GPU's array and leaves its
+ *     contents behind (nothing in it needs to start at zero: each partial
+ *     tile is written in full before it is read).  Calls whose launches
+ *     overlap on one GPU -- on two streams, or from two threads -- race on
+ *     it and give wrong results: order them on one stream.
+ */
+int fp8_block_gemm_backward_w_noalloc(int64_t M, int64_t N, int64_t K,
+                                      const uint8_t *qdy, const float *sdy,
+                                      const uint8_t *qw, const float *sw,
+                                      const uint8_t *qdyT, const float *sdyT,
+                                      const uint8_t *qxT, const float *sxT,
+                                      void *dx, int dx_dtype, void *dw, int dw_dtype, int scale_mode,
+                                      hipStream_t stream);
 
 /*
  * All three contractions through one entry point, with an explicit algorithm.

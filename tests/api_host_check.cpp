@@ -85,6 +85,13 @@ hipError_t launch_gemm_mx_bwd(const GemmArgs& gd, const GemmArgs& gw, hipStream_
   g_log.push_back({"gemm_mx_bwd", gd, gw, -1, false, 0, 0, 0});
   return hipSuccess;
 }
+// a stand-in address for the static scratch (never dereferenced)
+alignas(256) static unsigned char g_fake_scratch[256];
+hipError_t static_scratch(void** ptr, size_t* bytes) {
+  *ptr = g_fake_scratch;
+  *bytes = FP8BLK_NOALLOC_SCRATCH_BYTES;
+  return hipSuccess;
+}
 }  // namespace fp8blk
 
 // ---------------------------------------------------------------- checks ---
@@ -246,9 +253,35 @@ static void gemm_checks() {
                 fp8_block_gemm_backward(M, N, K, a.p, sap, b.p, sbp, a.p, sap, b.p, sbp, dx.p, 0, dw.p, 1,
                                         FP8BLK_SCALE_POW2, bws.p, bneed - 16, nullptr),
                 FP8BLK_ERR_WORKSPACE, n);
+  // the no-allocation form: the same launches, the static scratch as workspace
+  n = g_log.size();
+  expect_status("noalloc pow2",
+                fp8_block_gemm_backward_w_noalloc(M, N, K, a.p, sap, b.p, sbp, a.p, sap, b.p, sbp, dx.p, 0, dw.p, 1,
+                                                  FP8BLK_SCALE_POW2, nullptr),
+                0, n);
+  CHECK(g_log.size() == n + 1 && g_log.back().kind == "gemm_mx_bwd" && g_log.back().g.bt &&
+            (void*)g_log.back().g2.ws == (void*)fp8blk::g_fake_scratch,
+        "noalloc: the fused launch on the static scratch");
+  n = g_log.size();
+  expect_status("noalloc fp32 too big",
+                fp8_block_gemm_backward_w_noalloc(M, N, 6144, a.p, sap, b.p, sbp, a.p, sap, b.p, sbp, dx.p, 0, dw.p,
+                                                  1, FP8BLK_SCALE_FP32, nullptr),
+                FP8BLK_ERR_SCRATCH, n);
+  expect_status("noalloc fp32",
+                fp8_block_gemm_backward_w_noalloc(M, N, K, a.p, sap, b.p, sbp, a.p, sap, b.p, sbp, dx.p, 0, dw.p, 1,
+                                                  FP8BLK_SCALE_FP32, nullptr),
+                0, n);
+  CHECK(g_log.size() == n + 2 && g_log[n].algo == (int)fp8blk::GemmAlgo::Promote && g_log[n].g.bt,
+        "noalloc fp32: the promote pair");
+  n = g_log.size();
+  expect_status("noalloc alias",
+                fp8_block_gemm_backward_w_noalloc(M, N, K, a.p, sap, b.p, sbp, a.p, sap, b.p, sbp, dw.p, 0, dw.p, 1,
+                                                  FP8BLK_SCALE_POW2, nullptr),
+                FP8BLK_ERR_ARG, n);
   CHECK(fp8_block_gemm_workspace_size(9, M, N, K) == (size_t)-1, "bad op");
   CHECK(fp8_block_gemm_workspace_size(FP8BLK_OP_FPROP, 100, N, K) == (size_t)-1, "bad shape");
   for (int st = 1; st >= -9; --st) CHECK(fp8_status_string(st) != nullptr, "status string");
+  CHECK(std::strstr(fp8_status_string(FP8BLK_ERR_SCRATCH), "scratch") != nullptr, "scratch status string");
 }
 
 // ---- slot tables: a host mirror of the kernels' walk (gemm_mx.hip).

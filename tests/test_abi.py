@@ -13,7 +13,7 @@ import blockwise_fp8_linear_amd as fb
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, ENULL, EDIM, EALIGN, EARG, EWS, EHIP, EDEV = 0, -1, -2, -3, -4, -5, -6, -7
+OK, ENULL, EDIM, EALIGN, EARG, EWS, EHIP, EDEV, ESCR = 0, -1, -2, -3, -4, -5, -6, -7, -8
 P = 0x100000          # a fake, 16-byte aligned device address (never used)
 P2 = 0x200000
 P3 = 0x300000
@@ -31,7 +31,7 @@ def test_exports_every_declared_function(lib):
         "fp8_quantize_rowgroup", "fp8_quantize_colgroup", "fp8_quantize_block", "fp8_quantize_dual",
         "fp8_quantize_block_batch",
         "fp8_block_gemm_fprop", "fp8_block_gemm_dgrad", "fp8_block_gemm_wgrad", "fp8_block_gemm_backward",
-        "fp8_block_gemm_dgrad_w", "fp8_block_gemm_backward_w",
+        "fp8_block_gemm_dgrad_w", "fp8_block_gemm_backward_w", "fp8_block_gemm_backward_w_noalloc",
         "fp8_block_gemm", "fp8_block_gemm_workspace_size", "fp8_status_string",
     }
     for n in names:
@@ -39,7 +39,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for rc in (OK, ENULL, EDIM, EALIGN, EARG, EWS, EHIP, EDEV):
+    for rc in (OK, ENULL, EDIM, EALIGN, EARG, EWS, EHIP, EDEV, ESCR):
         assert fb.fp8_status_string(rc)
     assert "unknown" in fb.fp8_status_string(-99)
 
@@ -229,6 +229,24 @@ def test_backward_scale_mode(lib, fn):
     assert f(*args(1)) in (EHIP, EDEV)                  # amax / 448: the promote algorithm
     for mode in (-1, 2):
         assert f(*args(mode)) == EARG
+
+
+def test_noalloc_backward_host_checks(lib):
+    """The no-allocation backward: argument errors as for the workspace form,
+    and a launch that would need more than the static scratch is refused
+    before anything runs (amax / 448 scales take the two-launch promote
+    path, whose split-K Wgrad partials for the down projection are 96 MiB)."""
+    f = lib.fp8_block_gemm_backward_w_noalloc
+    args = lambda M, N, K, mode, dx=0x800000, dw=0x900000: (M, N, K, P, P3, P2, P3, 0x400000, 0x500000, 0x600000,
+                                                            0x700000, dx, 0, dw, 1, mode, None)
+    assert f(*args(8192, 2048, 2048, 0)) in (EHIP, EDEV)       # fused launch, 32 MiB of slots: fits
+    assert f(*args(8192, 2048, 6144, 0)) in (EHIP, EDEV)
+    assert f(*args(8192, 2048, 6144, 1)) == ESCR               # needs 96 MiB > 64 MiB
+    assert f(*args(8192, 2048, 2048, 2)) == EARG
+    assert f(*args(8192, 2048, 2048, 0, dx=0x900000)) == EARG  # dx and dw alias
+    assert f(*args(8192, 200, 2048, 0)) == EDIM
+    assert f(*args(8192, 2048, 2048, 0, dx=None)) == ENULL
+    assert "scratch" in fb.fp8_status_string(ESCR)
 
 
 def test_workspace_query(lib):
