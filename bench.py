@@ -58,7 +58,7 @@ def kernel_of(kind, algo):
         return f"gemm_mx_bwd_kernel<{bt}> (+ bwd_fixup_kernel)"
     if kind == "gemm_wgrad":
         return ("gemm_mx_streamk_kernel<true> (+ sk_fixup_kernel)" if fast
-                else "gemm_kernel<promote, row scales> (+ splitk_reduce_kernel)")
+                else "gemm_sk_kernel<promote, row scales> (+ gk_fixup_kernel)")
     return kind + "_kernel"
 
 
@@ -351,8 +351,10 @@ def bf16_baseline(torch, linears, reps, steps=5):
 def onbox_ceilings(torch):
     """What this machine sustains, measured here: the GEMM kernels' MFMA work
     alone (libfp8probe: the same block-scaled 32x32x64 FP8 instruction, one
-    wave per SIMD, 16 accumulators, random codes, no memory traffic) and a
-    plain 1 GiB device-to-device copy (read + write bytes)."""
+    wave per SIMD, 16 accumulators, random codes, no memory traffic) and HBM
+    streaming (libfp8probe's copy and read kernels over 1 GiB: 16-byte
+    non-temporal accesses, eight in flight per lane; the copy counts read +
+    write bytes, the quantizers' 1:1 mix), besides torch's own copy."""
     import ctypes
     from blockwise_fp8_linear_amd.build import PROBE_LIB
     lib = ctypes.CDLL(PROBE_LIB)
@@ -386,11 +388,21 @@ def onbox_ceilings(torch):
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 256)
     dst = torch.empty_like(src)
-    t = timed(lambda: dst.copy_(src))
-    copy_gbs = 2 * n / t / 1e9
-    return {"mfma_fp8_TFLOP/s": round(mfma_tf, 1), "copy_GB/s": round(copy_gbs, 1),
-            "what": "best of 5: block-scaled FP8 MFMA loop (GEMM layout, random codes, no memory) "
-                    "and a 1 GiB device copy (read + write bytes)"}
+    lib.fp8probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                    ctypes.c_void_p]
+    lib.fp8probe_stream.restype = ctypes.c_int
+
+    def stream_probe(mode):
+        if lib.fp8probe_stream(mode, src.data_ptr(), dst.data_ptr(), n, 4096, stream) != 0:
+            raise RuntimeError("fp8probe_stream failed")
+    copy_gbs = 2 * n / timed(lambda: stream_probe(0)) / 1e9
+    read_gbs = n / timed(lambda: stream_probe(1)) / 1e9
+    torch_copy_gbs = 2 * n / timed(lambda: dst.copy_(src)) / 1e9
+    return {"mfma_fp8_TFLOP/s": round(mfma_tf, 1), "copy_GB/s": round(copy_gbs, 1), "read_GB/s": round(read_gbs, 1),
+            "torch_copy_GB/s": round(torch_copy_gbs, 1),
+            "what": "best of 5: block-scaled FP8 MFMA loop (GEMM layout, random codes, no memory); a streaming "
+                    "copy (read + write bytes) and a streaming read over 1 GiB (16-byte non-temporal accesses, "
+                    "8 in flight per lane, 4096 workgroups); torch's device copy of the same buffer"}
 
 
 def cpu_baseline(budget_s, mode=0):
@@ -522,9 +534,9 @@ def main():
         e = {"launches_per_step": a["launches"] // nb, "avg_ms": round(avg_ms, 5),
              "ms_per_step": round(a["ms"] / nb, 4)}
         if a["flops"]:
-            e["TFLOP/s"] = round(a["flops"] / (a["ms"] * 1e-3) / 1e12, 1)
+            e["TFLOP/s_incl_event_overhead"] = round(a["flops"] / (a["ms"] * 1e-3) / 1e12, 1)
         if a["bytes"]:
-            e["GB/s"] = round(a["bytes"] / (a["ms"] * 1e-3) / 1e9, 1)
+            e["GB/s_incl_event_overhead"] = round(a["bytes"] / (a["ms"] * 1e-3) / 1e9, 1)
         breakdown[kind] = e
     gemm_kinds = [k for k in agg if k.startswith("gemm")]
     gemm_ms = sum(agg[k]["ms"] for k in gemm_kinds)
@@ -623,8 +635,11 @@ def main():
         "gemm_only_TFLOP/s": round(gemm_flops_t / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
         "roofline": roof,
         "breakdown": breakdown,
-        "breakdown_note": "per-kind event times from 3 untimed steps with events around every launch "
-                          "(every 4th timed step carries events around the dominant kernel's launches only)",
+        "breakdown_note": "per-kind event times from 3 untimed steps with events around every launch; a "
+                          "pair of events adds a few microseconds to each launch (the first launch of a step "
+                          "can also include host enqueue time), so these per-kind rates understate the "
+                          "kernels, short ones most: the kernel traces in profiles/ give their durations. The "
+                          "roofline comes from the dominant kernel's own events in the timed steps",
         "sources_digest": sources_digest(),
     }
     if not args.no_ceilings:

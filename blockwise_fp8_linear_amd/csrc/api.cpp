@@ -183,7 +183,6 @@ static fp8blk::GemmArgs make_args(int op, int64_t M, int64_t N, int64_t K, const
     g.I = N; g.J = K; g.R = M;
     g.sb_j = 0; g.sb_r = 0; g.bmode = fp8blk::BScale::Row;
   }
-  g.splits = fp8blk::gemm_splits(g.I, g.J, g.R, g.bmode);
   return g;
 }
 

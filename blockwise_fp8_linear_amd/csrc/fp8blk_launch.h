@@ -47,8 +47,7 @@ struct GemmArgs {
   void* out;                // [I][J]
   bool out_f32;
   bool accumulate;          // fp32 output only: out += result
-  float* ws;                // split-K or stream-K workspace (may be null when none is needed)
-  int splits;
+  float* ws;                // stream-K workspace (may be null when none is needed)
   bool bt;                  // B stored [R][J] instead of [J][R] (Dgrad from the weight codes
                             // as quantized); weight-block scales only
 };
@@ -58,9 +57,7 @@ struct GemmArgs {
 // calls only repeat the same idempotent call).
 hipError_t ensure_lds_limit(const void* kernel, int bytes, std::atomic<uint64_t>* done);
 
-// Number of split-K slices the GEMM launcher uses at this shape and the
-// workspace bytes that needs.
-int gemm_splits(int64_t I, int64_t J, int64_t R, BScale bmode);
+// Workspace bytes that a contraction needs whichever kernel takes it.
 size_t gemm_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode);
 
 // Promote: MFMA from zero per 128-deep block, scale product applied on the
@@ -76,8 +73,8 @@ bool gemm_mx_eligible(const GemmArgs& g);
 size_t gemm_mx_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode);
 hipError_t launch_gemm_mx(const GemmArgs& g, hipStream_t stream);
 
-// Workspace bytes that launch_gemm(g, algo) itself uses (the general
-// kernel's split-K partials, or the 256x256 kernel's stream-K partial tiles).
+// Workspace bytes that launch_gemm(g, algo) itself uses (the stream-K
+// partial tiles of the general kernel or of the 256x256 kernel).
 size_t gemm_path_workspace_bytes(const GemmArgs& g, GemmAlgo algo);
 
 // The library's static device scratch on the current device (scratch.hip):

@@ -18,6 +18,8 @@ constexpr int64_t kMxTile = 256;
 // 128-blocks of a reduction whose weight-block scales those kernels hold in
 // LDS at once.
 constexpr int64_t kMxMaxKb = 128;
+// Output tile of the general kernel (gemm.hip).
+constexpr int64_t kGeneralTileI = 256, kGeneralTileJ = 128;
 
 // Range w of a grid of G over W units: [w W / G, (w + 1) W / G).
 inline int64_t h_start(int64_t w, int64_t W, int64_t G) { return w * W / G; }
@@ -34,14 +36,16 @@ inline int64_t h_owner(int64_t u, int64_t W, int64_t G) { return ((u + 1) * G - 
 // r's first segment (if partial) uses slot P(r), its last one (if partial
 // and not also the first) P(r) + f(r).
 
-// Wgrad alone on the persistent grid (gemm_mx_streamk_kernel): whole waves of
-// tiles run data-parallel, the rest stream-K over 512-deep units.
+// Wgrad alone on the persistent grid (gemm_mx_streamk_kernel, and the general
+// kernel's gemm_sk_kernel): whole waves of tiles run data-parallel, the rest
+// stream-K over 512-deep units.
 struct SkGeom {
   int64_t tiles_m, tiles_n;
   int64_t dp_tiles;  // tiles [0, dp_tiles) are data-parallel
   int64_t units;     // W: stream-K units (of the tiles from dp_tiles on)
   int64_t sk_grid;   // Gs = min(G, W): workgroups with stream-K work
   int64_t sk_tiles;  // T' when the ranges are permuted (see gemm_mx.hip), else 0
+  int64_t ublocks;   // 128-blocks per unit
   uint16_t slot[kSkGrid];
 };
 
@@ -52,7 +56,16 @@ struct SkPlan {
   size_t bytes;   // workspace bytes
 };
 
-SkPlan sk_plan(int64_t I, int64_t J, int64_t R);
+// Output tiles of tile_i x tile_j (the block-scaled-MFMA kernel's 256 x 256
+// by default; the general kernel's are 256 x 128), slots of that many fp32;
+// units of ublocks 128-blocks (4 by default: the reduction's block count
+// must then be a multiple of 4).
+SkPlan sk_plan(int64_t I, int64_t J, int64_t R, int64_t tile_i = kMxTile, int64_t tile_j = kMxTile,
+               int64_t ublocks = 4);
+
+// The general kernel's Wgrad plan: 256 x 128 tiles, units of four 128-blocks
+// when the reduction allows, else of one.
+SkPlan general_sk_plan(int64_t I, int64_t J, int64_t R);
 
 // Dgrad (problem 0: I = M, J = K, R = N, weight-block scales) and Wgrad
 // (problem 1: I = N, J = K, R = M, row scales) of one linear in one

@@ -40,6 +40,7 @@
 
 #include "fp8blk_device.h"
 #include "fp8blk_launch.h"
+#include "fp8blk_plan.h"
 
 namespace fp8blk {
 
@@ -130,10 +131,28 @@ __device__ __forceinline__ void mfma16_zero(v4f& p, const v8i& b, const v8i& a, 
   asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %2, %3, 0" : "=&v"(p), "+v"(prev) : "v"(b), "v"(a));
 }
 
+// Output tile t of a tiles_m x tiles_n grid -> its first row and column:
+// consecutive tiles walk down a group of GM tile rows before moving right,
+// so that tiles in flight together share operand panels in L2.
 template <class C>
-__global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t tiles_m, int64_t tiles_n,
-                                                          int64_t kb_per_split) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+__device__ __forceinline__ void gk_tile_origin(int64_t tile, int64_t tiles_m, int64_t tiles_n, int64_t& i0,
+                                               int64_t& j0) {
+  constexpr int64_t GM = 8;
+  const int64_t group = tile / (GM * tiles_n);
+  const int64_t first_m = group * GM;
+  const int64_t gsize = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+  const int64_t in_group = tile - group * GM * tiles_n;
+  i0 = (first_m + in_group % gsize) * C::BM;
+  j0 = (in_group / gsize) * C::BN;
+}
+
+// The contraction of the BM x BN output tile at (i0, j0) over the 128-blocks
+// [kb_begin, kb_end) into acc (zeroed first).  On return every direct load
+// has landed and every wave has passed the last barrier, so the LDS may be
+// refilled at once.
+template <class C>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* lds, int64_t i0, int64_t j0, int64_t kb_begin,
+                                          int64_t kb_end, v4f (&acc)[C::TM][C::TN]) {
   uint8_t* const tiles = lds;
   typedef typename C::SType ST;
   ST* const sa_lds = reinterpret_cast<ST*>(lds + 2 * C::STAGE);
@@ -145,23 +164,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
   const uint32_t wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const uint32_t l16 = lane & 15, g4 = lane >> 4;
 
-  // ---- which tile / split this workgroup owns
-  const int64_t ntiles = tiles_m * tiles_n;
-  const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t split = L / ntiles;
-  const int64_t tile = L - split * ntiles;
-  constexpr int64_t GM = 8;
-  const int64_t group = tile / (GM * tiles_n);
-  const int64_t first_m = group * GM;
-  const int64_t gsize = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
-  const int64_t in_group = tile - group * GM * tiles_n;
-  const int64_t tm = first_m + in_group % gsize;
-  const int64_t tn = in_group / gsize;
-  const int64_t i0 = tm * C::BM, j0 = tn * C::BN;
-
   const int64_t nkb = g.R / 128;
-  const int64_t kb_begin = split * kb_per_split;
-  const int64_t kb_end = (kb_begin + kb_per_split) < nkb ? (kb_begin + kb_per_split) : nkb;
   const int64_t R = g.R;
 
   // ---- direct global->LDS loads of one reduction block's tiles into stage
@@ -246,7 +249,6 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
     }
   };
 
-  v4f acc[C::TM][C::TN];
 #pragma unroll
   for (int a = 0; a < C::TM; ++a)
 #pragma unroll
@@ -391,23 +393,30 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
     wait_vmcnt<0>();  // this wave's loads of block kb+1 have landed
     __syncthreads();  // ... and every wave's; no wave reads stage cur any more
   }
+}
 
-  // ---- epilogue: lane holds out[i0+wm0+ms*16+l16][j0+wn0+ns*16+g4*4 .. +3]
+// Store a tile's accumulators: lane holds rows i0+wm0+ms*16+l16 and columns
+// j0+wn0+ns*16+g4*4 .. +3 of a row-major rows x cols matrix (row stride ld)
+// of fp32 (f32; acc: out += tile) or bf16 bits; rows and columns past the
+// edge are not stored.
+template <class C>
+__device__ __forceinline__ void gk_store(const v4f (&acc)[C::TM][C::TN], void* out, int64_t ld, int64_t rows,
+                                         int64_t cols, bool f32, bool accumulate, int64_t i0, int64_t j0) {
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t wm0 = (wave / C::WAVES_N) * C::WM, wn0 = (wave % C::WAVES_N) * C::WN;
+  const uint32_t l16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
   for (int ms = 0; ms < C::TM; ++ms) {
     const int64_t i = i0 + wm0 + ms * 16 + l16;
-    if (i >= g.I) continue;
+    if (i >= rows) continue;
 #pragma unroll
     for (int ns = 0; ns < C::TN; ++ns) {
       const int64_t j = j0 + wn0 + ns * 16 + g4 * 4;
-      if (j >= g.J) continue;
+      if (j >= cols) continue;
       const v4f v = acc[ms][ns];
-      if (g.splits > 1) {
-        float* dst = g.ws + split * g.I * g.J + i * g.J + j;
-        *reinterpret_cast<v4f*>(dst) = v;
-      } else if (g.out_f32) {
-        v4f* const dst = reinterpret_cast<v4f*>(static_cast<float*>(g.out) + i * g.J + j);
-        if (g.accumulate) {
+      if (f32) {
+        v4f* const dst = reinterpret_cast<v4f*>(static_cast<float*>(out) + i * ld + j);
+        if (accumulate) {
           const v4f o = *dst;
           *dst = v4f{o[0] + v[0], o[1] + v[1], o[2] + v[2], o[3] + v[3]};
         } else {
@@ -417,34 +426,119 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t ti
         uint2 o;
         o.x = bf16x2_rne(v[0], v[1]);
         o.y = bf16x2_rne(v[2], v[3]);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + i * g.J + j) = o;
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + i * ld + j) = o;
       }
     }
   }
 }
 
-// Deterministic split-K reduction: out[idx] = sum over s in order of ws[s][idx] (added to
-// out[idx] when accumulating).
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int splits, int64_t n4,
-                                                            void* out, bool out_f32, bool accumulate) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < n4; v += stride) {
-    v4f s = reinterpret_cast<const v4f*>(ws)[v];
-    for (int k = 1; k < splits; ++k) {
-      const v4f t = reinterpret_cast<const v4f*>(ws + (int64_t)k * n4 * 4)[v];
-      s[0] += t[0]; s[1] += t[1]; s[2] += t[2]; s[3] += t[3];
+// One output tile per workgroup, the whole reduction (Fprop and Dgrad).
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmArgs g, int64_t tiles_m, int64_t tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  int64_t i0, j0;
+  gk_tile_origin<C>(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, i0, j0);
+  v4f acc[C::TM][C::TN];
+  gemm_tile<C>(g, lds, i0, j0, 0, g.R / 128, acc);
+  gk_store<C>(acc, g.out, g.J, g.I, g.J, g.out_f32, g.accumulate, i0, j0);
+}
+
+// Wgrad (long reduction over tokens, few output tiles) on a persistent grid,
+// partitioned as in the block-scaled-MFMA kernel's Wgrad (gemm_mx.hip, see
+// fp8blk_plan.h): whole waves of tiles data-parallel, the rest stream-K over
+// 512-deep units; a piece of a tile shared by several workgroups goes, in
+// fp32, to its own slot of the workspace, and gk_fixup_kernel adds the
+// pieces of every shared tile in reduction order (deterministic).  No
+// workgroup waits for another.
+__device__ __forceinline__ int64_t gk_start(int64_t w, int64_t W, int64_t G) { return w * W / G; }
+__device__ __forceinline__ int64_t gk_owner(int64_t u, int64_t W, int64_t G) { return ((u + 1) * G - 1) / W; }
+__device__ __forceinline__ int64_t gk_slot(const uint16_t* table, int64_t r, bool first) {
+  const uint32_t e = table[r];
+  return (int64_t)(e >> 1) + (first ? 0 : (int64_t)(e & 1));
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void gemm_sk_kernel(GemmArgs g, SkGeom sg, float* partials) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int64_t G = gridDim.x;
+  const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t UB = sg.ublocks, U = g.R / (128 * UB);  // 128-blocks per unit, units per tile
+  v4f acc[C::TM][C::TN];
+  for (int64_t t = w; t < sg.dp_tiles; t += G) {
+    int64_t i0, j0;
+    gk_tile_origin<C>(t, sg.tiles_m, sg.tiles_n, i0, j0);
+    gemm_tile<C>(g, lds, i0, j0, 0, U * UB, acc);
+    gk_store<C>(acc, g.out, g.J, g.I, g.J, g.out_f32, g.accumulate, i0, j0);
+  }
+  const int64_t W = sg.units, Gs = sg.sk_grid;
+  const int64_t r = sg.sk_tiles > 0 ? (w % sg.sk_tiles) * (Gs / sg.sk_tiles) + w / sg.sk_tiles : w;
+  const int64_t ubeg = w < Gs ? gk_start(r, W, Gs) : 0, uend = w < Gs ? gk_start(r + 1, W, Gs) : 0;
+  for (int64_t u = ubeg; u < uend;) {
+    const int64_t ts = u / U;
+    const int64_t lo = u - ts * U;
+    const int64_t hi = (uend - ts * U) < U ? (uend - ts * U) : U;
+    int64_t i0, j0;
+    gk_tile_origin<C>(sg.dp_tiles + ts, sg.tiles_m, sg.tiles_n, i0, j0);
+    gemm_tile<C>(g, lds, i0, j0, lo * UB, hi * UB, acc);
+    if (lo == 0 && hi == U) {
+      gk_store<C>(acc, g.out, g.J, g.I, g.J, g.out_f32, g.accumulate, i0, j0);
+    } else {
+      float* const slot = partials + gk_slot(sg.slot, r, u == ubeg) * (int64_t)(C::BM * C::BN);
+      gk_store<C>(acc, slot, C::BN, C::BM, C::BN, true, false, 0, 0);
     }
-    if (out_f32) {
-      if (accumulate) {
-        const v4f o = reinterpret_cast<const v4f*>(out)[v];
-        s = v4f{o[0] + s[0], o[1] + s[1], o[2] + s[2], o[3] + s[3]};
+    u = ts * U + hi;
+  }
+}
+
+// The shared tiles of gemm_sk_kernel: block (ts, rr) sums rows
+// 16 rr .. 16 rr + 15 of stream-K tile ts over its pieces in reduction order
+// (piece 0: the last segment of range f, the tile's first, if f started in an
+// earlier tile, else f's first segment; piece k >= 1: the first segment of
+// range f + k) and stores them.
+template <class C>
+__global__ __launch_bounds__(256) void gk_fixup_kernel(GemmArgs g, SkGeom sg, const float* __restrict__ partials) {
+  constexpr int ROWS = 16, PER = ROWS * C::BN / 4 / 256;  // float4 per thread
+  static_assert(PER >= 1 && ROWS * C::BN == PER * 4 * 256, "whole float4s per thread");
+  const int64_t ts = blockIdx.x / (C::BM / ROWS);
+  const int64_t r0 = (blockIdx.x % (C::BM / ROWS)) * ROWS;
+  const int64_t U = g.R / (128 * sg.ublocks), W = sg.units, G = sg.sk_grid;
+  const int64_t f = gk_owner(ts * U, W, G);
+  const int pieces = (int)(gk_owner(ts * U + U - 1, W, G) - f + 1);
+  if (pieces == 1) return;  // stored by the GEMM itself
+  const int64_t first_slot = gk_slot(sg.slot, f, !(gk_start(f, W, G) < ts * U));
+  int64_t i0, j0;
+  gk_tile_origin<C>(sg.dp_tiles + ts, sg.tiles_m, sg.tiles_n, i0, j0);
+  v4f sum[PER];
+  for (int pc = 0; pc < pieces; ++pc) {
+    const int64_t slot = pc == 0 ? first_slot : gk_slot(sg.slot, f + pc, true);
+    const v4f* src = reinterpret_cast<const v4f*>(partials + slot * (int64_t)(C::BM * C::BN) + r0 * C::BN);
+    v4f v[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) v[k] = __builtin_nontemporal_load(src + threadIdx.x + 256 * k);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      if (pc == 0) sum[k] = v[k];
+      else sum[k] = v4f{sum[k][0] + v[k][0], sum[k][1] + v[k][1], sum[k][2] + v[k][2], sum[k][3] + v[k][3]};
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    const int64_t i = i0 + r0 + idx / (C::BN / 4), j = j0 + (idx % (C::BN / 4)) * 4;
+    if (i >= g.I || j >= g.J) continue;
+    if (g.out_f32) {
+      v4f* const dst = reinterpret_cast<v4f*>(static_cast<float*>(g.out) + i * g.J + j);
+      if (g.accumulate) {
+        const v4f o = *dst;
+        *dst = v4f{o[0] + sum[k][0], o[1] + sum[k][1], o[2] + sum[k][2], o[3] + sum[k][3]};
+      } else {
+        *dst = sum[k];
       }
-      reinterpret_cast<v4f*>(out)[v] = s;
     } else {
       uint2 o;
-      o.x = bf16x2_rne(s[0], s[1]);
-      o.y = bf16x2_rne(s[2], s[3]);
-      reinterpret_cast<uint2*>(out)[v] = o;
+      o.x = bf16x2_rne(sum[k][0], sum[k][1]);
+      o.y = bf16x2_rne(sum[k][2], sum[k][3]);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + i * g.J + j) = o;
     }
   }
 }
@@ -472,38 +566,39 @@ template <class C>
 static hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
   const int64_t tiles_m = (g.I + C::BM - 1) / C::BM;
   const int64_t tiles_n = (g.J + C::BN - 1) / C::BN;
-  const int64_t nkb = g.R / 128;
-  const int splits = g.splits > 0 ? g.splits : 1;
-  const int64_t kb_per_split = (nkb + splits - 1) / splits;
-  const int64_t blocks = tiles_m * tiles_n * splits;
   static std::atomic<uint64_t> attr_set{0};
   if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(&gemm_kernel<C>), C::LDS, &attr_set)) return e;
-  hipLaunchKernelGGL(gemm_kernel<C>, dim3((uint32_t)blocks), dim3(C::THREADS), C::LDS, stream, g, tiles_m, tiles_n,
-                     kb_per_split);
+  hipLaunchKernelGGL(gemm_kernel<C>, dim3((uint32_t)(tiles_m * tiles_n)), dim3(C::THREADS), C::LDS, stream, g, tiles_m,
+                     tiles_n);
   return hipGetLastError();
 }
 
-static hipError_t launch_splitk_reduce(const GemmArgs& g, hipStream_t stream) {
-  const int64_t n4 = g.I * g.J / 4;
-  int64_t rblocks = (n4 + 255) / 256;
-  if (rblocks > 4096) rblocks = 4096;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)rblocks), dim3(256), 0, stream, g.ws, g.splits, n4, g.out,
-                     g.out_f32, g.accumulate);
+// Wgrad on the general kernel: the persistent stream-K launch, then the
+// fix-up of shared tiles if there are any.
+template <class C>
+static hipError_t launch_cfg_sk(const GemmArgs& g, hipStream_t stream) {
+  const SkPlan p = general_sk_plan(g.I, g.J, g.R);
+  static_assert(C::BM == kGeneralTileI && C::BN == kGeneralTileJ, "the plan's tile shape");
+  static std::atomic<uint64_t> attr_set{0};
+  if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(&gemm_sk_kernel<C>), C::LDS, &attr_set)) return e;
+  float* const partials = p.slots > 0 ? g.ws : nullptr;
+  hipLaunchKernelGGL(gemm_sk_kernel<C>, dim3((uint32_t)p.grid), dim3(C::THREADS), C::LDS, stream, g, p.geom,
+                     partials);
+  if (hipError_t e = hipGetLastError()) return e;
+  if (p.slots == 0) return hipSuccess;
+  const int64_t sk_tiles = p.geom.tiles_m * p.geom.tiles_n - p.geom.dp_tiles;
+  hipLaunchKernelGGL(gk_fixup_kernel<C>, dim3((uint32_t)(sk_tiles * (C::BM / 16))), dim3(256), 0, stream, g, p.geom,
+                     partials);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs& g, GemmAlgo algo, hipStream_t stream) {
-  // the 256x256 kernel needs no split-K reduction (Wgrad runs stream-K)
   if (algo == GemmAlgo::ScaledMfma && gemm_mx_eligible(g)) return launch_gemm_mx(g, stream);
-  hipError_t e;
   if (g.bt)
-    e = algo == GemmAlgo::Promote ? launch_cfg<PromoteBlockBT>(g, stream) : launch_cfg<ScaledBlockBT>(g, stream);
-  else if (algo == GemmAlgo::Promote)
-    e = g.bmode == BScale::Row ? launch_cfg<PromoteRow>(g, stream) : launch_cfg<PromoteBlock>(g, stream);
-  else
-    e = g.bmode == BScale::Row ? launch_cfg<ScaledRow>(g, stream) : launch_cfg<ScaledBlock>(g, stream);
-  if (e != hipSuccess || g.splits <= 1) return e;
-  return launch_splitk_reduce(g, stream);
+    return algo == GemmAlgo::Promote ? launch_cfg<PromoteBlockBT>(g, stream) : launch_cfg<ScaledBlockBT>(g, stream);
+  if (g.bmode == BScale::Row)
+    return algo == GemmAlgo::Promote ? launch_cfg_sk<PromoteRow>(g, stream) : launch_cfg_sk<ScaledRow>(g, stream);
+  return algo == GemmAlgo::Promote ? launch_cfg<PromoteBlock>(g, stream) : launch_cfg<ScaledBlock>(g, stream);
 }
 
 }  // namespace fp8blk

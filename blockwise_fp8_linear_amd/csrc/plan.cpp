@@ -11,7 +11,6 @@ namespace fp8blk {
 
 namespace {
 
-constexpr int64_t kCUs = 256;
 constexpr size_t kSlotBytes = size_t(kMxTile) * kMxTile * sizeof(float);
 
 // Walk range r's segments the way the kernels do -- over units [ubeg, uend)
@@ -55,11 +54,12 @@ int64_t slot_table(uint16_t* slot, int64_t G, int64_t W, int64_t w0, int64_t u0,
 
 }  // namespace
 
-SkPlan sk_plan(int64_t I, int64_t J, int64_t R) {
+SkPlan sk_plan(int64_t I, int64_t J, int64_t R, int64_t tile_i, int64_t tile_j, int64_t ublocks) {
   SkPlan p{};
-  p.geom.tiles_m = (I + kMxTile - 1) / kMxTile;
-  p.geom.tiles_n = (J + kMxTile - 1) / kMxTile;
-  const int64_t T = p.geom.tiles_m * p.geom.tiles_n, U = R / 512;
+  p.geom.tiles_m = (I + tile_i - 1) / tile_i;
+  p.geom.tiles_n = (J + tile_j - 1) / tile_j;
+  p.geom.ublocks = ublocks;
+  const int64_t T = p.geom.tiles_m * p.geom.tiles_n, U = R / (128 * ublocks);
   p.grid = T * U < kSkGrid ? T * U : kSkGrid;
   p.geom.dp_tiles = (T / p.grid) * p.grid;
   const int64_t W = (T - p.geom.dp_tiles) * U;
@@ -68,7 +68,7 @@ SkPlan sk_plan(int64_t I, int64_t J, int64_t R) {
   p.geom.sk_grid = Gs;
   p.geom.sk_tiles = (W > 0 && W % Gs == 0 && U % (W / Gs) == 0) ? T - p.geom.dp_tiles : 0;
   p.slots = W > 0 ? slot_table(p.geom.slot, Gs, W, W, U, U) : 0;
-  p.bytes = (size_t)p.slots * kSlotBytes;
+  p.bytes = (size_t)p.slots * (size_t)(tile_i * tile_j) * sizeof(float);
   return p;
 }
 
@@ -98,16 +98,6 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
-int gemm_splits(int64_t I, int64_t J, int64_t R, BScale bmode) {
-  if (bmode == BScale::Block) return 1;
-  const int64_t tiles = ((I + 255) / 256) * ((J + 255) / 256);
-  const int64_t nkb = R / 128;
-  int s = 1;
-  // split the reduction until the grid covers the CUs, keeping >= 8 blocks per slice
-  while (tiles * s < kCUs && nkb / (2 * s) >= 8) s *= 2;
-  return s;
-}
-
 bool gemm_mx_eligible(const GemmArgs& g) {
   const int64_t nkb = g.R / 128;
   if (nkb % 4 != 0) return false;
@@ -127,19 +117,27 @@ size_t gemm_mx_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode) {
   return sk_plan(I, J, R).bytes;
 }
 
+SkPlan general_sk_plan(int64_t I, int64_t J, int64_t R) {
+  return sk_plan(I, J, R, kGeneralTileI, kGeneralTileJ, (R / 128) % 4 == 0 ? 4 : 1);
+}
+
+// The general kernel's Wgrad (row scales) runs stream-K on 256 x 128 tiles.
+static size_t general_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode) {
+  return bmode == BScale::Row ? general_sk_plan(I, J, R).bytes : 0;
+}
+
 size_t gemm_workspace_bytes(int64_t I, int64_t J, int64_t R, BScale bmode) {
-  // enough for either path: split-K partials of the general kernel, or the
-  // stream-K partial tiles of the block-scaled-MFMA kernel
-  const int s = gemm_splits(I, J, R, bmode);
-  const size_t split_bytes = s > 1 ? (size_t)s * (size_t)I * (size_t)J * sizeof(float) : 0;
-  const size_t mx_bytes = gemm_mx_workspace_bytes(I, J, R, bmode);
-  return split_bytes > mx_bytes ? split_bytes : mx_bytes;
+  // enough for either path: the stream-K partial tiles of the general kernel
+  // or of the block-scaled-MFMA kernel
+  const size_t gen = general_workspace_bytes(I, J, R, bmode);
+  const size_t mx = gemm_mx_workspace_bytes(I, J, R, bmode);
+  return gen > mx ? gen : mx;
 }
 
 size_t gemm_path_workspace_bytes(const GemmArgs& g, GemmAlgo algo) {
   if (algo == GemmAlgo::ScaledMfma && gemm_mx_eligible(g))
     return g.bmode == BScale::Row ? sk_plan(g.I, g.J, g.R).bytes : 0;
-  return g.splits > 1 ? (size_t)g.splits * (size_t)g.I * (size_t)g.J * sizeof(float) : 0;
+  return general_workspace_bytes(g.I, g.J, g.R, g.bmode);
 }
 
 bool gemm_mx_bwd_eligible(const GemmArgs& gd, const GemmArgs& gw) {

@@ -82,7 +82,68 @@ __global__ __launch_bounds__(256) void quotient_check_kernel(uint32_t* counts) {
   if (threadIdx.x == 0) counts[blockIdx.y * gridDim.x + blockIdx.x] = (uint32_t)n;
 }
 
+// On-box HBM ceiling: streaming kernels over one buffer, each lane moving
+// kStreamUnroll 16-byte pieces per step (all loads issued before the first
+// store or use), non-temporal loads and stores, a grid-stride loop over
+// 16-byte pieces.  copy: read src, write dst (as many bytes written as read,
+// the quantizers' ratio); read: read src only, folded into one word per
+// thread so that the loads are kept.
+constexpr int kStreamUnroll = 8;
+
+__global__ __launch_bounds__(256) void copy_probe_kernel(const fp8blk::u32x4* __restrict__ src,
+                                                         fp8blk::u32x4* __restrict__ dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i0 = (int64_t)blockIdx.x * 256 * kStreamUnroll + threadIdx.x; i0 < n16;
+       i0 += stride * kStreamUnroll) {
+    fp8blk::u32x4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const int64_t i = i0 + (int64_t)u * 256;
+      if (i < n16) v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const int64_t i = i0 + (int64_t)u * 256;
+      if (i < n16) __builtin_nontemporal_store(v[u], dst + i);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void read_probe_kernel(const fp8blk::u32x4* __restrict__ src, int64_t n16,
+                                                         uint32_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  uint32_t acc = 0;
+  for (int64_t i0 = (int64_t)blockIdx.x * 256 * kStreamUnroll + threadIdx.x; i0 < n16;
+       i0 += stride * kStreamUnroll) {
+    fp8blk::u32x4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const int64_t i = i0 + (int64_t)u * 256;
+      v[u] = i < n16 ? __builtin_nontemporal_load(src + i) : fp8blk::u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 }  // namespace
+
+extern "C" int fp8probe_stream(int mode, const void* src, void* dst, size_t bytes, int workgroups,
+                               hipStream_t stream) {
+  if (src == nullptr || dst == nullptr || bytes == 0 || bytes % 16 != 0 || workgroups <= 0 || (mode != 0 && mode != 1))
+    return -1;
+  if (((uintptr_t)src & 15) != 0 || ((uintptr_t)dst & 15) != 0) return -1;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  const auto* s = static_cast<const fp8blk::u32x4*>(src);
+  if (mode == 0)
+    hipLaunchKernelGGL(copy_probe_kernel, dim3((uint32_t)workgroups), dim3(256), 0, stream, s,
+                       static_cast<fp8blk::u32x4*>(dst), n16);
+  else
+    hipLaunchKernelGGL(read_probe_kernel, dim3((uint32_t)workgroups), dim3(256), 0, stream, s, n16,
+                       static_cast<uint32_t*>(dst));
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
 
 extern "C" int fp8probe_fp32_quotient_check(uint32_t* counts, hipStream_t stream) {
   if (counts == nullptr) return -1;

@@ -1,8 +1,9 @@
 /*
  * fp8probe.h -- measurement probe shipped beside libfp8blk (libfp8probe.so).
- * Not part of the hot path: the benchmark uses it to state an on-box ceiling
- * for the block-scaled FP8 matrix-core work of the GEMM kernels, and a test
- * uses it to check the amax / 448 quantizers' quotient exhaustively.
+ * Not part of the hot path: the benchmark uses it to state on-box ceilings
+ * for the block-scaled FP8 matrix-core work of the GEMM kernels and for the
+ * HBM streaming of the quantizers, and a test uses it to check the
+ * amax / 448 quantizers' quotient exhaustively.
  */
 #ifndef FP8PROBE_H
 #define FP8PROBE_H
@@ -26,6 +27,17 @@ int fp8probe_mfma(int workgroups, int iters, uint32_t seed, float *out, hipStrea
 
 /* The FLOP count of one fp8probe_mfma call (2 per multiply-add). */
 double fp8probe_mfma_flops(int workgroups, int iters);
+
+/*
+ * On-box HBM ceiling: a streaming kernel over `bytes` (a multiple of 16;
+ * src and dst 16-byte aligned) on `workgroups` workgroups of 256 threads,
+ * each lane moving 8 16-byte pieces per step with non-temporal loads and
+ * stores.  mode 0: copy src to dst (bytes read = bytes written, the
+ * quantizers' ratio); mode 1: read src only, dst receiving one word per
+ * thread (workgroups * 256 uint32) so that the loads are kept.
+ * Returns 0, -1 for bad arguments, -6 if the launch failed.
+ */
+int fp8probe_stream(int mode, const void *src, void *dst, size_t bytes, int workgroups, hipStream_t stream);
 
 /*
  * Check, on the device, the quantizers' quotient under FP8BLK_SCALE_FP32

@@ -263,9 +263,9 @@ static void gemm_checks() {
             (void*)g_log.back().g2.ws == (void*)fp8blk::g_fake_scratch,
         "noalloc: the fused launch on the static scratch");
   n = g_log.size();
-  expect_status("noalloc fp32 too big",
-                fp8_block_gemm_backward_w_noalloc(M, N, 6144, a.p, sap, b.p, sbp, a.p, sap, b.p, sbp, dx.p, 0, dw.p,
-                                                  1, FP8BLK_SCALE_FP32, nullptr),
+  expect_status("noalloc too big",
+                fp8_block_gemm_backward_w_noalloc(1024, 2560, 3840, a.p, sap, b.p, sbp, a.p, sap, b.p, sbp, dx.p, 0,
+                                                  dw.p, 1, FP8BLK_SCALE_POW2, nullptr),
                 FP8BLK_ERR_SCRATCH, n);
   expect_status("noalloc fp32",
                 fp8_block_gemm_backward_w_noalloc(M, N, K, a.p, sap, b.p, sbp, a.p, sap, b.p, sbp, dx.p, 0, dw.p, 1,
@@ -342,7 +342,8 @@ static void plan_checks() {
   const int64_t shapes[][3] = {{8192, 4096, 2048}, {8192, 2048, 2048}, {8192, 12288, 2048}, {8192, 2048, 6144},
                                {1024, 1536, 1024}, {2048, 1536, 1152}, {512, 1024, 640},   {1024, 512, 384},
                                {9216, 1152, 768},  {2048, 256, 256},   {1024, 4096, 6144}, {512, 5120, 7680},
-                               {2048, 4352, 4096}, {4608, 2560, 1408}, {2560, 6656, 896},  {512, 512, 128}};
+                               {2048, 4352, 4096}, {4608, 2560, 1408}, {2560, 6656, 896},  {512, 512, 128},
+                               {384, 640, 512},    {640, 384, 1024},   {1024, 2560, 3840}, {128, 384, 256}};
   for (const auto& sh : shapes) {
     const int64_t M = sh[0], N = sh[1], K = sh[2];
     char what[96];
@@ -351,6 +352,18 @@ static void plan_checks() {
       std::snprintf(what, sizeof what, "backward %lldx%lldx%lld", (long long)M, (long long)N, (long long)K);
       check_slots(what, p.geom.slot, p.slots, p.grid, p.geom.units, p.geom.w0, p.geom.u0, p.geom.u1);
       CHECK(p.bytes == (size_t)p.slots * 256 * 256 * 4, "%s: bytes", what);
+    }
+    {  // the general kernel's Wgrad: 256 x 128 tiles, units of 4 or 1 blocks
+      const fp8blk::SkPlan p = fp8blk::general_sk_plan(N, K, M);
+      std::snprintf(what, sizeof what, "general wgrad %lldx%lldx%lld", (long long)M, (long long)N, (long long)K);
+      const int64_t U = M / (128 * p.geom.ublocks);
+      CHECK(p.geom.ublocks == ((M / 128) % 4 == 0 ? 4 : 1), "%s: unit size", what);
+      if (p.geom.units > 0)
+        check_slots(what, p.geom.slot, p.slots, p.geom.sk_grid, p.geom.units, p.geom.units, U, U);
+      else
+        CHECK(p.slots == 0, "%s: no stream-K units, no slots", what);
+      CHECK(p.bytes == (size_t)p.slots * 256 * 128 * 4, "%s: bytes", what);
+      CHECK(p.slots <= 2 * fp8blk::kSkGrid, "%s: at most two partial segments per range", what);
     }
     if ((M / 128) % 4 == 0) {
       const fp8blk::SkPlan p = fp8blk::sk_plan(N, K, M);  // Wgrad: I = N, J = K, R = M

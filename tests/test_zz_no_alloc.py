@@ -5,8 +5,8 @@ agree with the oracle within the GEMM tolerance on sampled rows.  The calls
 run back to back, each leaving its partial tiles in the shared scratch for
 the next: a large shape, then a smaller one, then one whose partial tiles
 take nearly all of the scratch; amax / 448 scales (the promote pair, whose
-split-K partials fill the scratch exactly); and a launch that would need
-more than the scratch, refused before anything runs."""
+Wgrad's stream-K partial tiles go to the scratch); and a launch that would
+need more than the scratch, refused before anything runs."""
 import numpy as np
 import pytest
 
@@ -77,24 +77,27 @@ def test_noalloc_backward_calls_in_a_row():
     # 240 partial tiles: 60 of the 64 MiB
     _one_call(2048, 1536, 1152, (90, 2))
     # amax / 448 scales: Dgrad then Wgrad with the promote algorithm, the
-    # Wgrad's split-K partials filling the 64 MiB exactly
+    # Wgrad's 256 partial 256x128 tiles taking 32 MiB
     _one_call(8192, 2048, 2048, (90, 3), mode=fb.FP8BLK_SCALE_FP32, oracle_rows=True)
     _one_call(1024, 1536, 1024, (90, 4))
 
 
 def test_noalloc_refuses_more_than_its_scratch():
     import torch
-    M, N, K = 8192, 2048, 6144          # amax / 448 scales: 96 MiB of split-K partials
-    ops, _ = _operands(M, N, K, (91, 0), fb.FP8BLK_SCALE_FP32)
+    M, N, K = 1024, 2560, 3840          # the fused launch: 288 partial 256x256 tiles, 72 MiB
+    ops, _ = _operands(M, N, K, (91, 0), fb.FP8BLK_SCALE_POW2)
     dx, dw = _filled((M, K), torch.bfloat16), _filled((N, K), torch.bfloat16)
     torch.cuda.synchronize()
     with pytest.raises(RuntimeError, match="scratch"):
-        fb.fp8_block_gemm_backward_w_noalloc(*ops, dx, dw, scale_mode=fb.FP8BLK_SCALE_FP32)
+        fb.fp8_block_gemm_backward_w_noalloc(*ops, dx, dw)
     torch.cuda.synchronize()
     assert bool((dx.view(torch.int16) == -1).all()) and bool((dw.view(torch.int16) == -1).all()), \
         "a refused call wrote its outputs"
-    # power-of-two scales at the same shape: the fused launch, 32 MiB
+    # the workspace form takes it; the down projection's shape fits the scratch
+    rdx, rdw = fb.fp8_block_gemm_backward_w(*ops)
+    M, N, K = 8192, 2048, 6144
     ops, _ = _operands(M, N, K, (91, 1), fb.FP8BLK_SCALE_POW2)
+    dx, dw = _filled((M, K), torch.bfloat16), _filled((N, K), torch.bfloat16)
     fb.fp8_block_gemm_backward_w_noalloc(*ops, dx, dw)
     rdx, rdw = fb.fp8_block_gemm_backward_w(*ops)
     torch.cuda.synchronize()
