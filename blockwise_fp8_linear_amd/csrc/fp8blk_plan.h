@@ -69,15 +69,23 @@ SkPlan general_sk_plan(int64_t I, int64_t J, int64_t R);
 
 // Dgrad (problem 0: I = M, J = K, R = N, weight-block scales) and Wgrad
 // (problem 1: I = N, J = K, R = M, row scales) of one linear in one
-// persistent launch (gemm_mx_bwd_kernel).
+// persistent launch (gemm_mx_bwd_kernel).  Both problems' tiles are cut into
+// 512-deep units, problem 0's first; range r (one per workgroup) covers
+// units [rstart[r], rstart[r+1]).  The host picks the ranges per shape
+// (plan.cpp): one even cut of all units, or problem 0 on the first G0 ranges
+// and problem 1 on the rest, each cut evenly in whole tiles or in units.
 struct BwdGeom {
   int64_t tm0, tn0, u0, t0;  // problem 0: tile grid, units per tile, tiles
   int64_t tm1, tn1, u1;      // problem 1
   int64_t w0;                // units of problem 0
   int64_t units;             // W, all units
-  // k0, k1: when a problem's tiles fall whole into ranges, k of them per
-  // range (else 0); the ranges' tiles are then dealt out round-robin.
-  int64_t k0, k1;
+  // dealing: when problem p's tiles lie in ranges [rp0[p], rp0[p] + rpn[p])
+  // alone and each of them holds whole tiles, deal[p] = 1 and the j-th tile
+  // of the problem's i-th range is tile j * rpn[p] + i, so that the ranges
+  // running side by side work on neighbouring tiles and share operand panels
+  // in L2 (such tiles never reach the fix-up).
+  int64_t rp0[2], rpn[2], deal[2];
+  uint32_t rstart[kSkGrid + 1];
   uint16_t slot[kSkGrid];
 };
 
@@ -87,6 +95,18 @@ struct BwdPlan {
   int64_t slots;
   size_t bytes;
 };
+
+// The largest r < G with rstart[r] <= u: the range that holds unit u (ranges
+// are never empty).
+inline int64_t h_range_of(const uint32_t* rstart, int64_t G, int64_t u) {
+  int64_t lo = 0, hi = G;
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) / 2;
+    if ((int64_t)rstart[mid] <= u) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
 
 BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K);
 

@@ -642,21 +642,21 @@ __global__ __launch_bounds__(256) void sk_fixup_kernel(GemmArgs g, SkGeom sg, co
 // 0 is Dgrad (weight-block scales), problem 1 Wgrad (row scales); the two
 // have the same FLOP count.  The reductions of all their tiles are cut into
 // units of four 128-blocks, problem 0's tiles first, and range r of G takes
-// units [r W / G, (r + 1) W / G) of all W of them, so every workgroup does
-// the same work and the CUs stay busy across both GEMMs.  Segments, slots
-// and the fix-up of shared tiles work as in the Wgrad kernel above; when a
-// problem's tiles fall whole into ranges (BwdGeom k0, k1), the j-th tile of
-// its i-th range is tile j R + i (R ranges), so that the ranges running side
-// by side work on neighbouring tiles and share operand panels in L2.
+// units [rstart[r], rstart[r + 1]) of them: the host picks the cut that
+// balances the ranges' modelled cost, tiles and partial segments both
+// counted, so the CUs stay busy across both GEMMs.  Segments, slots and the
+// fix-up of shared tiles work as in the Wgrad kernel above; when a problem's
+// tiles fall whole into ranges of its own (dealt), the j-th tile of its i-th
+// range is tile j R + i (R ranges), so that the ranges running side by side
+// work on neighbouring tiles and share operand panels in L2.
 
 // BT: Dgrad reads the weight codes as quantized (gd.b is W[N][K]).
 template <bool BT>
 __global__ __launch_bounds__(THREADS) void gemm_mx_bwd_kernel(GemmArgs gd, GemmArgs gw, BwdGeom bg,
                                                               float* partials) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
-  const int64_t G = gridDim.x, W = bg.units;
   const int64_t r = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t ubeg = sk_start(r, W, G), uend = sk_start(r + 1, W, G);
+  const int64_t ubeg = bg.rstart[r], uend = bg.rstart[r + 1];
   v16f acc[TM][TN];
   for (int64_t u = ubeg; u < uend;) {
     const bool p1 = u >= bg.w0;
@@ -665,9 +665,9 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_bwd_kernel(GemmArgs gd, GemmA
     const int64_t lo = u - base - ts * U;                   // first unit of the segment, within the tile
     const int64_t tend = base + (ts + 1) * U;
     const int64_t hi = (uend < tend ? uend : tend) - base - ts * U;  // one past its last
-    const int64_t k = p1 ? bg.k1 : bg.k0;
-    const int64_t tiles = p1 ? bg.tm1 * bg.tn1 : bg.t0;
-    const int64_t tt = k > 0 ? (ts % k) * (tiles / k) + ts / k : ts;  // the tile itself
+    const int q = p1 ? 1 : 0;
+    // dealt: the j-th tile of the problem's i-th range is tile j * R + i
+    const int64_t tt = bg.deal[q] ? ((u - ubeg) / U) * bg.rpn[q] + (r - bg.rp0[q]) : ts;  // the tile itself
     int64_t i0, j0;
     tile_origin(tt, p1 ? bg.tm1 : bg.tm0, p1 ? bg.tn1 : bg.tn0, i0, j0);
     lds_barrier();  // the previous segment's epilogue is done with LDS
@@ -687,20 +687,33 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_bwd_kernel(GemmArgs gd, GemmA
   }
 }
 
+// The range of a backward launch that holds unit u: the largest r < G with
+// rstart[r] <= u (ranges are never empty).
+__device__ __forceinline__ int64_t bwd_range_of(const BwdGeom& bg, int64_t G, int64_t u) {
+  int64_t lo = 0, hi = G;
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) / 2;
+    if ((int64_t)bg.rstart[mid] <= u) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // The shared tiles of a backward launch: block (t, r) sums rows
 // 16r..16r+15 of tile t (problem 0's tiles, then problem 1's) over its
 // pieces in reduction order and stores them; slots as in sk_fixup_kernel.
+// (Tiles of a dealt problem are never shared.)
 __global__ __launch_bounds__(256) void bwd_fixup_kernel(GemmArgs gd, GemmArgs gw, BwdGeom bg, int64_t G,
                                                         const float* __restrict__ partials) {
   const int64_t t = blockIdx.x / (BM / FIX_ROWS);
   const int64_t r0 = (blockIdx.x % (BM / FIX_ROWS)) * FIX_ROWS;
   const bool p1 = t >= bg.t0;
   const int64_t ts = p1 ? t - bg.t0 : t, U = p1 ? bg.u1 : bg.u0;
-  const int64_t first = (p1 ? bg.w0 : 0) + ts * U, W = bg.units;
-  const int64_t f = sk_owner(first, W, G);
-  const int pieces = (int)(sk_owner(first + U - 1, W, G) - f + 1);
+  const int64_t first = (p1 ? bg.w0 : 0) + ts * U;
+  const int64_t f = bwd_range_of(bg, G, first);
+  const int pieces = (int)(bwd_range_of(bg, G, first + U - 1) - f + 1);
   if (pieces == 1) return;  // stored by the GEMM itself
-  const int64_t first_slot = slot_of(bg.slot, f, !(sk_start(f, W, G) < first));
+  const int64_t first_slot = slot_of(bg.slot, f, !((int64_t)bg.rstart[f] < first));
   int64_t i0, j0;
   tile_origin(ts, p1 ? bg.tm1 : bg.tm0, p1 ? bg.tn1 : bg.tn0, i0, j0);
   const int64_t I = p1 ? gw.I : gd.I, J = p1 ? gw.J : gd.J;

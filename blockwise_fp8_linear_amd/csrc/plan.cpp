@@ -38,18 +38,71 @@ void partial_ends(int64_t ubeg, int64_t uend, int64_t w0, int64_t u0, int64_t u1
   }
 }
 
-// Fill slot[0 .. G) for ranges of W units over the problems above; returns
-// the number of partial segments (slots).
-int64_t slot_table(uint16_t* slot, int64_t G, int64_t W, int64_t w0, int64_t u0, int64_t u1) {
+// Fill slot[0 .. G) for ranges [rstart[r], rstart[r+1]) of units over the
+// problems above; returns the number of partial segments (slots).
+int64_t slot_table(uint16_t* slot, const uint32_t* rstart, int64_t G, int64_t w0, int64_t u0, int64_t u1) {
   int64_t P = 0;
   for (int64_t r = 0; r < G; ++r) {
     bool f = false, l = false;
-    partial_ends(h_start(r, W, G), h_start(r + 1, W, G), w0, u0, u1, &f, &l);
+    partial_ends(rstart[r], rstart[r + 1], w0, u0, u1, &f, &l);
     slot[r] = (uint16_t)((P << 1) | (f ? 1 : 0));
     P += (f ? 1 : 0) + (l ? 1 : 0);
   }
   for (int64_t r = G; r < kSkGrid; ++r) slot[r] = (uint16_t)(P << 1);
   return P;
+}
+
+// ---- the fused backward's partition.  Cost model, in 128-blocks of MFMA
+// work: every segment pays a fixed cost (pipeline fill and epilogue, about
+// eight blocks' worth on the decoder layer's shapes), a partial one a little
+// more (its tile leaves in fp32), and any partial tile at all costs the
+// fix-up launch that follows.
+constexpr double kSegCost = 8.0, kPartialCost = 2.0, kFixupCost = 8.0;
+
+// Makespan of explicit ranges (exact walk), fix-up included.
+double ranges_cost(const uint32_t* rstart, int64_t G, int64_t w0, int64_t u0, int64_t u1) {
+  double worst = 0.0;
+  bool any_partial = false;
+  for (int64_t r = 0; r < G; ++r) {
+    double c = 0.0;
+    for (int64_t u = rstart[r]; u < (int64_t)rstart[r + 1];) {
+      const bool p1 = u >= w0;
+      const int64_t base = p1 ? w0 : 0, U = p1 ? u1 : u0;
+      const int64_t ts = (u - base) / U, lo = u - base - ts * U;
+      const int64_t tend = base + (ts + 1) * U;
+      const int64_t hi = ((int64_t)rstart[r + 1] < tend ? (int64_t)rstart[r + 1] : tend) - base - ts * U;
+      const bool partial = !(lo == 0 && hi == U);
+      c += 4.0 * (double)(hi - lo) + kSegCost + (partial ? kPartialCost : 0.0);
+      any_partial = any_partial || partial;
+      u = base + ts * U + hi;
+    }
+    worst = c > worst ? c : worst;
+  }
+  return worst + (any_partial ? kFixupCost : 0.0);
+}
+
+// One side of a two-sided partition: T tiles of U units on Gs ranges, cut in
+// whole tiles (tile_cut) or evenly in units; estimated makespan and whether
+// tiles get shared.
+double side_cost(int64_t T, int64_t U, int64_t Gs, bool tile_cut, bool* partial) {
+  if (tile_cut) {
+    *partial = false;
+    const int64_t tiles = (T + Gs - 1) / Gs;
+    return (double)tiles * (4.0 * (double)U + kSegCost);
+  }
+  const int64_t W = T * U, q = (W + Gs - 1) / Gs;
+  *partial = !(W % Gs == 0 && q % U == 0);
+  const int64_t segs = (q + U - 1) / U + (*partial ? 1 : 0);
+  return 4.0 * (double)q + (double)segs * kSegCost + (*partial ? 2.0 * kPartialCost : 0.0);
+}
+
+// Range starts of one side: ranges [r0, r0 + Gs) over units [base, base + T U).
+// A whole-tile cut gives the first T mod Gs ranges one tile more than the
+// others (so that tile j of range i can be j Gs + i).
+void side_starts(uint32_t* rstart, int64_t r0, int64_t Gs, int64_t base, int64_t T, int64_t U, bool tile_cut) {
+  const int64_t each = T / Gs, extra = T % Gs;
+  for (int64_t i = 0; i < Gs; ++i)
+    rstart[r0 + i] = (uint32_t)(base + (tile_cut ? U * (i * each + (i < extra ? i : extra)) : (i * T * U) / Gs));
 }
 
 }  // namespace
@@ -67,7 +120,13 @@ SkPlan sk_plan(int64_t I, int64_t J, int64_t R, int64_t tile_i, int64_t tile_j, 
   p.geom.units = W;
   p.geom.sk_grid = Gs;
   p.geom.sk_tiles = (W > 0 && W % Gs == 0 && U % (W / Gs) == 0) ? T - p.geom.dp_tiles : 0;
-  p.slots = W > 0 ? slot_table(p.geom.slot, Gs, W, W, U, U) : 0;
+  if (W > 0) {
+    uint32_t rstart[kSkGrid + 1];
+    for (int64_t r = 0; r <= Gs; ++r) rstart[r] = (uint32_t)h_start(r, W, Gs);
+    p.slots = slot_table(p.geom.slot, rstart, Gs, W, U, U);
+  } else {
+    p.slots = 0;
+  }
   p.bytes = (size_t)p.slots * (size_t)(tile_i * tile_j) * sizeof(float);
   return p;
 }
@@ -84,16 +143,67 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K) {
   b.u1 = M / 512;
   b.w0 = b.t0 * b.u0;
   b.units = b.w0 + b.tm1 * b.tn1 * b.u1;
-  p.grid = b.units < kSkGrid ? b.units : kSkGrid;
-  // round-robin tiles for a problem whose ranges all hold whole tiles: every
-  // range of the grid holds the same number q of units (G divides W), the
-  // problem starts and ends on range boundaries, and U divides q
-  if (b.units % p.grid == 0) {
-    const int64_t q = b.units / p.grid;
-    if (b.w0 % q == 0 && q % b.u0 == 0) b.k0 = q / b.u0;
-    if ((b.units - b.w0) % q == 0 && q % b.u1 == 0) b.k1 = q / b.u1;
+  const int64_t G = b.units < kSkGrid ? b.units : kSkGrid;
+  const int64_t T1 = b.tm1 * b.tn1;
+  p.grid = G;
+
+  // candidate 1: one even cut of all units (the two problems end to end)
+  for (int64_t r = 0; r <= G; ++r) b.rstart[r] = (uint32_t)h_start(r, b.units, G);
+  double best = ranges_cost(b.rstart, G, b.w0, b.u0, b.u1), best_sum = 1e300;
+  // candidates 2: problem 0 on ranges [0, G0), problem 1 on [G0, G), each side
+  // cut in whole tiles or evenly in units (no side gets more ranges than it
+  // has tiles or units, so no range is empty)
+  int64_t best_g0 = 0;
+  bool best_cut0 = false, best_cut1 = false;
+  for (int64_t g0 = 1; g0 < G; ++g0) {
+    const int64_t g1 = G - g0;
+    for (int m = 0; m < 4; ++m) {
+      const bool cut0 = m & 1, cut1 = m & 2;
+      if ((cut0 ? b.t0 : b.w0) < g0 || (cut1 ? T1 : b.units - b.w0) < g1) continue;
+      bool part0 = false, part1 = false;
+      const double c0 = side_cost(b.t0, b.u0, g0, cut0, &part0);
+      const double c1 = side_cost(T1, b.u1, g1, cut1, &part1);
+      const double c = (c0 > c1 ? c0 : c1) + ((part0 || part1) ? kFixupCost : 0.0);
+      // ties: the one with less work in all (more slack off the critical side)
+      const double sum = (double)g0 * c0 + (double)g1 * c1;
+      if (c < best - 1e-9 || (best_g0 > 0 && c < best + 1e-9 && sum < best_sum)) {
+        best = c;
+        best_sum = sum;
+        best_g0 = g0;
+        best_cut0 = cut0;
+        best_cut1 = cut1;
+      }
+    }
   }
-  p.slots = slot_table(b.slot, p.grid, b.units, b.w0, b.u0, b.u1);
+  if (best_g0 > 0) {
+    side_starts(b.rstart, 0, best_g0, 0, b.t0, b.u0, best_cut0);
+    side_starts(b.rstart, best_g0, G - best_g0, b.w0, T1, b.u1, best_cut1);
+    b.rstart[G] = (uint32_t)b.units;
+  }
+  // dealing: a problem whose ranges are its own and hold whole tiles
+  const int64_t pfirst[2] = {0, b.w0}, plast[2] = {b.w0, b.units}, pU[2] = {b.u0, b.u1};
+  for (int q = 0; q < 2; ++q) {
+    const int64_t r0 = h_range_of(b.rstart, G, pfirst[q]);
+    const int64_t r1 = h_range_of(b.rstart, G, plast[q] - 1) + 1;
+    bool whole = (int64_t)b.rstart[r0] == pfirst[q] && (int64_t)b.rstart[r1] == plast[q];
+    for (int64_t r = r0; whole && r < r1; ++r)
+      whole = ((int64_t)b.rstart[r] - pfirst[q]) % pU[q] == 0 && ((int64_t)b.rstart[r + 1] - pfirst[q]) % pU[q] == 0;
+    // every range but the last ones holds the same number of tiles, one more
+    // than those: tile j of range i is then j * R + i for all of them
+    int64_t hi_count = 0, lo_count = 0;
+    bool dealable = whole;
+    for (int64_t r = r0; dealable && r < r1; ++r) {
+      const int64_t n = ((int64_t)b.rstart[r + 1] - (int64_t)b.rstart[r]) / pU[q];
+      if (r == r0) hi_count = n;
+      if (n == hi_count && lo_count == 0) continue;
+      if (lo_count == 0 && n == hi_count - 1) lo_count = n;
+      else if (n != lo_count) dealable = false;
+    }
+    b.rp0[q] = r0;
+    b.rpn[q] = r1 - r0;
+    b.deal[q] = dealable ? 1 : 0;
+  }
+  p.slots = slot_table(b.slot, b.rstart, G, b.w0, b.u0, b.u1);
   p.bytes = (size_t)p.slots * kSlotBytes;
   return p;
 }

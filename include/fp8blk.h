@@ -325,7 +325,7 @@ int fp8_block_gemm_backward_w(int64_t M, int64_t N, int64_t K,
  *     FP8BLK_ERR_SCRATCH before launching anything.  The fused launch of
  *     power-of-two scales needs at most 32 MiB at the decoder layer's
  *     shapes (it can need up to 128 MiB at other shapes, e.g. 72 MiB at
- *     M = 1024, N = 2560, K = 3840); with amax / 448 scales (the promote
+ *     M = N = 1536, K = 2560); with amax / 448 scales (the promote
  *     pair) a call needs at most 64 MiB, so it always fits.
  *   Concurrency: every call on a GPU shares that GPU's array and leaves its
  *     contents behind (nothing in it needs to start at zero: each partial

@@ -264,7 +264,7 @@ static void gemm_checks() {
         "noalloc: the fused launch on the static scratch");
   n = g_log.size();
   expect_status("noalloc too big",
-                fp8_block_gemm_backward_w_noalloc(1024, 2560, 3840, a.p, sap, b.p, sbp, a.p, sap, b.p, sbp, dx.p, 0,
+                fp8_block_gemm_backward_w_noalloc(1536, 1536, 2560, a.p, sap, b.p, sbp, a.p, sap, b.p, sbp, dx.p, 0,
                                                   dw.p, 1, FP8BLK_SCALE_POW2, nullptr),
                 FP8BLK_ERR_SCRATCH, n);
   expect_status("noalloc fp32",
@@ -291,25 +291,43 @@ static int64_t slot_of(const uint16_t* t, int64_t r, bool first) {
   return (int64_t)(t[r] >> 1) + (first ? 0 : (int64_t)(t[r] & 1));
 }
 
-// Walk every range of W units over problems [0, w0) (tiles of u0 units) and
-// [w0, W) (u1); record for every partial segment (problem, tile, first unit)
-// the slot its range writes; then enumerate each shared tile's pieces as the
-// fix-up does and check that piece k is the slot that wrote units
-// [piece start ..).
+// Walk every range [rs[r], rs[r+1]) of W units over problems [0, w0) (tiles
+// of u0 units) and [w0, W) (u1) as the kernels do; check that every unit of
+// every tile is reduced exactly once, mapping a dealt problem's segments to
+// tiles as the backward kernel does (deal, rp0, rpn: BwdGeom's; all zero for
+// the Wgrad plans), and that dealt tiles are never shared.  Record for every
+// partial segment (problem, tile, first unit) the slot its range writes;
+// then enumerate each shared tile's pieces as the fix-up does and check that
+// piece k is the slot that wrote units [piece start ..).
 static void check_slots(const char* what, const uint16_t* table, int64_t slots, int64_t G, int64_t W, int64_t w0,
-                        int64_t u0, int64_t u1) {
+                        int64_t u0, int64_t u1, const uint32_t* rs, const int64_t* deal = nullptr,
+                        const int64_t* rp0 = nullptr, const int64_t* rpn = nullptr) {
+  CHECK(rs[0] == 0 && (int64_t)rs[G] == W, "%s: ranges cover [%u, %u), not [0, %lld)", what, rs[0], rs[G],
+        (long long)W);
+  for (int64_t r = 0; r < G; ++r)
+    CHECK(rs[r] < rs[r + 1], "%s: range %lld is empty or reversed", what, (long long)r);
   std::set<int64_t> used;
   // (unit of the piece's start) -> slot
   std::vector<int64_t> slot_at(W, -1);
+  // units reduced per tile, problem 0's tiles then problem 1's
+  const int64_t t0 = w0 / u0, t1 = u1 > 0 ? (W - w0) / u1 : 0;
+  std::vector<int64_t> cov(t0 + t1, 0);
   for (int64_t r = 0; r < G; ++r) {
-    const int64_t ubeg = fp8blk::h_start(r, W, G), uend = fp8blk::h_start(r + 1, W, G);
+    const int64_t ubeg = rs[r], uend = rs[r + 1];
     for (int64_t u = ubeg; u < uend;) {
       const bool p1 = u >= w0;
       const int64_t base = p1 ? w0 : 0, U = p1 ? u1 : u0;
       const int64_t ts = (u - base) / U, lo = u - base - ts * U;
       const int64_t tend = base + (ts + 1) * U;
       const int64_t hi = (uend < tend ? uend : tend) - base - ts * U;
+      const int q = p1 ? 1 : 0;
+      const bool dealt = deal != nullptr && deal[q] != 0;
+      const int64_t tt = dealt ? ((u - ubeg) / U) * rpn[q] + (r - rp0[q]) : ts;
+      CHECK(tt >= 0 && tt < (p1 ? t1 : t0), "%s: range %lld maps a segment to tile %lld of %lld", what,
+            (long long)r, (long long)tt, (long long)(p1 ? t1 : t0));
+      if (tt >= 0 && tt < (p1 ? t1 : t0)) cov[(p1 ? t0 : 0) + tt] += hi - lo;
       if (!(lo == 0 && hi == U)) {
+        CHECK(!dealt, "%s: range %lld holds part of a dealt tile", what, (long long)r);
         const int64_t s = slot_of(table, r, u == ubeg);
         CHECK(s >= 0 && s < slots, "%s: range %lld writes slot %lld outside [0, %lld)", what, (long long)r,
               (long long)s, (long long)slots);
@@ -319,21 +337,31 @@ static void check_slots(const char* what, const uint16_t* table, int64_t slots, 
       u = base + ts * U + hi;
     }
   }
+  for (int64_t t = 0; t < t0 + t1; ++t)
+    CHECK(cov[t] == (t < t0 ? u0 : u1), "%s: tile %lld reduced over %lld units", what, (long long)t,
+          (long long)cov[t]);
   CHECK((int64_t)used.size() == slots, "%s: %zu slots written, plan says %lld", what, used.size(), (long long)slots);
   // the fix-up: tile starting at unit `first` with U units
   auto fixup = [&](int64_t first, int64_t U) {
-    const int64_t f = fp8blk::h_owner(first, W, G);
-    const int64_t pieces = fp8blk::h_owner(first + U - 1, W, G) - f + 1;
+    const int64_t f = fp8blk::h_range_of(rs, G, first);
+    const int64_t pieces = fp8blk::h_range_of(rs, G, first + U - 1) - f + 1;
     if (pieces == 1) return;
     for (int64_t pc = 0; pc < pieces; ++pc) {
-      const int64_t s = pc == 0 ? slot_of(table, f, !(fp8blk::h_start(f, W, G) < first)) : slot_of(table, f + pc, true);
-      const int64_t start = pc == 0 ? first : fp8blk::h_start(f + pc, W, G);
+      const int64_t s = pc == 0 ? slot_of(table, f, !((int64_t)rs[f] < first)) : slot_of(table, f + pc, true);
+      const int64_t start = pc == 0 ? first : (int64_t)rs[f + pc];
       CHECK(start < W && slot_at[start] == s, "%s: fix-up of the tile at unit %lld reads slot %lld for piece %lld",
             what, (long long)first, (long long)s, (long long)pc);
     }
   };
   for (int64_t u = 0; u < w0; u += u0) fixup(u, u0);
   for (int64_t u = w0; u < W; u += u1) fixup(u, u1);
+}
+
+// The Wgrad kernels' even cut: range w of Gs over W units starts at w W / Gs.
+static std::vector<uint32_t> even_ranges(int64_t W, int64_t G) {
+  std::vector<uint32_t> rs(G + 1);
+  for (int64_t w = 0; w <= G; ++w) rs[w] = (uint32_t)fp8blk::h_start(w, W, G);
+  return rs;
 }
 
 static void plan_checks() {
@@ -350,7 +378,10 @@ static void plan_checks() {
     if ((M / 128) % 4 == 0 && (N / 128) % 4 == 0) {
       const fp8blk::BwdPlan p = fp8blk::bwd_plan(M, N, K);
       std::snprintf(what, sizeof what, "backward %lldx%lldx%lld", (long long)M, (long long)N, (long long)K);
-      check_slots(what, p.geom.slot, p.slots, p.grid, p.geom.units, p.geom.w0, p.geom.u0, p.geom.u1);
+      const fp8blk::BwdGeom& g = p.geom;
+      check_slots(what, g.slot, p.slots, p.grid, g.units, g.w0, g.u0, g.u1, g.rstart, g.deal, g.rp0, g.rpn);
+      CHECK(g.t0 == g.tm0 * g.tn0 && g.w0 == g.t0 * g.u0 && g.units == g.w0 + g.tm1 * g.tn1 * g.u1,
+            "%s: geometry", what);
       CHECK(p.bytes == (size_t)p.slots * 256 * 256 * 4, "%s: bytes", what);
     }
     {  // the general kernel's Wgrad: 256 x 128 tiles, units of 4 or 1 blocks
@@ -359,7 +390,8 @@ static void plan_checks() {
       const int64_t U = M / (128 * p.geom.ublocks);
       CHECK(p.geom.ublocks == ((M / 128) % 4 == 0 ? 4 : 1), "%s: unit size", what);
       if (p.geom.units > 0)
-        check_slots(what, p.geom.slot, p.slots, p.geom.sk_grid, p.geom.units, p.geom.units, U, U);
+        check_slots(what, p.geom.slot, p.slots, p.geom.sk_grid, p.geom.units, p.geom.units, U, U,
+                    even_ranges(p.geom.units, p.geom.sk_grid).data());
       else
         CHECK(p.slots == 0, "%s: no stream-K units, no slots", what);
       CHECK(p.bytes == (size_t)p.slots * 256 * 128 * 4, "%s: bytes", what);
@@ -369,7 +401,8 @@ static void plan_checks() {
       const fp8blk::SkPlan p = fp8blk::sk_plan(N, K, M);  // Wgrad: I = N, J = K, R = M
       std::snprintf(what, sizeof what, "wgrad %lldx%lldx%lld", (long long)M, (long long)N, (long long)K);
       if (p.geom.units > 0)
-        check_slots(what, p.geom.slot, p.slots, p.geom.sk_grid, p.geom.units, p.geom.units, M / 512, M / 512);
+        check_slots(what, p.geom.slot, p.slots, p.geom.sk_grid, p.geom.units, p.geom.units, M / 512, M / 512,
+                    even_ranges(p.geom.units, p.geom.sk_grid).data());
       else
         CHECK(p.slots == 0, "%s: no stream-K units, no slots", what);
     }

@@ -234,7 +234,7 @@ def test_backward_scale_mode(lib, fn):
 def test_noalloc_backward_host_checks(lib):
     """The no-allocation backward: argument errors as for the workspace form,
     and a launch that would need more than the static scratch is refused
-    before anything runs (the fused launch at 1024 x 2560 x 3840 cuts its
+    before anything runs (the fused launch at 1536 x 1536 x 2560 cuts its
     ranges into 288 partial 256x256 tiles: 72 MiB)."""
     f = lib.fp8_block_gemm_backward_w_noalloc
     args = lambda M, N, K, mode, dx=0x800000, dw=0x900000: (M, N, K, P, P3, P2, P3, 0x400000, 0x500000, 0x600000,
@@ -242,7 +242,7 @@ def test_noalloc_backward_host_checks(lib):
     assert f(*args(8192, 2048, 2048, 0)) in (EHIP, EDEV)       # fused launch, 32 MiB of slots: fits
     assert f(*args(8192, 2048, 6144, 0)) in (EHIP, EDEV)
     assert f(*args(8192, 2048, 6144, 1)) in (EHIP, EDEV)       # promote pair: 32 MiB of Wgrad partials
-    assert f(*args(1024, 2560, 3840, 0)) == ESCR               # needs 72 MiB > 64 MiB
+    assert f(*args(1536, 1536, 2560, 0)) == ESCR               # needs 72 MiB > 64 MiB
     assert f(*args(8192, 2048, 2048, 2)) == EARG
     assert f(*args(8192, 2048, 2048, 0, dx=0x900000)) == EARG  # dx and dw alias
     assert f(*args(8192, 200, 2048, 0)) == EDIM

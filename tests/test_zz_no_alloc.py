@@ -84,7 +84,7 @@ def test_noalloc_backward_calls_in_a_row():
 
 def test_noalloc_refuses_more_than_its_scratch():
     import torch
-    M, N, K = 1024, 2560, 3840          # the fused launch: 288 partial 256x256 tiles, 72 MiB
+    M, N, K = 1536, 1536, 2560          # the fused launch: 288 partial 256x256 tiles, 72 MiB
     ops, _ = _operands(M, N, K, (91, 0), fb.FP8BLK_SCALE_POW2)
     dx, dw = _filled((M, K), torch.bfloat16), _filled((N, K), torch.bfloat16)
     torch.cuda.synchronize()
