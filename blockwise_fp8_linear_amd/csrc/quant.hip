@@ -20,6 +20,8 @@
 
 namespace fp8blk {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 // ---------------------------------------------------------------------------
 // Row groups.  A DPP row (16 lanes) owns one 128-element group: each lane
 // loads 8 bf16 (16 B), the row's 16 lanes cover the group's 256 B.  A wave
@@ -259,18 +261,50 @@ __device__ __forceinline__ uint32_t quant4_cols(uint32_t w0, uint32_t w1, const 
   return (uint32_t)r;
 }
 
-template <class S>
+// Tile order of the one-pass quantizer.  A tile's scales are 128 four-byte
+// values strided through s (one per row) and 128 through sT (one per
+// column); the 8 tiles side by side along a row band fill one 32-byte
+// sector of s, the 8 above one another one of sT.  Where the shape allows
+// (kDualBlocked: a multiple of 16 row tiles and of 8 column tiles, whole
+// multiples of 8 blocks), the tiles go in blocks of 8 column tiles x 16 row
+// tiles, block k to the workgroups k, k + 8, ... mod 8, i.e. to one XCD
+// (workgroups are dealt to the 8 XCDs in turn), walked down each column of
+// the block: every sector of s and sT is then written by one XCD, whose L2
+// merges the pieces before writing the sector back.  Measured on the
+// activation shapes: written bytes at the algorithmic count (+11% in row-band
+// order, from partial sectors written back from several L2s), and 0-8%
+// faster.  Other shapes walk row band by row band.  NT: the codes leave with
+// non-temporal stores (measured 4-10% faster from 32 column tiles on in the
+// blocked order, 3% slower at 16).
+constexpr uint32_t kDualBlockCols = 8, kDualBlockRows = 16, kDualNtColTiles = 32;
+
+__host__ __device__ __forceinline__ bool dual_blocked(uint32_t row_tiles, uint32_t col_tiles) {
+  return row_tiles % kDualBlockRows == 0 && col_tiles % kDualBlockCols == 0 &&
+         (row_tiles / kDualBlockRows) * (col_tiles / kDualBlockCols) % 8 == 0;
+}
+
+template <class S, bool NT>
 __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ s,
-    uint8_t* __restrict__ qT, int64_t ld_qT, float* __restrict__ sT, uint32_t row_tiles, uint32_t col_tiles) {
+    uint8_t* __restrict__ qT, int64_t ld_qT, float* __restrict__ sT, uint32_t row_tiles, uint32_t col_tiles,
+    uint32_t blocked) {
   __shared__ uint32_t red[kDualThreads / 64][16][4];
   __shared__ __attribute__((aligned(16))) uint2 tq[128][16];  // column codes: [column][8-row block]
   const uint32_t t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  // consecutive workgroups walk along the rows, so that the ones in flight
-  // together read whole rows of x (measured: a few per cent faster than
-  // walking down the columns, with or without the XCD remap)
-  const uint32_t rt = blockIdx.x / col_tiles;
-  const uint32_t ct = blockIdx.x - rt * col_tiles;
+  uint32_t rt, ct;
+  if (blocked) {
+    constexpr uint32_t kPerBlock = kDualBlockCols * kDualBlockRows;
+    const uint32_t xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+    const uint32_t blk = xcd + 8 * (j / kPerBlock), w = j % kPerBlock;
+    const uint32_t col_blocks = col_tiles / kDualBlockCols;
+    rt = (blk / col_blocks) * kDualBlockRows + w % kDualBlockRows;
+    ct = (blk % col_blocks) * kDualBlockCols + w / kDualBlockRows;
+  } else {
+    // consecutive workgroups walk along the rows, so that the ones in flight
+    // together read whole rows of x
+    rt = blockIdx.x / col_tiles;
+    ct = blockIdx.x - rt * col_tiles;
+  }
   const int64_t m0 = (int64_t)rt * 128, c0 = (int64_t)ct * 128;
   const uint32_t rb = t >> 4, cb = t & 15;
   const int64_t r0 = m0 + rb * 8;
@@ -291,7 +325,9 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     uint2 o;
     o.x = quant4(v[i].x, v[i].y, sc);
     o.y = quant4(v[i].z, v[i].w, sc);
-    *reinterpret_cast<uint2*>(q + (r0 + i) * ld_q + c0 + cb * 8) = o;
+    uint2* const qp = reinterpret_cast<uint2*>(q + (r0 + i) * ld_q + c0 + cb * 8);
+    if constexpr (NT) __builtin_nontemporal_store((u32x2{o.x, o.y}), reinterpret_cast<u32x2*>(qp));
+    else *qp = o;
     if (cb == 0) s[(r0 + i) * G + ct] = sc.s;
   }
 
@@ -348,7 +384,9 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     const uint32_t pu = (2 * p) ^ (c >> 3);  // physical unit of row block 2p
     u32x4 w = *reinterpret_cast<const u32x4*>(&tq[c][pu & ~1u]);
     if (pu & 1) w = u32x4{w[2], w[3], w[0], w[1]};  // the pair is stored swapped
-    *reinterpret_cast<u32x4*>(qT + (c0 + c) * ld_qT + m0 + 16 * p) = w;
+    u32x4* const qTp = reinterpret_cast<u32x4*>(qT + (c0 + c) * ld_qT + m0 + 16 * p);
+    if constexpr (NT) __builtin_nontemporal_store(w, qTp);
+    else *qTp = w;
   }
   if (rb == 0) {
 #pragma unroll
@@ -419,12 +457,24 @@ hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int6
                              float* s, uint8_t* qT, int64_t ld_qT, float* sT, bool fp32_scale, hipStream_t stream) {
   const uint32_t rt = (uint32_t)(rows / 128);
   const uint32_t ct = (uint32_t)(cols / 128);
-  if (fp32_scale)
-    hipLaunchKernelGGL(quant_dual_kernel<Fp32Scale>, dim3(rt * ct), dim3(kDualThreads), 0, stream, x, ld_x, q, ld_q, s,
-                       qT, ld_qT, sT, rt, ct);
-  else
-    hipLaunchKernelGGL(quant_dual_kernel<Pow2Scale>, dim3(rt * ct), dim3(kDualThreads), 0, stream, x, ld_x, q, ld_q, s,
-                       qT, ld_qT, sT, rt, ct);
+  const uint32_t blocked = dual_blocked(rt, ct) ? 1u : 0u;
+  const bool nt = blocked && ct >= kDualNtColTiles;
+  const dim3 grid(rt * ct), block(kDualThreads);
+  if (fp32_scale) {
+    if (nt)
+      hipLaunchKernelGGL((quant_dual_kernel<Fp32Scale, true>), grid, block, 0, stream, x, ld_x, q, ld_q, s, qT, ld_qT,
+                         sT, rt, ct, blocked);
+    else
+      hipLaunchKernelGGL((quant_dual_kernel<Fp32Scale, false>), grid, block, 0, stream, x, ld_x, q, ld_q, s, qT, ld_qT,
+                         sT, rt, ct, blocked);
+  } else {
+    if (nt)
+      hipLaunchKernelGGL((quant_dual_kernel<Pow2Scale, true>), grid, block, 0, stream, x, ld_x, q, ld_q, s, qT, ld_qT,
+                         sT, rt, ct, blocked);
+    else
+      hipLaunchKernelGGL((quant_dual_kernel<Pow2Scale, false>), grid, block, 0, stream, x, ld_x, q, ld_q, s, qT, ld_qT,
+                         sT, rt, ct, blocked);
+  }
   return hipGetLastError();
 }
 
