@@ -87,6 +87,11 @@ struct BwdGeom {
   int64_t rp0[2], rpn[2], deal[2];
   uint32_t rstart[kSkGrid + 1];
   uint16_t slot[kSkGrid];
+  // the tiles that several ranges share (problem 0's numbered 0 .. t0 - 1,
+  // then problem 1's), ascending: each range boundary inside a tile makes
+  // that tile shared, so there are fewer than kSkGrid
+  int64_t nshared;
+  uint32_t shared[kSkGrid];
 };
 
 struct BwdPlan {

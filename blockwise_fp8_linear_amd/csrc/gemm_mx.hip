@@ -699,13 +699,14 @@ __device__ __forceinline__ int64_t bwd_range_of(const BwdGeom& bg, int64_t G, in
   return lo;
 }
 
-// The shared tiles of a backward launch: block (t, r) sums rows
-// 16r..16r+15 of tile t (problem 0's tiles, then problem 1's) over its
-// pieces in reduction order and stores them; slots as in sk_fixup_kernel.
-// (Tiles of a dealt problem are never shared.)
+// The shared tiles of a backward launch: block (k, r) sums rows
+// 16r..16r+15 of the k-th shared tile t = shared[k] (problem 0's tiles
+// numbered first, then problem 1's) over its pieces in reduction order and
+// stores them; slots as in sk_fixup_kernel.  (Tiles of a dealt problem are
+// never shared.)
 __global__ __launch_bounds__(256) void bwd_fixup_kernel(GemmArgs gd, GemmArgs gw, BwdGeom bg, int64_t G,
                                                         const float* __restrict__ partials) {
-  const int64_t t = blockIdx.x / (BM / FIX_ROWS);
+  const int64_t t = bg.shared[blockIdx.x / (BM / FIX_ROWS)];
   const int64_t r0 = (blockIdx.x % (BM / FIX_ROWS)) * FIX_ROWS;
   const bool p1 = t >= bg.t0;
   const int64_t ts = p1 ? t - bg.t0 : t, U = p1 ? bg.u1 : bg.u0;
@@ -796,10 +797,9 @@ hipError_t launch_bwd(const GemmArgs& gd, const GemmArgs& gw, float* ws, hipStre
   hipLaunchKernelGGL(gemm_mx_bwd_kernel<BT>, dim3((uint32_t)p.grid), dim3(THREADS), LDS_BYTES, stream, gd, gw, p.geom,
                      partials);
   if (hipError_t e = hipGetLastError()) return e;
-  if (p.slots == 0) return hipSuccess;
-  const int64_t T = p.geom.t0 + p.geom.tm1 * p.geom.tn1;
-  hipLaunchKernelGGL(bwd_fixup_kernel, dim3((uint32_t)(T * (BM / FIX_ROWS))), dim3(256), 0, stream, gd, gw, p.geom,
-                     p.grid, partials);
+  if (p.geom.nshared == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_fixup_kernel, dim3((uint32_t)(p.geom.nshared * (BM / FIX_ROWS))), dim3(256), 0, stream, gd,
+                     gw, p.geom, p.grid, partials);
   return hipGetLastError();
 }
 

@@ -205,6 +205,16 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K) {
   }
   p.slots = slot_table(b.slot, b.rstart, G, b.w0, b.u0, b.u1);
   p.bytes = (size_t)p.slots * kSlotBytes;
+  // shared tiles: those holding a range boundary strictly inside them
+  b.nshared = 0;
+  for (int64_t r = 1; r < G; ++r) {
+    const int64_t u = b.rstart[r];
+    const bool p1 = u >= b.w0;
+    const int64_t off = u - (p1 ? b.w0 : 0), U = p1 ? b.u1 : b.u0;
+    if (off % U == 0) continue;  // the boundary falls between tiles
+    const int64_t t = (p1 ? b.t0 : 0) + off / U;
+    if (b.nshared == 0 || b.shared[b.nshared - 1] != (uint32_t)t) b.shared[b.nshared++] = (uint32_t)t;
+  }
   return p;
 }
 

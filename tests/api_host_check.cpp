@@ -15,6 +15,7 @@
 //     producer wrote.
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <set>
 #include <string>
 #include <vector>
@@ -382,6 +383,17 @@ static void plan_checks() {
       check_slots(what, g.slot, p.slots, p.grid, g.units, g.w0, g.u0, g.u1, g.rstart, g.deal, g.rp0, g.rpn);
       CHECK(g.t0 == g.tm0 * g.tn0 && g.w0 == g.t0 * g.u0 && g.units == g.w0 + g.tm1 * g.tn1 * g.u1,
             "%s: geometry", what);
+      // the shared-tile list: exactly the tiles spanning more than one range, ascending
+      std::vector<uint32_t> want;
+      for (int64_t t = 0; t < g.t0 + g.tm1 * g.tn1; ++t) {
+        const bool p1 = t >= g.t0;
+        const int64_t U = p1 ? g.u1 : g.u0, first = p1 ? g.w0 + (t - g.t0) * U : t * U;
+        if (fp8blk::h_range_of(g.rstart, p.grid, first) != fp8blk::h_range_of(g.rstart, p.grid, first + U - 1))
+          want.push_back((uint32_t)t);
+      }
+      CHECK(g.nshared == (int64_t)want.size() && std::equal(want.begin(), want.end(), g.shared),
+            "%s: %lld shared tiles listed, %zu span several ranges", what, (long long)g.nshared, want.size());
+      CHECK((p.slots == 0) == (g.nshared == 0), "%s: slots without shared tiles or the reverse", what);
       CHECK(p.bytes == (size_t)p.slots * 256 * 256 * 4, "%s: bytes", what);
     }
     {  // the general kernel's Wgrad: 256 x 128 tiles, units of 4 or 1 blocks
