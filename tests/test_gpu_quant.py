@@ -247,6 +247,15 @@ def test_dual_strided_input_padded_outputs():
     _assert_dual(wide, "column slice, padded outputs", cols=2048, pad_q=256, pad_qT=128)
 
 
+def test_dual_blocked_order_strided_padded():
+    """A shape the one-pass quantizer walks in XCD blocks of 8 x 16 tiles with
+    non-temporal code stores (16 row tiles, 64 column tiles), read from a
+    column slice of a wider tensor into padded outputs: every tile is
+    written, bit for bit, and nothing past the outputs' ends."""
+    wide = synth.normal_bf16((2048, 8192 + 256), 1.0, 49, 0)
+    _assert_dual(wide, "blocked order, column slice, padded outputs", cols=8192, pad_q=128, pad_qT=256)
+
+
 def test_dual_decoder_layer():
     for lin in synth.decoder_layer():
         _assert_dual(lin["x"], f"X {lin['name']}")
