@@ -1,6 +1,7 @@
 // Host-side launch planning of libfp8blk's GEMMs (see fp8blk_plan.h): the
-// persistent kernels' range partitions and workspace slot tables, the
-// general kernel's split-K factor, and which kernel a contraction can take.
+// persistent kernels' range partitions and workspace slot tables (both
+// GEMM kernels' stream-K Wgrad, the fused backward), workspace sizes, and
+// which kernel a contraction can take.
 // Plain C++, no device code, so that it can also be built and exercised on a
 // host alone (the C ABI's sanitizer test does).
 #include "fp8blk_plan.h"

@@ -259,7 +259,8 @@ def test_workspace_query(lib):
     # O-projection wgrad: 64 output tiles of 256x256 whose 8192-token
     # reduction (16 units of 512) is cut into 4 pieces each by the 256
     # workgroups: one 256x256 fp32 slot per partial segment (256 of them),
-    # and enough for the general kernel's split-K partials too
+    # and at least what the general kernel's stream-K partials need (256 of
+    # its 256x128 tiles)
     n = q(2, 8192, 2048, 2048)
     assert n == max(256 * 256 * 256 * 4, 2 * 2048 * 2048 * 4)
     # the fused backward of the same linear: Dgrad's 256 tiles fall whole

@@ -259,7 +259,7 @@ def test_fp32_scales_promote_small_shapes(shape):
 @pytest.mark.parametrize("li", [0, 3])
 def test_fp32_scales_promote_decoder_layer_full_size(li):
     """QKV and down-projection linears at 8192 tokens with amax / 448 scales:
-    fprop, dgrad and wgrad (split-K) on sampled output rows."""
+    fprop, dgrad and wgrad (stream-K) on sampled output rows."""
     lin = synth.decoder_layer(linears=(synth.LAYER_LINEARS[li],))[0]
     layer = Layer(lin["x"], lin["w"], lin["dy"], mode=1)
     for op in OPS:
@@ -269,7 +269,7 @@ def test_fp32_scales_promote_decoder_layer_full_size(li):
 
 def test_named_entry_points_and_determinism():
     """The named C entry points (default algorithm) equal the generic one, and
-    repeated runs -- including split-K Wgrad -- are bit-identical."""
+    repeated runs -- including the stream-K Wgrad -- are bit-identical."""
     import torch
     M, N, K = 8192, 2048, 256
     layer = Layer(synth.normal_bf16((M, K), 1.0, 65, 0), synth.normal_bf16((N, K), 0.02, 65, 1),
@@ -287,8 +287,8 @@ def test_named_entry_points_and_determinism():
     assert torch.equal(a, b) and torch.equal(a, c)
     assert torch.equal(f1, f2) and torch.equal(d1, d2)
     rows = _sample_rows(N, (65, 3), k=8)
-    check_op(layer, "wgrad", "promote", rows=rows, what="split-K")
-    check_op(layer, "wgrad", "scaled", rows=rows, what="split-K")
+    check_op(layer, "wgrad", "promote", rows=rows, what="stream-K")
+    check_op(layer, "wgrad", "scaled", rows=rows, what="stream-K")
 
 
 # Wgrad shapes (M, N, K) that exercise the persistent Wgrad kernel of the
@@ -336,7 +336,7 @@ def test_many_tiles_ragged(shape, ops):
 # fp32 accumulation into an existing output (FP8BLK_OUT_FP32_ACCUM, the fp32
 # main-gradient case): the result must be exactly fl32(old + r), r being what
 # FP8BLK_OUT_FP32 stores, for every op, both algorithms, and the Wgrad paths
-# that sum partial tiles (stream-K fix-up, split-K reduction).
+# that sum partial tiles (the stream-K fix-ups of both GEMM paths).
 @pytest.mark.parametrize("shape", [(1024, 4096, 6144), (2048, 256, 256), (640, 384, 1024), (4224, 4224, 512)])
 def test_fp32_accumulate(shape):
     import torch
