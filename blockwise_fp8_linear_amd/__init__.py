@@ -53,6 +53,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built: run `python -m blockwise_fp8_linear_amd.build` "
                            "(or __graft_entry__.build()) first")
+    # torch ships its own HIP runtime under the same soname as the system's.
+    # Loaded first, this library would pull in the system copy and torch its
+    # own: two runtimes in one process, whose streams and kernels do not mix
+    # (every launch fails).  Importing torch first makes the library bind to
+    # torch's runtime.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     sig = {
