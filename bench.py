@@ -123,6 +123,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="replay every timed step from one HIP graph captured after the warm-up (the host then "
+                         "enqueues one graph per step); the roofline's kernel durations then come from eager "
+                         "steps run right after the timed ones")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
@@ -565,6 +569,15 @@ def main():
     T = Timer(torch, True, per_step * n_sampled, only=dom_kinds)
     bare = Timer(torch, False)
     bounds = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_sampled)]
+    graph = None
+    if args.graph:
+        # capture one whole step (every call only enqueues on the current
+        # stream, which is the capture stream here); replays run all of it
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(Timer(torch, False))
+        graph.replay()
+        torch.cuda.synchronize()
     gc.collect()
     gc.disable()
     torch.cuda.synchronize()
@@ -573,14 +586,25 @@ def main():
         if i % SAMPLE == 0:
             b0, b1 = bounds[i // SAMPLE]
             b0.record()
-            step(T)
+            if graph is not None:
+                graph.replay()
+            else:
+                step(T)
             b1.record()
+        elif graph is not None:
+            graph.replay()
         else:
             step(bare)
     enqueued = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gc.enable()
+    if graph is not None:
+        # events cannot surround single kernels inside a replay: the dominant
+        # kernel's durations come from as many eager steps, right after
+        for i in range(n_sampled):
+            step(T)
+        torch.cuda.synchronize()
     per_step_ms = sorted(b0.elapsed_time(b1) for b0, b1 in bounds)
 
     def pct(p):
@@ -616,9 +640,10 @@ def main():
         "step_ms_spread": {"p10": pct(0.1), "median": pct(0.5), "p90": pct(0.9),
                            "mean": round(sum(per_step_ms) / len(per_step_ms), 4),
                            "host_enqueue_ms": round(enqueued / args.steps * 1e3, 4),
-                           "what": "single-step times of every 4th timed step (events at its start and end; "
-                                   "those steps also carry the events around the dominant kernel's launches); "
-                                   "host_enqueue_ms: host time per timed step to enqueue the steps"},
+                           "what": "single-step times of every 4th timed step (events at its start and end" +
+                                   ("" if args.graph else
+                                    "; those steps also carry the events around the dominant kernel's launches") +
+                                   "); host_enqueue_ms: host time per timed step to enqueue the steps"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -630,6 +655,7 @@ def main():
                    "backward": "separate" if args.separate_bwd else "fused",
                    "weight_quant": "per weight" if args.separate_wquant else "batched per layer",
                    "dgrad_weights": "transposed copy" if args.transposed_weights else "codes as quantized",
+                   "launch": "one HIP graph per step" if args.graph else "eager",
                    "gemm_tflop_per_step": round(step_flops / 1e12, 4)},
         "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
         "gemm_only_TFLOP/s": round(gemm_flops_t / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
@@ -639,7 +665,8 @@ def main():
                           "pair of events adds a few microseconds to each launch (the first launch of a step "
                           "can also include host enqueue time), so these per-kind rates understate the "
                           "kernels, short ones most: the kernel traces in profiles/ give their durations. The "
-                          "roofline comes from the dominant kernel's own events in the timed steps",
+                          "roofline comes from the dominant kernel's own events in the timed steps" +
+                          (" (with --graph: in as many eager steps right after them)" if args.graph else ""),
         "sources_digest": sources_digest(),
     }
     if not args.no_ceilings:
