@@ -19,7 +19,9 @@
 //   * the scale bytes of four consecutive 128-blocks are packed in one
 //     register per operand row and picked by the instruction's op_sel; the
 //     weight-block scales of a tile are staged in LDS once;
-//   * the epilogue stages each wave's tile through LDS and stores whole rows;
+//   * the epilogue stages each wave's tile through LDS and stores whole rows,
+//     non-temporal: a round of tiles writes 32 MiB of output, which through
+//     L2 would evict the operand panels the next tiles read;
 //   * Dgrad can read the weight codes W[n][k] as quantized (reduction along
 //     the rows, no transposed copy): that B tile is staged as 128 weight rows
 //     of 256 bytes and its fragments come from LDS transpose reads
@@ -372,7 +374,8 @@ struct Dst {
 // ring and any earlier staging are free.
 template <int BATCH, class Src>
 __device__ __forceinline__ void store_tile_from(const Dst& d, uint8_t* lds, int64_t i0, int64_t j0, Src src) {
-  // ---- epilogue, staged through LDS so that global stores are whole rows.
+  // ---- epilogue, staged through LDS so that global stores are whole rows,
+  // non-temporal (the output is not read again here).
   // src(a, b) lane l, element e holds row i = wm0 + 32a + l%32 and column
   // j = wn0 + 32b + 8*(e/4) + 4*(l/32) + e%4.  Each wave writes its 128 x 128
   // tile to its own 32 KiB of LDS in units of 4 consecutive columns, the unit
@@ -431,7 +434,8 @@ __device__ __forceinline__ void store_tile_from(const Dst& d, uint8_t* lds, int6
           // the pair is stored swapped when its physical unit is odd (row odd)
           const u32x4 o = (row & 1) ? u32x4{v[s][2], v[s][3], v[s][0], v[s][1]} : v[s];
           const int64_t i = i0 + wm0 + row;
-          if (full || (i < d.rows && col_ok)) *reinterpret_cast<u32x4*>(outh + i * d.ld + col0 + 8 * k) = o;
+          if (full || (i < d.rows && col_ok))
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(outh + i * d.ld + col0 + 8 * k));
         }
       }
     } else {
@@ -476,15 +480,17 @@ __device__ __forceinline__ void store_tile_from(const Dst& d, uint8_t* lds, int6
               const uint32_t row = (pb + s) * 2 + (lane >> 5), k = lane & 31;
               const int64_t i = i0 + wm0 + 64 * h + row;
               if (full || (i < d.rows && col_ok))
-                *reinterpret_cast<v4f*>(outf + i * d.ld + col0 + 4 * k) =
-                    v4f{o[s][0] + v[s][0], o[s][1] + v[s][1], o[s][2] + v[s][2], o[s][3] + v[s][3]};
+                __builtin_nontemporal_store(
+                    v4f{o[s][0] + v[s][0], o[s][1] + v[s][1], o[s][2] + v[s][2], o[s][3] + v[s][3]},
+                    reinterpret_cast<v4f*>(outf + i * d.ld + col0 + 4 * k));
             }
           } else {
 #pragma unroll
             for (int s = 0; s < BATCH; ++s) {
               const uint32_t row = (pb + s) * 2 + (lane >> 5), k = lane & 31;
               const int64_t i = i0 + wm0 + 64 * h + row;
-              if (full || (i < d.rows && col_ok)) *reinterpret_cast<v4f*>(outf + i * d.ld + col0 + 4 * k) = v[s];
+              if (full || (i < d.rows && col_ok))
+                __builtin_nontemporal_store(v[s], reinterpret_cast<v4f*>(outf + i * d.ld + col0 + 4 * k));
             }
           }
         }
