@@ -19,9 +19,10 @@
 //   * the scale bytes of four consecutive 128-blocks are packed in one
 //     register per operand row and picked by the instruction's op_sel; the
 //     weight-block scales of a tile are staged in LDS once;
-//   * the epilogue stages each wave's tile through LDS and stores whole rows,
-//     non-temporal: a round of tiles writes 32 MiB of output, which through
-//     L2 would evict the operand panels the next tiles read;
+//   * the epilogue stages each wave's tile through LDS and stores whole rows
+//     with non-temporal stores, which drain faster than plain ones (the
+//     waves wait less at the end of a tile; the operand fetches are the
+//     same either way);
 //   * Dgrad can read the weight codes W[n][k] as quantized (reduction along
 //     the rows, no transposed copy): that B tile is staged as 128 weight rows
 //     of 256 bytes and its fragments come from LDS transpose reads
