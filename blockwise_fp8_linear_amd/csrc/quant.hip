@@ -274,8 +274,9 @@ __device__ __forceinline__ uint32_t quant4_cols(uint32_t w0, uint32_t w1, const 
 // activation shapes: written bytes at the algorithmic count (+11% in row-band
 // order, from partial sectors written back from several L2s), and 0-8%
 // faster.  Other shapes walk row band by row band.  NT: the codes leave with
-// non-temporal stores (measured 4-10% faster from 32 column tiles on in the
-// blocked order, 3% slower at 16).
+// non-temporal stores, except in the blocked order below 32 column tiles
+// (measured: blocked, 4-10% faster from 32 column tiles on, 3% slower at
+// 16; row-band order, 1-20% faster on every shape tried).
 constexpr uint32_t kDualBlockCols = 8, kDualBlockRows = 16, kDualNtColTiles = 32;
 
 __host__ __device__ __forceinline__ bool dual_blocked(uint32_t row_tiles, uint32_t col_tiles) {
@@ -458,7 +459,7 @@ hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int6
   const uint32_t rt = (uint32_t)(rows / 128);
   const uint32_t ct = (uint32_t)(cols / 128);
   const uint32_t blocked = dual_blocked(rt, ct) ? 1u : 0u;
-  const bool nt = blocked && ct >= kDualNtColTiles;
+  const bool nt = !blocked || ct >= kDualNtColTiles;
   const dim3 grid(rt * ct), block(kDualThreads);
   if (fp32_scale) {
     if (nt)
