@@ -20,8 +20,10 @@
 //     register per operand row and picked by the instruction's op_sel; the
 //     weight-block scales of a tile are staged in LDS once;
 //   * the epilogue stages each wave's tile through LDS and stores whole rows
-//     with non-temporal stores, which drain faster than plain ones (the
-//     waves wait less at the end of a tile; the operand fetches are the
+//     with non-temporal stores: measured faster than plain ones (the fused
+//     backward most), although issuing them takes a little longer, so the
+//     gain is outside the epilogue -- plausibly the output no longer sitting
+//     dirty in L2 for operand fetches to evict (the fetch counts are the
 //     same either way);
 //   * Dgrad can read the weight codes W[n][k] as quantized (reduction along
 //     the rows, no transposed copy): that B tile is staged as 128 weight rows
@@ -376,7 +378,7 @@ struct Dst {
 template <int BATCH, class Src>
 __device__ __forceinline__ void store_tile_from(const Dst& d, uint8_t* lds, int64_t i0, int64_t j0, Src src) {
   // ---- epilogue, staged through LDS so that global stores are whole rows,
-  // non-temporal (the output is not read again here).
+  // non-temporal (the output is not read again here; see the file header).
   // src(a, b) lane l, element e holds row i = wm0 + 32a + l%32 and column
   // j = wn0 + 32b + 8*(e/4) + 4*(l/32) + e%4.  Each wave writes its 128 x 128
   // tile to its own 32 KiB of LDS in units of 4 consecutive columns, the unit
