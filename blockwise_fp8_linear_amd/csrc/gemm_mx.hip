@@ -31,8 +31,12 @@
 //     (ds_read_b64_tr_b8);
 //   * Wgrad (long reduction over tokens, few output tiles) runs stream-K:
 //     a persistent grid in which every workgroup does the same number of
-//     512-deep reduction units, tiles shared by several workgroups being
-//     summed, in a fixed order, by the last of them to finish.
+//     512-deep reduction units; a tile shared by several workgroups is
+//     written piece by piece to fp32 workspace slots, which a fix-up kernel
+//     adds in reduction order (deterministic; no workgroup waits for
+//     another).  The fused backward (Dgrad and Wgrad of one linear in one
+//     persistent launch) partitions its units the same way, by host-planned
+//     ranges.
 // Requirements (else the caller falls back to gemm.hip): the number of
 // 128-blocks of the reduction is a multiple of 4 (at most 128 for
 // weight-block scales) and the per-row scale arrays are 16-byte aligned.
