@@ -273,18 +273,19 @@ __device__ __forceinline__ uint32_t quant4_cols(uint32_t w0, uint32_t w1, const 
 // merges the pieces before writing the sector back.  Measured on the
 // activation shapes: written bytes at the algorithmic count (+11% in row-band
 // order, from partial sectors written back from several L2s), and 0-8%
-// faster.  Other shapes walk row band by row band.  NT: the codes leave with
-// non-temporal stores, except in the blocked order below 32 column tiles
-// (measured: blocked, 4-10% faster from 32 column tiles on, 3% slower at
-// 16; row-band order, 1-20% faster on every shape tried).
-constexpr uint32_t kDualBlockCols = 8, kDualBlockRows = 16, kDualNtColTiles = 32;
+// faster.  Other shapes walk row band by row band.  The codes leave with
+// plain stores: non-temporal ones were faster for the quantizer timed alone
+// (launch after launch) but slower in a training step, where the GEMMs read
+// the codes right after (they no longer found them in the caches) and the
+// quantizer itself ran slower too.
+constexpr uint32_t kDualBlockCols = 8, kDualBlockRows = 16;
 
 __host__ __device__ __forceinline__ bool dual_blocked(uint32_t row_tiles, uint32_t col_tiles) {
   return row_tiles % kDualBlockRows == 0 && col_tiles % kDualBlockCols == 0 &&
          (row_tiles / kDualBlockRows) * (col_tiles / kDualBlockCols) % 8 == 0;
 }
 
-template <class S, bool NT>
+template <class S>
 __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ s,
     uint8_t* __restrict__ qT, int64_t ld_qT, float* __restrict__ sT, uint32_t row_tiles, uint32_t col_tiles,
@@ -327,8 +328,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     o.x = quant4(v[i].x, v[i].y, sc);
     o.y = quant4(v[i].z, v[i].w, sc);
     uint2* const qp = reinterpret_cast<uint2*>(q + (r0 + i) * ld_q + c0 + cb * 8);
-    if constexpr (NT) __builtin_nontemporal_store((u32x2{o.x, o.y}), reinterpret_cast<u32x2*>(qp));
-    else *qp = o;
+    *qp = o;
     if (cb == 0) s[(r0 + i) * G + ct] = sc.s;
   }
 
@@ -386,8 +386,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     u32x4 w = *reinterpret_cast<const u32x4*>(&tq[c][pu & ~1u]);
     if (pu & 1) w = u32x4{w[2], w[3], w[0], w[1]};  // the pair is stored swapped
     u32x4* const qTp = reinterpret_cast<u32x4*>(qT + (c0 + c) * ld_qT + m0 + 16 * p);
-    if constexpr (NT) __builtin_nontemporal_store(w, qTp);
-    else *qTp = w;
+    *qTp = w;
   }
   if (rb == 0) {
 #pragma unroll
@@ -459,23 +458,13 @@ hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int6
   const uint32_t rt = (uint32_t)(rows / 128);
   const uint32_t ct = (uint32_t)(cols / 128);
   const uint32_t blocked = dual_blocked(rt, ct) ? 1u : 0u;
-  const bool nt = !blocked || ct >= kDualNtColTiles;
   const dim3 grid(rt * ct), block(kDualThreads);
-  if (fp32_scale) {
-    if (nt)
-      hipLaunchKernelGGL((quant_dual_kernel<Fp32Scale, true>), grid, block, 0, stream, x, ld_x, q, ld_q, s, qT, ld_qT,
-                         sT, rt, ct, blocked);
-    else
-      hipLaunchKernelGGL((quant_dual_kernel<Fp32Scale, false>), grid, block, 0, stream, x, ld_x, q, ld_q, s, qT, ld_qT,
-                         sT, rt, ct, blocked);
-  } else {
-    if (nt)
-      hipLaunchKernelGGL((quant_dual_kernel<Pow2Scale, true>), grid, block, 0, stream, x, ld_x, q, ld_q, s, qT, ld_qT,
-                         sT, rt, ct, blocked);
-    else
-      hipLaunchKernelGGL((quant_dual_kernel<Pow2Scale, false>), grid, block, 0, stream, x, ld_x, q, ld_q, s, qT, ld_qT,
-                         sT, rt, ct, blocked);
-  }
+  if (fp32_scale)
+    hipLaunchKernelGGL(quant_dual_kernel<Fp32Scale>, grid, block, 0, stream, x, ld_x, q, ld_q, s, qT, ld_qT, sT, rt, ct,
+                       blocked);
+  else
+    hipLaunchKernelGGL(quant_dual_kernel<Pow2Scale>, grid, block, 0, stream, x, ld_x, q, ld_q, s, qT, ld_qT, sT, rt, ct,
+                       blocked);
   return hipGetLastError();
 }
 

@@ -248,10 +248,10 @@ def test_dual_strided_input_padded_outputs():
 
 
 def test_dual_blocked_order_strided_padded():
-    """A shape the one-pass quantizer walks in XCD blocks of 8 x 16 tiles with
-    non-temporal code stores (16 row tiles, 64 column tiles), read from a
-    column slice of a wider tensor into padded outputs: every tile is
-    written, bit for bit, and nothing past the outputs' ends."""
+    """A shape the one-pass quantizer walks in XCD blocks of 8 x 16 tiles
+    (16 row tiles, 64 column tiles), read from a column slice of a wider
+    tensor into padded outputs: every tile is written, bit for bit, and
+    nothing past the outputs' ends."""
     wide = synth.normal_bf16((2048, 8192 + 256), 1.0, 49, 0)
     _assert_dual(wide, "blocked order, column slice, padded outputs", cols=8192, pad_q=128, pad_qT=256)
 
