@@ -111,6 +111,8 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 //    every bf16 amax and every bf16 x with |x| <= amax, i.e. for every
 //    element a quantizer can see.
 struct Pow2Scale {
+  // the conversion can take the scale itself (cvt2_pow2 below)
+  static constexpr bool kScaledCvt = true;
   float s, inv;
   __device__ __forceinline__ explicit Pow2Scale(uint32_t amax_bits) {
     const int e = scale_exponent(amax_bits);
@@ -121,6 +123,7 @@ struct Pow2Scale {
 };
 
 struct Fp32Scale {
+  static constexpr bool kScaledCvt = false;
   float s;      // the stored scale
   float f;      // 2^64 if s < 2^-64, else 1
   float sf, r;  // s * f (exact) and fl32(1 / (s * f))
@@ -140,6 +143,7 @@ struct Fp32Scale {
 };
 
 struct Fp32ScaleDiv {
+  static constexpr bool kScaledCvt = false;
   float s;
   __device__ __forceinline__ explicit Fp32ScaleDiv(uint32_t amax_bits) {
     s = amax_bits == 0 ? 1.0f : __uint_as_float(amax_bits << 16) / 448.0f;
@@ -150,13 +154,36 @@ struct Fp32ScaleDiv {
   }
 };
 
+// Two bf16 (the halves of w, low half first) divided by the power-of-two
+// scale s and rounded to E4M3 (RNE) in one instruction, CDNA4's
+// v_cvt_scalef32_pk_fp8_bf16: the two codes go to the low (HI = false) or
+// high half of the result, the other half is old's.  The instruction divides
+// by 2^(exponent field of s); for the normal scales 2^-126 .. 2^126 the
+// power-of-two rule produces it gives, for every bf16 x with |x / s| <= 448,
+// the code that rounding the exact quotient x * 2^-e gives (a GPU probe over
+// all 65536 bf16 patterns and every such exponent found no difference from
+// cvt_pk_fp8_f32 of the exact product).  It replaces the unpacking to fp32,
+// the multiply and the conversion of two values.
+typedef short v2i16_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf16_t __attribute__((ext_vector_type(2)));
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt2_pow2(uint32_t old, uint32_t w, float s) {
+  const v2i16_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(v2i16_t, old),
+                                                              __builtin_bit_cast(v2bf16_t, w), s, HI);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 // Four bf16 (two words) scaled by sc and rounded to E4M3 (RNE) into one
 // word, byte i holding element i.
 template <class S>
 __device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, const S& sc) {
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(sc(bf16_lo(w0)), sc(bf16_hi(w0)), 0, false);
-  r = __builtin_amdgcn_cvt_pk_fp8_f32(sc(bf16_lo(w1)), sc(bf16_hi(w1)), r, true);
-  return (uint32_t)r;
+  if constexpr (S::kScaledCvt) {
+    return cvt2_pow2<true>(cvt2_pow2<false>(0u, w0, sc.s), w1, sc.s);
+  } else {
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(sc(bf16_lo(w0)), sc(bf16_hi(w0)), 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(sc(bf16_lo(w1)), sc(bf16_hi(w1)), r, true);
+    return (uint32_t)r;
+  }
 }
 
 // Same for four values given as lo/hi halves of four different words
@@ -166,6 +193,25 @@ __device__ __forceinline__ uint32_t quant4_sel(float a, float b, float c, float 
   int r = __builtin_amdgcn_cvt_pk_fp8_f32(sc(a), sc(b), 0, false);
   r = __builtin_amdgcn_cvt_pk_fp8_f32(sc(c), sc(d), r, true);
   return (uint32_t)r;
+}
+
+// One column of four rows: wi holds row i's value in its half H (0: low
+// 16 bits), all with the scale sc; byte i of the result is row i's code.
+// With a power-of-two scale each pair of rows is gathered into one word
+// (v_perm_b32) and converted by the scaled instruction.
+template <int H, class S>
+__device__ __forceinline__ uint32_t quant4_col(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, const S& sc) {
+  if constexpr (S::kScaledCvt) {
+    constexpr uint32_t sel = H ? 0x07060302u : 0x05040100u;  // half H of the low word, then of the high word
+    // the gathered word is dead after the conversion, so it also serves as
+    // the half that the second conversion overwrites (no register to clear)
+    const uint32_t p01 = __builtin_amdgcn_perm(w1, w0, sel);
+    const uint32_t r = cvt2_pow2<false>(p01, p01, sc.s);
+    return cvt2_pow2<true>(r, __builtin_amdgcn_perm(w3, w2, sel), sc.s);
+  } else {
+    const auto f = [](uint32_t w) { return H ? bf16_hi(w) : bf16_lo(w); };
+    return quant4_sel(f(w0), f(w1), f(w2), f(w3), sc);
+  }
 }
 
 // 4x4 byte transpose: in[r] holds bytes (r,0..3); out[c] gets bytes (0..3,c).

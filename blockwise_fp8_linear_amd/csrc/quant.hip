@@ -130,14 +130,14 @@ __global__ __launch_bounds__(kColThreads) void quant_colgroup_kernel(
   m = lane8_max_pk(m);
   const S inv0(m & 0xFFFFu), inv1(m >> 16);
   u32x4 o0, o1;
-  o0.x = quant4_sel(bf16_lo(w[0]), bf16_lo(w[1]), bf16_lo(w[2]), bf16_lo(w[3]), inv0);
-  o0.y = quant4_sel(bf16_lo(w[4]), bf16_lo(w[5]), bf16_lo(w[6]), bf16_lo(w[7]), inv0);
-  o0.z = quant4_sel(bf16_lo(w[8]), bf16_lo(w[9]), bf16_lo(w[10]), bf16_lo(w[11]), inv0);
-  o0.w = quant4_sel(bf16_lo(w[12]), bf16_lo(w[13]), bf16_lo(w[14]), bf16_lo(w[15]), inv0);
-  o1.x = quant4_sel(bf16_hi(w[0]), bf16_hi(w[1]), bf16_hi(w[2]), bf16_hi(w[3]), inv1);
-  o1.y = quant4_sel(bf16_hi(w[4]), bf16_hi(w[5]), bf16_hi(w[6]), bf16_hi(w[7]), inv1);
-  o1.z = quant4_sel(bf16_hi(w[8]), bf16_hi(w[9]), bf16_hi(w[10]), bf16_hi(w[11]), inv1);
-  o1.w = quant4_sel(bf16_hi(w[12]), bf16_hi(w[13]), bf16_hi(w[14]), bf16_hi(w[15]), inv1);
+  o0.x = quant4_col<0>(w[0], w[1], w[2], w[3], inv0);
+  o0.y = quant4_col<0>(w[4], w[5], w[6], w[7], inv0);
+  o0.z = quant4_col<0>(w[8], w[9], w[10], w[11], inv0);
+  o0.w = quant4_col<0>(w[12], w[13], w[14], w[15], inv0);
+  o1.x = quant4_col<1>(w[0], w[1], w[2], w[3], inv1);
+  o1.y = quant4_col<1>(w[4], w[5], w[6], w[7], inv1);
+  o1.z = quant4_col<1>(w[8], w[9], w[10], w[11], inv1);
+  o1.w = quant4_col<1>(w[12], w[13], w[14], w[15], inv1);
   const int64_t c = c0 + 2 * cp;
   *reinterpret_cast<u32x4*>(qT + c * ld_qT + m0 + rp * 16) = o0;
   *reinterpret_cast<u32x4*>(qT + (c + 1) * ld_qT + m0 + rp * 16) = o1;
@@ -248,18 +248,11 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_batch_kernel(BlockJob
 // amax is a DPP reduction and each lane stores 8 codes per row.  Column
 // groups: a packed per-column max over the thread's rows, then over the 16
 // row blocks (wave shuffles, then LDS across the 4 waves); the thread's 8x8
-// codes are transposed in registers and staged in LDS, from where whole
-// 128-byte lines of the transposed output are stored.
+// codes are formed column by column (each pair of rows gathered into one
+// word by a byte permute, then converted) and staged in LDS, from where
+// whole 128-byte lines of the transposed output are stored.
 // ---------------------------------------------------------------------------
 constexpr int kDualThreads = 256;
-
-// Four codes, each value with its own scale (four columns).
-template <class S>
-__device__ __forceinline__ uint32_t quant4_cols(uint32_t w0, uint32_t w1, const S* sc) {
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(sc[0](bf16_lo(w0)), sc[1](bf16_hi(w0)), 0, false);
-  r = __builtin_amdgcn_cvt_pk_fp8_f32(sc[2](bf16_lo(w1)), sc[3](bf16_hi(w1)), r, true);
-  return (uint32_t)r;
-}
 
 // Tile order of the one-pass quantizer.  A tile's scales are 128 four-byte
 // values strided through s (one per row) and 128 through sT (one per
@@ -357,27 +350,25 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
   // column j's amax is half j % 2 of cm[j / 2]
   const S inv[8] = {S(cm[0] & 0xFFFFu), S(cm[0] >> 16), S(cm[1] & 0xFFFFu), S(cm[1] >> 16),
                     S(cm[2] & 0xFFFFu), S(cm[2] >> 16), S(cm[3] & 0xFFFFu), S(cm[3] >> 16)};
-  // codes of row i, columns 0..3 in lo[i] and 4..7 in hi[i], each column with its own scale
-  uint32_t lo[8], hi[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    lo[i] = quant4_cols(v[i].x, v[i].y, &inv[0]);
-    hi[i] = quant4_cols(v[i].z, v[i].w, &inv[4]);
-  }
-  // The thread's 8x8 codes, transposed in registers (8 rows of one column
-  // per 8 bytes), go through LDS as tq[column][row block], the 8-byte unit
+  // The thread's 8x8 codes, one column at a time (rows 0..3 and 4..7 of
+  // column j, each with the column's scale: word j / 2 of each row, half
+  // j % 2), go through LDS as tq[column][row block], the 8-byte unit
   // XOR-swizzled by the column block cb, and leave as whole 128-byte lines of
   // qT: 8 lanes per column, 16 bytes (two row blocks) each.
-  uint32_t ta[4], tb[4];
   const int64_t cc = c0 + cb * 8;
-  transpose4x4(&lo[0], ta);
-  transpose4x4(&lo[4], tb);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) tq[cb * 8 + j][rb ^ cb] = make_uint2(ta[j], tb[j]);
-  transpose4x4(&hi[0], ta);
-  transpose4x4(&hi[4], tb);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) tq[cb * 8 + 4 + j][rb ^ cb] = make_uint2(ta[j], tb[j]);
+  for (int j = 0; j < 8; ++j) {
+    const int m = j >> 1;
+    uint32_t a, b;
+    if (j & 1) {
+      a = quant4_col<1>(v[0][m], v[1][m], v[2][m], v[3][m], inv[j]);
+      b = quant4_col<1>(v[4][m], v[5][m], v[6][m], v[7][m], inv[j]);
+    } else {
+      a = quant4_col<0>(v[0][m], v[1][m], v[2][m], v[3][m], inv[j]);
+      b = quant4_col<0>(v[4][m], v[5][m], v[6][m], v[7][m], inv[j]);
+    }
+    tq[cb * 8 + j][rb ^ cb] = make_uint2(a, b);
+  }
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
