@@ -82,6 +82,30 @@ __global__ __launch_bounds__(256) void quotient_check_kernel(uint32_t* counts) {
   if (threadIdx.x == 0) counts[blockIdx.y * gridDim.x + blockIdx.x] = (uint32_t)n;
 }
 
+// The power-of-two quantizers' conversion (cvt2_pow2: v_cvt_scalef32_pk_fp8_bf16
+// given the stored scale 2^e) against the fp32 path it replaces (the exact
+// product x * 2^-e rounded by cvt_pk_fp8_f32), for every bf16 pattern x
+// (thread t of block (b, y): bits 256 b + t, in both halves of the word) and
+// every scale exponent e = y - 126, -126 <= e <= 126, wherever |x| * 2^-e <=
+// 448 (the codes of a finite x the rule can produce).  Each block writes
+// how many of its threads found a difference.
+__global__ __launch_bounds__(256) void pow2_cvt_check_kernel(uint32_t* counts) {
+  const uint32_t bits = blockIdx.x * 256 + threadIdx.x;
+  const int e = (int)blockIdx.y - 126;
+  const float s = __builtin_ldexpf(1.0f, e), inv = __builtin_ldexpf(1.0f, -e);
+  const float x = __uint_as_float(bits << 16);
+  const float v = x * inv;
+  bool bad = false;
+  if (__builtin_isfinite(x) && __builtin_fabsf(v) <= 448.0f) {
+    const uint32_t ref = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xFFFFu;
+    const uint32_t got = fp8blk::cvt2_pow2<false>(0u, bits | (bits << 16), s) & 0xFFFFu;
+    const uint32_t got_hi = fp8blk::cvt2_pow2<true>(0u, bits | (bits << 16), s) >> 16;
+    bad = got != ref || got_hi != ref;
+  }
+  const int n = __syncthreads_count(bad);
+  if (threadIdx.x == 0) counts[blockIdx.y * gridDim.x + blockIdx.x] = (uint32_t)n;
+}
+
 // On-box HBM ceiling: streaming kernels over one buffer, each lane moving
 // kStreamUnroll 16-byte pieces per step (all loads issued before the first
 // store or use), non-temporal loads and stores, a grid-stride loop over
@@ -148,6 +172,12 @@ extern "C" int fp8probe_stream(int mode, const void* src, void* dst, size_t byte
 extern "C" int fp8probe_fp32_quotient_check(uint32_t* counts, hipStream_t stream) {
   if (counts == nullptr) return -1;
   hipLaunchKernelGGL(quotient_check_kernel, dim3(128, 0x7F80), dim3(256), 0, stream, counts);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+extern "C" int fp8probe_pow2_cvt_check(uint32_t* counts, hipStream_t stream) {
+  if (counts == nullptr) return -1;
+  hipLaunchKernelGGL(pow2_cvt_check_kernel, dim3(256, 253), dim3(256), 0, stream, counts);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

@@ -52,6 +52,19 @@ int fp8probe_stream(int mode, const void *src, void *dst, size_t bytes, int work
 #define FP8PROBE_QCHECK_BLOCKS (128 * 0x7F80)
 int fp8probe_fp32_quotient_check(uint32_t *counts, hipStream_t stream);
 
+/*
+ * Check, on the device, the power-of-two quantizers' conversion (CDNA4's
+ * v_cvt_scalef32_pk_fp8_bf16 given the stored scale s = 2^e) against the
+ * exact product x * 2^-e rounded to E4M3 by v_cvt_pk_fp8_f32, for every
+ * bf16 pattern x and every e in [-126, 126] with |x| * 2^-e <= 448 (each
+ * result half of the instruction).  counts: device buffer of
+ * FP8PROBE_CVTCHECK_BLOCKS uint32; entry 256 (e + 126) + j receives how many
+ * of the bf16 patterns 256 j .. 256 j + 255 differ.  Returns 0, -1 for a
+ * NULL buffer, -6 if the launch failed.
+ */
+#define FP8PROBE_CVTCHECK_BLOCKS (256 * 253)
+int fp8probe_pow2_cvt_check(uint32_t *counts, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

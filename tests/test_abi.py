@@ -308,6 +308,10 @@ def test_probe_library():
     assert p.fp8probe_mfma(0, 10, 1, P, None) == -1
     assert p.fp8probe_mfma(256, 0, 1, P, None) == -1
     assert p.fp8probe_mfma(256, 10, 1, None, None) == -1
+    p.fp8probe_pow2_cvt_check.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    assert p.fp8probe_pow2_cvt_check(None, None) == -1
+    p.fp8probe_fp32_quotient_check.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    assert p.fp8probe_fp32_quotient_check(None, None) == -1
 
 
 def test_c_program_against_the_header(tmp_path):

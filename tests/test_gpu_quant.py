@@ -410,3 +410,26 @@ def test_fp32_scale_quotient_exhaustive():
     assert c.min() >= 0, "the probe left blocks unwritten"
     bad = np.flatnonzero(c)
     assert bad.size == 0, f"{int(c.sum())} elements differ; first at amax bits {hex(int(bad[0]) // 128)}"
+
+
+def test_pow2_scaled_conversion_exhaustive():
+    """The power-of-two quantizers convert with the scaled instruction given
+    the stored scale: for every bf16 pattern and every scale exponent the
+    rule produces, wherever the quotient is in range, it must give the code
+    of the exact quotient (the fp32 path: exact product, then the plain
+    conversion, which the cast tests tie to the oracle)."""
+    import ctypes
+    import os
+    import torch
+    import blockwise_fp8_linear_amd as fb
+    note("fp8probe_pow2_cvt_check: grid 256 x 253")
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(fb.LIB_PATH), "libfp8probe.so"))
+    lib.fp8probe_pow2_cvt_check.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.fp8probe_pow2_cvt_check.restype = ctypes.c_int
+    counts = torch.full((256 * 253,), -1, dtype=torch.int32, device="cuda")
+    assert lib.fp8probe_pow2_cvt_check(counts.data_ptr(), torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    c = host(counts)
+    assert c.min() >= 0, "the probe left blocks unwritten"
+    bad = np.flatnonzero(c)
+    assert bad.size == 0, f"{int(c.sum())} conversions differ; first at e = {int(bad[0]) // 256 - 126}"
