@@ -324,6 +324,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* lds, int64
           // the block's first product: only LAG MFMAs (and no promotions)
           // were issued since its MFMA, so add the missing wait states
           if (k == LAG) asm volatile("s_nop 4" : "+v"(pp[j & 3]));
+          // the block's last LAG products have no later MFMA to pass them
+          // through, so nothing else keeps their promotions from moving up
+          // to right behind their own MFMAs (a reordered build did that and
+          // read a product 7 wait states after its MFMA): these wait states,
+          // after the last MFMA and tied to every product buffer, pin them
+          if (k == STEPS) asm volatile("s_nop 7\n\ts_nop 7" : "+v"(pp[0]), "+v"(pp[1]), "+v"(pp[2]), "+v"(pp[3]));
           const v4f p = pp[j & 3];
           if constexpr (C::BROW) {
 #pragma unroll
