@@ -17,8 +17,11 @@
 // 128-deep blocks.  Each block's A and B tiles (BM x 128 and BN x 128 bytes)
 // go to LDS by direct global->LDS loads, double buffered (the next block
 // loads while this one is computed), with the 16-byte chunks of a row
-// XOR-swizzled by (row & 7) so that the MFMA fragment reads are free of bank
-// conflicts.  One v_mfma_*_16x16x128_f8f6f4 consumes exactly one 128-deep
+// XOR-swizzled by (row & 7).  That leaves a two-way LDS bank conflict on the
+// fragment reads (rows r and r + 8 of a 16-row fragment collide: the
+// counters read about 2e7 conflict cycles per launch); a swizzle that folds
+// in row >> 3 removes most of it but measured no faster, since this
+// kernel's time goes elsewhere, so the simpler one stays.  One v_mfma_*_16x16x128_f8f6f4 consumes exactly one 128-deep
 // block for a 16x16 sub-tile, so the per-block scale product is applied
 // between blocks:
 //   PROMOTE = true : P = MFMA(A_b, B_b) from zero, then
