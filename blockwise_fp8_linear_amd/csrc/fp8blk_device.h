@@ -158,12 +158,13 @@ struct Fp32ScaleDiv {
 // scale s and rounded to E4M3 (RNE) in one instruction, CDNA4's
 // v_cvt_scalef32_pk_fp8_bf16: the two codes go to the low (HI = false) or
 // high half of the result, the other half is old's.  The instruction divides
-// by 2^(exponent field of s); for the normal scales 2^-126 .. 2^126 the
-// power-of-two rule produces it gives, for every bf16 x with |x / s| <= 448,
-// the code that rounding the exact quotient x * 2^-e gives (a GPU probe over
-// all 65536 bf16 patterns and every such exponent found no difference from
-// cvt_pk_fp8_f32 of the exact product).  It replaces the unpacking to fp32,
-// the multiply and the conversion of two values.
+// by 2^(exponent field of s).  Given a scale 2^e, -126 <= e <= 126 (every
+// scale the power-of-two rule produces), it returns for every bf16 x with
+// |x / s| <= 448 the code of the exact quotient x * 2^-e rounded to nearest
+// even: fp8probe_pow2_cvt_check compares it with cvt_pk_fp8_f32 of the
+// exact product over all 65536 bf16 patterns at every such e and finds no
+// difference.  It replaces the unpacking to fp32, the multiply and the
+// conversion of two values.
 typedef short v2i16_t __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf16_t __attribute__((ext_vector_type(2)));
 template <bool HI>

@@ -21,8 +21,9 @@
 // fragment reads (rows r and r + 8 of a 16-row fragment collide: the
 // counters read about 2e7 conflict cycles per launch); a swizzle that folds
 // in row >> 3 removes most of it but measured no faster, since this
-// kernel's time goes elsewhere, so the simpler one stays.  One v_mfma_*_16x16x128_f8f6f4 consumes exactly one 128-deep
-// block for a 16x16 sub-tile, so the per-block scale product is applied
+// kernel's time goes elsewhere, so the simpler one stays.  One
+// v_mfma_*_16x16x128_f8f6f4 consumes exactly one 128-deep block for a 16x16
+// sub-tile, so the per-block scale product is applied
 // between blocks:
 //   PROMOTE = true : P = MFMA(A_b, B_b) from zero, then
 //                    acc = fma(P, fl32(sa*sb), acc) on the VALU, in fp32 --
