@@ -433,3 +433,49 @@ def test_pow2_scaled_conversion_exhaustive():
     assert c.min() >= 0, "the probe left blocks unwritten"
     bad = np.flatnonzero(c)
     assert bad.size == 0, f"{int(c.sum())} conversions differ; first at e = {int(bad[0]) // 256 - 126}"
+
+
+def _sweep_values():
+    """Every non-negative finite bf16 magnitude up to 448 and its negative."""
+    mags = (np.arange(0x8000, dtype=np.uint32) << 16).view(np.float32)
+    mags = mags[np.isfinite(mags) & (mags <= 448.0)]
+    return np.concatenate([mags, -mags]).astype(np.float32)
+
+
+def test_colgroup_exhaustive_cast():
+    """The row-group kernel's exhaustive cast sweep through the separate
+    column-group kernel: each column a group of 128 rows whose amax is
+    exactly 448 * 2^e (row 0), the other 127 rows every bf16 magnitude up to
+    448 scaled by 2^e, for every e in [-126, 118]."""
+    vals = _sweep_values()
+    per = 127
+    ng = (vals.size + per - 1) // per
+    vals = np.concatenate([vals, np.zeros(ng * per - vals.size, np.float32)]).reshape(ng, per)
+    cols = []
+    for e in range(-126, 119):
+        blk = np.empty((ng, 128), np.float32)
+        blk[:, 0] = 448.0 * np.float32(2.0 ** e)
+        blk[:, 1:] = vals * np.float32(2.0 ** e)
+        cols.append(blk)
+    x = np.concatenate(cols)                                    # groups as rows
+    x = np.concatenate([x, np.zeros(((-x.shape[0]) % 128, 128), np.float32)])
+    _assert_colgroup(np.ascontiguousarray(synth.bf16_bits_from_f32(x).T), "exhaustive cast")
+
+
+def test_block_exhaustive_cast():
+    """The same sweep through the block quantizer (and its transposed copy):
+    each 128 x 128 block holds amax 448 * 2^e at (0, 0) and 16383 of the
+    scaled magnitudes, every magnitude appearing at every e in [-126, 118]."""
+    vals = _sweep_values()
+    per = 128 * 128 - 1
+    nb = (vals.size + per - 1) // per
+    vals = np.concatenate([vals, np.zeros(nb * per - vals.size, np.float32)]).reshape(nb, per)
+    blocks = []
+    for e in range(-126, 119):
+        b = np.empty((nb, 128 * 128), np.float32)
+        b[:, 0] = 448.0 * np.float32(2.0 ** e)
+        b[:, 1:] = vals * np.float32(2.0 ** e)
+        blocks.append(b.reshape(nb, 128, 128))
+    w = np.concatenate(blocks)                                  # [blocks, 128, 128]
+    w = np.ascontiguousarray(w.transpose(1, 0, 2).reshape(128, -1))   # blocks side by side
+    _assert_block(synth.bf16_bits_from_f32(w), "exhaustive cast")
