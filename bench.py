@@ -474,7 +474,7 @@ def cpu_baseline(budget_s, mode=0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: the benchmark runs on one GPU only (--gpus {args.gpus} requested); "
               "across GPUs only the Wgrad gradients would need an all-reduce; it is not implemented", file=sys.stderr)
         sys.exit(2)
     import torch
